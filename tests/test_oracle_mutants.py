@@ -1,0 +1,45 @@
+"""Plant plausible mistakes in a scratch copy of the oracle (CPU only) and
+check that the pins in test_oracle_pins.py catch every one of them."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "rope_sign": ("y[i] = x[i] * c - x[i + half] * s;", "y[i] = x[i] * c + x[i + half] * s;"),
+    "rope_theta": ("pow(base, -2.0 * (double)i / (double)d)", "pow(base, -1.0 * (double)i / (double)d)"),
+    "rope_pair": ("y[i + half] = x[i + half] * c + x[i] * s;",
+                  "y[i + half] = x[i + half] * c + x[i + 1 < half ? i + 1 : i] * s;"),
+    "proj_transpose": ("s += x[c] * P[(size_t)c * d + j];", "s += x[c] * P[(size_t)j * d + c];"),
+    "prune_tie": ("return (u->idx > v->idx) - (u->idx < v->idx);", "return (u->idx < v->idx) - (u->idx > v->idx);"),
+    "prune_signed": ("keys[c].mag = fabs(x[c]);", "keys[c].mag = x[c];"),
+    "scale_k": ("double scale = 1.0 / sqrt((double)d);", "double scale = 1.0 / sqrt((double)k);"),
+    "dense_half": ("scratch[n + t] = s * scale;", "scratch[n + t] = s * scale * 0.5;"),
+    "v_uses_k_index": ("o[vidx[(size_t)t * k + i]] += a * vval[(size_t)t * k + i];",
+                       "o[kidx[(size_t)t * k + i]] += a * vval[(size_t)t * k + i];"),
+    "evict_row": ("long row = pos - R;", "long row = pos - R + 1;"),
+    "ring_slot": ("long slot = pos % R;", "long slot = (pos + 1) % R;"),
+    "round_ties_away": ("double r = nearbyint(ax / ulp) * ulp;", "double r = round(ax / ulp) * ulp;"),
+    "subnormal_spacing": ("ex = -14;", "ex = -15;"),
+    "drop_newest": ("long nd = ctx < R ? ctx : R;", "long nd = ctx < R ? ctx : R - 1;"),
+    "softmax_bias": ("scratch[t] = exp(scratch[t] - m);",
+                     "scratch[t] = exp(scratch[t] - m) * (t == 0 ? 1.0000001 : 1.0);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    src = open(os.path.join(ROOT, "oracle", "swan_oracle.c")).read()
+    a, b = MUTANTS[name]
+    assert a in src, f"mutation site of {name} no longer in the oracle"
+    ign = shutil.ignore_patterns("*.so", "__pycache__", "csrc", "*.tmp")
+    for sub in ("oracle", "tests", "decode_attention_compressed_02_amd"):
+        shutil.copytree(os.path.join(ROOT, sub), tmp_path / sub, ignore=ign)
+    (tmp_path / "oracle" / "swan_oracle.c").write_text(src.replace(a, b, 1))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        "tests/test_oracle_pins.py"], cwd=tmp_path, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"

@@ -1,0 +1,329 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a library
+routine (numpy's binary16 conversion, a sort), a closed form, an invariant,
+textbook dense attention reached through a different route (Lemmas 1 and 2
+of the SWAN appendix), brute force on tiny inputs, or a trace printed on a
+page (tests/golden/).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from decode_attention_compressed_02_amd import workloads as wl
+
+D = 128
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# binary16 storage rounding == numpy's IEEE conversion
+# ---------------------------------------------------------------------------
+
+def test_round_f16_matches_numpy():
+    r = rng(1)
+    x = np.concatenate([
+        r.standard_normal(20000),
+        r.standard_normal(5000) * 1e-5,  # subnormal range
+        r.standard_normal(5000) * 3e4,  # near overflow
+        np.ldexp(1.0 + (np.arange(1, 2048) + 0.5) / 1024.0, 0),  # exact ties between fp16 values
+        np.ldexp(np.arange(1, 300) + 0.5, -24),  # ties among subnormals
+        [0.0, -0.0, 65504.0, 65519.99, 65520.0, 65536.0, -65520.0, 2.0 ** -25, 2.0 ** -24, 3 * 2.0 ** -26],
+    ])
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16)
+    got = oracle.round_f16(x)
+    np.testing.assert_array_equal(got.astype(np.float16).view(np.uint16), want.view(np.uint16))
+    # the result is itself exactly representable
+    finite = np.isfinite(got)
+    np.testing.assert_array_equal(got[finite], want[finite].astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
+# RoPE: closed forms of the rotation at basis vectors, identity at 0,
+# isometry, relative-position property
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("i,theta", [(0, 1.0), (16, 0.1), (32, 0.01), (48, 0.001)])
+def test_rope_basis_vectors(i, theta):
+    # theta_i = 10000^(-2i/128): 1, 10^-1, 10^-2, 10^-3 at i = 0, 16, 32, 48
+    for p in (1.0, 3.0, 1000.0):
+        e = np.zeros(D)
+        e[i] = 1.0
+        y = oracle.rope(e, p)
+        want = np.zeros(D)
+        want[i], want[i + 64] = math.cos(p * theta), math.sin(p * theta)
+        np.testing.assert_allclose(y, want, atol=1e-12)
+        e = np.zeros(D)
+        e[i + 64] = 1.0
+        y = oracle.rope(e, p)
+        want = np.zeros(D)
+        want[i], want[i + 64] = -math.sin(p * theta), math.cos(p * theta)
+        np.testing.assert_allclose(y, want, atol=1e-12)
+
+
+def test_rope_identity_isometry_relative():
+    r = rng(2)
+    q, k = r.standard_normal(D), r.standard_normal(D)
+    np.testing.assert_array_equal(oracle.rope(q, 0.0), q)
+    for m, n in [(5, 2), (1000, 17), (131071, 65536)]:
+        qm, kn = oracle.rope(q, m), oracle.rope(k, n)
+        assert abs(np.linalg.norm(qm) - np.linalg.norm(q)) < 1e-12
+        # <RoPE(q, m), RoPE(k, n)> depends only on m - n
+        assert abs(qm @ kn - oracle.rope(q, m - n) @ k) < 1e-9
+
+
+def test_projection_is_rowvector_product():
+    r = rng(3)
+    x = r.standard_normal(D)
+    perm = r.permutation(D)
+    P = np.eye(D)[:, perm]  # x @ P picks coordinates perm
+    np.testing.assert_allclose(oracle.project(x, 7.0, P), oracle.rope(x, 7.0)[perm], atol=1e-15)
+    np.testing.assert_allclose(oracle.project(x, 0.0, np.eye(D)), x, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# Lemmas 1 and 2 (SWAN appendix A.1): with k = d_h, no dense buffer and no
+# rounding, the rotated sparse decode followed by un-rotation equals textbook
+# attention softmax(q K^T / sqrt(d)) V (SWAN decode formula, section 3)
+# ---------------------------------------------------------------------------
+
+def textbook_attention(q, K, V):
+    s = q @ K.T / math.sqrt(q.shape[-1])
+    a = np.exp(s - s.max(axis=-1, keepdims=True))
+    a /= a.sum(axis=-1, keepdims=True)
+    return a @ V
+
+
+@pytest.mark.parametrize("T,g", [(1, 1), (37, 4), (300, 2)])
+def test_lossless_rotation(T, g):
+    r = rng(10 + T)
+    P_qk = wl.random_orthogonal(r, D)
+    P_vo = wl.random_orthogonal(r, D)
+    assert np.abs(P_qk @ P_qk.T - np.eye(D)).max() < 1e-13
+    m = T - 1  # the query sits at the newest position
+    q = r.standard_normal((g, D))
+    K = r.standard_normal((T, D)) * 2.0
+    V = r.standard_normal((T, D))
+    qhat = np.stack([oracle.project(q[h], m, P_qk) for h in range(g)])
+    Khat = np.stack([oracle.project(K[t], t, P_qk) for t in range(T)])
+    Vhat = V @ P_vo  # the absorbed value weights emit rotated values
+    idx = np.tile(np.arange(D, dtype=np.uint8), (T, 1))
+    out_hat = oracle.attend(qhat, idx, Khat, idx, Vhat, np.zeros((0, D)), np.zeros((0, D)))
+    Qr = np.stack([oracle.rope(q[h], m) for h in range(g)])
+    Kr = np.stack([oracle.rope(K[t], t) for t in range(T)])
+    want = textbook_attention(Qr, Kr, V)
+    np.testing.assert_allclose(out_hat @ P_vo.T, want, atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# sparse with k = d_h equals dense; densified brute force; closed forms
+# ---------------------------------------------------------------------------
+
+def test_sparse_full_k_equals_dense():
+    r = rng(4)
+    g, n = 4, 50
+    q = r.standard_normal((g, D))
+    K = r.standard_normal((n, D))
+    V = r.standard_normal((n, D))
+    idx = np.tile(np.arange(D, dtype=np.uint8), (n, 1))
+    empty = np.zeros((0, D))
+    all_sparse = oracle.attend(q, idx, K, idx, V, empty, empty)
+    all_dense = oracle.attend(q, idx[:0], K[:0], idx[:0], V[:0], K, V)
+    mixed = oracle.attend(q, idx[:20], K[:20], idx[:20], V[:20], K[20:], V[20:])
+    np.testing.assert_allclose(all_sparse, all_dense, atol=1e-14, rtol=0)
+    np.testing.assert_allclose(mixed, all_dense, atol=1e-14, rtol=0)
+    np.testing.assert_allclose(all_dense, textbook_attention(q, K, V), atol=1e-13)
+
+
+def densify(idx, val, d=D):
+    out = np.zeros((idx.shape[0], d))
+    for t in range(idx.shape[0]):
+        for i in range(idx.shape[1]):
+            out[t, idx[t, i]] += val[t, i]
+    return out
+
+
+@pytest.mark.parametrize("g,n,nd,k,d", [(3, 7, 3, 5, 16), (1, 1, 0, 1, 8), (2, 0, 4, 3, 8), (4, 9, 2, 32, 128)])
+def test_bruteforce_tiny(g, n, nd, k, d):
+    r = rng(100 + n * 10 + k)
+    q = r.standard_normal((g, d))
+    kidx = np.array([np.sort(r.choice(d, k, replace=False)) for _ in range(n)], np.uint8).reshape(n, k)
+    vidx = np.array([np.sort(r.choice(d, k, replace=False)) for _ in range(n)], np.uint8).reshape(n, k)
+    kval, vval = r.standard_normal((n, k)), r.standard_normal((n, k))
+    kd, vd = r.standard_normal((nd, d)), r.standard_normal((nd, d))
+    got = oracle.attend(q, kidx, kval, vidx, vval, kd, vd)
+    K = np.concatenate([densify(kidx, kval, d), kd])
+    V = np.concatenate([densify(vidx, vval, d), vd])
+    # naive per-head loop, independent of the vectorised helper above
+    for h in range(g):
+        s = [sum(q[h, c] * K[t, c] for c in range(d)) / math.sqrt(d) for t in range(n + nd)]
+        mx = max(s)
+        e = [math.exp(x - mx) for x in s]
+        z = sum(e)
+        o = [sum(e[t] / z * V[t, c] for t in range(n + nd)) for c in range(d)]
+        np.testing.assert_allclose(got[h], o, atol=1e-12)
+
+
+def test_zero_query_gives_mean_value():
+    r = rng(5)
+    n, nd, k = 40, 6, 10
+    kidx = np.stack([np.sort(r.choice(D, k, replace=False)) for _ in range(n)]).astype(np.uint8)
+    vidx = np.stack([np.sort(r.choice(D, k, replace=False)) for _ in range(n)]).astype(np.uint8)
+    kval, vval = r.standard_normal((n, k)), r.standard_normal((n, k))
+    kd, vd = r.standard_normal((nd, D)), r.standard_normal((nd, D))
+    got = oracle.attend(np.zeros((2, D)), kidx, kval, vidx, vval, kd, vd)
+    want = np.concatenate([densify(vidx, vval), vd]).mean(axis=0)
+    np.testing.assert_allclose(got, np.stack([want, want]), atol=1e-14)
+
+
+def test_dominant_token():
+    # one key aligned with q and scaled so its score dominates: output -> its value
+    r = rng(6)
+    n, k = 30, 8
+    kidx = np.stack([np.sort(r.choice(D, k, replace=False)) for _ in range(n)]).astype(np.uint8)
+    vidx = np.stack([np.sort(r.choice(D, k, replace=False)) for _ in range(n)]).astype(np.uint8)
+    kval, vval = r.standard_normal((n, k)) * 0.01, r.standard_normal((n, k))
+    q = np.zeros((1, D))
+    q[0, kidx[17]] = 100.0 * np.sign(kval[17])
+    kval[17] = np.sign(kval[17]) * 10.0
+    got = oracle.attend(q, kidx, kval, vidx, vval, np.zeros((0, D)), np.zeros((0, D)))
+    np.testing.assert_allclose(got[0], densify(vidx[17:18], vval[17:18])[0], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# magnitude top-k: brute-force sort, ties, invariants
+# ---------------------------------------------------------------------------
+
+def brute_topk(x, k):
+    order = sorted(range(len(x)), key=lambda c: (-abs(x[c]), c))
+    keep = sorted(order[:k])
+    return np.array(keep, np.uint8), np.array([x[c] for c in keep])
+
+
+@pytest.mark.parametrize("k", [1, 5, 32, 64, 127, 128])
+def test_prune_matches_bruteforce(k):
+    r = rng(7 + k)
+    for trial in range(30):
+        x = oracle.round_f16(r.standard_normal(D) * (8.0 if trial % 3 == 0 else 1.0))
+        if trial % 5 == 0:  # heavy ties: few distinct magnitudes, random signs
+            x = r.choice([-2.0, -1.0, -0.0, 0.0, 1.0, 2.0], size=D)
+        idx, val = oracle.prune(x, k)
+        bi, bv = brute_topk(x, k)
+        np.testing.assert_array_equal(idx, bi)
+        np.testing.assert_array_equal(val, bv)
+        assert np.all(np.diff(idx.astype(int)) > 0)
+        dropped = np.setdiff1d(np.arange(D), idx)
+        if k < D:
+            assert np.abs(val).min() >= np.abs(x[dropped]).max()
+
+
+def test_prune_tie_break_lower_index():
+    x = np.ones(D)
+    x[::2] = -1.0
+    idx, val = oracle.prune(x, 10)
+    np.testing.assert_array_equal(idx, np.arange(10))
+    x = np.zeros(D)
+    x[100] = -0.0
+    x[5] = 0.5
+    idx, _ = oracle.prune(x, 3)
+    np.testing.assert_array_equal(idx, [0, 1, 5])
+
+
+# ---------------------------------------------------------------------------
+# dense-buffer ring (page 3, section 3.2 trace) and eviction into sparse rows
+# ---------------------------------------------------------------------------
+
+def test_ring_trace_matches_page(golden):
+    W = 8
+    cache = oracle.OracleCache(1, 1, 1, D, W, D, 16)
+    seen = {}
+    for t in range(10):
+        # token t is recognisable by its value t + 1 in every coordinate
+        khat = np.full((1, 1, D), t + 1.0)
+        cache.append(khat, -khat, np.array([t]))
+        seen[t] = [int(round(cache.ringk[0, 0, s, 0])) - 1 if t >= s else None for s in range(W)]
+    for line in golden("ring_trace_w8.txt"):
+        t, *slots = line.split()
+        want = [None if s == "-" else int(s) for s in slots]
+        assert seen[int(t)] == want, (t, seen[int(t)], want)
+    # tokens 0 and 1 were evicted into sparse rows 0 and 1 (k = d keeps all)
+    np.testing.assert_array_equal(cache.kval[0, 0, 0], np.full(D, 1.0))
+    np.testing.assert_array_equal(cache.kval[0, 0, 1], np.full(D, 2.0))
+    np.testing.assert_array_equal(cache.vval[0, 0, 1], np.full(D, -2.0))
+
+
+def test_textbook_decode_when_buffer_holds_everything():
+    # R >= context: no sparse part, the step is the plain decode formula over
+    # the appended cache (SWAN section 3) in the rotated basis.
+    r = rng(8)
+    B, N, H, R, T = 2, 4, 2, 64, 20
+    P = np.stack([wl.random_orthogonal(r, D) for _ in range(H)])
+    Kraw = r.standard_normal((B, H, T, D))
+    Vraw = r.standard_normal((B, H, T, D))
+    cache = oracle.OracleCache(B, N, H, D, R, 32, 8)
+    cache.prefill(Kraw, Vraw, np.array([T, T]), P)
+    q, knew, vnew = r.standard_normal((B, N, D)), r.standard_normal((B, H, D)), r.standard_normal((B, H, D))
+    pos = np.array([T, T])
+    qhat, khat, out = cache.step(q, knew, vnew, pos, P)
+    g = N // H
+    for b in range(B):
+        for h in range(H):
+            K = np.stack([oracle.round_f16(oracle.project(Kraw[b, h, t], t, P[h])) for t in range(T)]
+                         + [oracle.round_f16(oracle.project(knew[b, h], T, P[h]))])
+            V = oracle.round_f16(np.concatenate([Vraw[b, h], vnew[b, h][None]]))
+            qh = np.stack([oracle.project(q[b, h * g + j], T, P[h]) for j in range(g)])
+            np.testing.assert_allclose(out[b, h * g:(h + 1) * g], textbook_attention(qh, K, V), atol=1e-13)
+
+
+def test_step_evicts_oldest_and_attends_all():
+    # After the step at position p with R < p + 1: rows 0..p-R are the pruned
+    # tokens 0..p-R, the buffer holds p-R+1..p; densified attention over
+    # exactly those tokens equals the step's output.
+    r = rng(9)
+    R, k, T = 4, 16, 11
+    P = wl.random_orthogonal(r, D)[None]
+    Kraw, Vraw = r.standard_normal((1, 1, T, D)), r.standard_normal((1, 1, T, D))
+    cache = oracle.OracleCache(1, 2, 1, D, R, k, 32)
+    cache.prefill(Kraw, Vraw, np.array([T]), P)
+    q, knew, vnew = r.standard_normal((1, 2, D)), r.standard_normal((1, 1, D)), r.standard_normal((1, 1, D))
+    qhat, khat, out = cache.step(q, knew, vnew, np.array([T]), P)
+    Kall = np.concatenate([Kraw[0, 0], knew[0]])
+    Vall = np.concatenate([Vraw[0, 0], vnew[0]])
+    Khat = np.stack([oracle.round_f16(oracle.project(Kall[t], t, P[0])) for t in range(T + 1)])
+    Vhat = oracle.round_f16(Vall)
+    rows_k, rows_v = [], []
+    for t in range(T + 1):
+        if t <= T - R:  # evicted and pruned
+            rows_k.append(densify(*[a[None] for a in brute_topk(Khat[t], k)])[0])
+            rows_v.append(densify(*[a[None] for a in brute_topk(Vhat[t], k)])[0])
+        else:
+            rows_k.append(Khat[t])
+            rows_v.append(Vhat[t])
+    want = textbook_attention(qhat[0], np.stack(rows_k), np.stack(rows_v))
+    np.testing.assert_allclose(out[0], want, atol=1e-13)
+    assert cache.kidx[0, 0, T - R].any() and not cache.kidx[0, 0, T - R + 1].any()
+
+
+def test_zero_buffer_prunes_new_token_first():
+    # R = 0 (the pages' zero-buffer variant): every token, the new one
+    # included, is attended through its pruned sparse row.
+    r = rng(11)
+    k, T = 8, 6
+    P = wl.random_orthogonal(r, D)[None]
+    Kraw, Vraw = r.standard_normal((1, 1, T, D)), r.standard_normal((1, 1, T, D))
+    cache = oracle.OracleCache(1, 1, 1, D, 0, k, 16)
+    cache.prefill(Kraw, Vraw, np.array([T]), P)
+    q, knew, vnew = r.standard_normal((1, 1, D)), r.standard_normal((1, 1, D)), r.standard_normal((1, 1, D))
+    qhat, khat, out = cache.step(q, knew, vnew, np.array([T]), P)
+    Kall = np.concatenate([Kraw[0, 0], knew[0]])
+    Vall = np.concatenate([Vraw[0, 0], vnew[0]])
+    Ks = np.stack([densify(*[a[None] for a in brute_topk(oracle.round_f16(oracle.project(Kall[t], t, P[0])), k)])[0]
+                   for t in range(T + 1)])
+    Vs = np.stack([densify(*[a[None] for a in brute_topk(oracle.round_f16(Vall[t]), k)])[0] for t in range(T + 1)])
+    np.testing.assert_allclose(out[0], textbook_attention(qhat[0], Ks, Vs), atol=1e-13)
