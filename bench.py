@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the SWAN hybrid-cache decode step on one MI355X.
+
+Workload (default): batch 16, 32 query / 8 kv heads (GQA 4), d_h = 128,
+context 32768 at the first step, dense buffer R = 256, k = 32 kept
+coordinates, 16 consecutive decode steps.  Inputs are seeded synthetic
+tensors of that shape (raw keys and queries N(0,1), values N(0,1) in the
+stored basis, random orthogonal P_QK); the initial hybrid cache is built on
+the GPU from a 32767-token history with swan_prefill_convert.
+
+A timed step is the whole hot path: swan_project_qk -> swan_append_evict ->
+swan_decode_split -> swan_decode_reduce, all inputs already resident in HBM.
+Prints one JSON line (rank 0).
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_compressed_02_amd", "csrc", f)
+                  for f in ("decode.hip", "swan_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def build_state(w, split_tokens: int):
+    """Generate the seeded history on the host (threads over sequences), move
+    it to the GPU and convert it to the hybrid cache there."""
+    import torch
+    from decode_attention_compressed_02_amd import swan as S
+    from decode_attention_compressed_02_amd import workloads as wl
+    from decode_attention_compressed_02_amd.cache import SwanDecoder
+
+    B, H = w.B, w.H_kv
+    T = [w.history_len(b) for b in range(B)]
+    Tm = max(T)
+    dims = S.make_dims(w.B, w.N_h, w.H_kv, w.R, w.k, n_cap=w.n_cap() + 64, split_tokens=split_tokens)
+    P = torch.from_numpy(wl.projection_qk(w)).cuda()
+    dec = SwanDecoder(dims, P, w.rope_base)
+    K = torch.empty((B, H, Tm, 128), dtype=torch.float32, device="cuda")
+    V = torch.empty_like(K)
+    t0 = time.time()
+    with cf.ThreadPoolExecutor(max_workers=min(16, B)) as ex:
+        for b, (kb, vb) in enumerate(ex.map(lambda b: wl.history(w, b), range(B))):
+            K[b, :, :T[b]].copy_(torch.from_numpy(kb))
+            V[b, :, :T[b]].copy_(torch.from_numpy(vb))
+    log(f"generated + uploaded history {B}x{H}x{Tm} in {time.time() - t0:.1f}s")
+    lens = torch.tensor(T, dtype=torch.int32, device="cuda")
+    dec.prefill(lens, Tm, K, V)
+    torch.cuda.synchronize()
+    del K, V
+    torch.cuda.empty_cache()
+    return dec
+
+
+def cpu_baseline(w, steps: int, seqs: list[int]):
+    """The float64 oracle on a sample of the workload: the chosen sequences,
+    all kv heads, the first `steps` decode steps.  Returns (KV tokens/s,
+    threads, seconds, sample description)."""
+    import oracle
+    from decode_attention_compressed_02_amd import workloads as wl
+
+    sub = w.scaled(B=len(seqs), ctx=tuple(w.ctx[b] for b in seqs))
+    oc = oracle.OracleCache.for_workload(sub, sub.n_cap() + steps)
+    Tm = max(sub.history_len(b) for b in range(sub.B))
+    K = np.zeros((sub.B, sub.H_kv, Tm, 128), np.float32)
+    V = np.zeros_like(K)
+    for i, b in enumerate(seqs):
+        K[i], V[i] = wl.history(w, b)
+    P = wl.projection_qk(w).astype(np.float64)
+    threads = oracle.default_threads()
+    t0 = time.time()
+    oc.prefill(K, V, np.array([sub.history_len(b) for b in range(sub.B)], np.int64), P, w.rope_base, threads)
+    log(f"oracle prefill of the sample in {time.time() - t0:.1f}s")
+    del K, V
+    tokens, secs = 0, 0.0
+    for s in range(steps):
+        q, kr, vn, pos = wl.step_inputs(w, s)
+        q, kr, vn, pos = q[seqs], kr[seqs], vn[seqs], pos[seqs].astype(np.int64)
+        t = time.perf_counter()
+        oc.step(q, kr, vn, pos, P, w.rope_base, threads)
+        secs += time.perf_counter() - t
+        tokens += int(np.sum(pos + 1))
+    used = min(threads, sub.B * sub.H_kv)
+    desc = (f"sequences {seqs} of {w.B} (all {w.H_kv} kv heads), steps 0..{steps - 1}: "
+            f"project + append/evict + decode in float64")
+    return tokens / secs, used, secs, desc
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=16)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload number (1-4); 3 is the headline")
+    ap.add_argument("--split-tokens", type=int, default=0, help="sparse rows per split (0 = automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences in the oracle sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the SWAN decode step here runs on a single MI355X "
+              "(no collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from decode_attention_compressed_02_amd import accounting as acc
+    from decode_attention_compressed_02_amd import swan as S
+    from decode_attention_compressed_02_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    S.lib()
+    w = wl.config(args.config)
+    n_steps = args.warmup + args.steps
+    if n_steps > w.steps:
+        w = w.scaled(steps=n_steps)
+    dec = build_state(w, args.split_tokens)
+    log(f"device {torch.cuda.get_device_name(0)}; dims {dec.dims}")
+
+    # step inputs for every step, resident in HBM before timing
+    inputs = []
+    for s in range(max(args.warmup, args.steps)):
+        q, kr, vn, pos = wl.step_inputs(w, s)
+        inputs.append(tuple(torch.from_numpy(a).cuda() for a in (q, kr, vn, pos)) + (int(pos.max()),))
+    max_pos_all = max(x[4] for x in inputs)
+    dec.ensure_workspace(max_pos_all)
+    kb0, vb0 = dec.cache.k_buf.clone(), dec.cache.v_buf.clone()
+    nsplit = S.swan_decode_num_splits(dec.dims, inputs[0][4])
+
+    stream = torch.cuda.current_stream()
+
+    def run_step(x, ev=None):
+        q, kr, vn, pos, mp = x
+        dec.project(q, kr, pos)
+        dec.append(pos, mp, vn)
+        if ev is not None:
+            ev[0].record(stream)
+        S.swan_decode_split(dec.dims, dec.cache.struct(), pos, mp, dec.q_hat, dec.workspace)
+        if ev is not None:
+            ev[1].record(stream)
+        S.swan_decode_reduce(dec.dims, pos, mp, dec.workspace, dec.o_hat)
+
+    for s in range(args.warmup):
+        run_step(inputs[s])
+    torch.cuda.synchronize()
+    # back to the initial state: the steps only changed the buffer and rows past n
+    dec.cache.k_buf.copy_(kb0)
+    dec.cache.v_buf.copy_(vb0)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run_step(inputs[s], evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = wall * 1e3 / args.steps
+    split_ms = [a.elapsed_time(b) for a, b in evs]
+    tokens = sum(int(inputs[s][3].sum().item()) + w.B for s in range(args.steps))  # sum_b (pos_b + 1)
+    value = tokens / wall
+    # algorithmic bytes of the split kernel per launch, averaged over the timed steps
+    split_bytes, dec_bytes, flops = [], [], []
+    for s in range(args.steps):
+        pos = inputs[s][3].cpu().numpy()
+        n = [max(0, int(p) + 1 - w.R) for p in pos]
+        f = [min(int(p) + 1, w.R) for p in pos]
+        split_bytes.append(acc.split_kernel_bytes(n, w.H_kv, w.N_h, f, w.k))
+        dec_bytes.append(acc.decode_bytes(n, w.H_kv, w.N_h, f, w.k))
+        flops.append(acc.decode_flops(n, w.H_kv, w.N_h, f, w.k))
+    split_avg_ms = float(np.mean(split_ms))
+    achieved = float(np.mean(split_bytes)) / (split_avg_ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha") == kernel_source_hash() and tr.get("workload") == w.name:
+            traffic = tr.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": "decode-attn KV tokens/sec and achieved HBM GB/s (% of peak) per step",
+        "value": value,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) raw keys/queries, stored-basis values, random orthogonal P_QK)",
+        "config": {"workload": f"config {args.config}: {w.name}", "B": w.B, "N_h": w.N_h, "H_kv": w.H_kv,
+                   "d_h": w.d_h, "ctx_first_step": int(w.ctx[0]), "R": w.R, "k": w.k,
+                   "storage": "fp16 values, uint8 indices, fp16 dense buffer", "splits": nsplit,
+                   "split_tokens": dec.dims.split_tokens or "auto"},
+        "step_hbm_GBps": float(np.mean(dec_bytes)) / (ms_step * 1e-3) / 1e9,
+        "step_frac_of_peak": float(np.mean(dec_bytes)) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "split_kernel_ms": split_avg_ms,
+        "decode_gflops_per_step": float(np.mean(flops)) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "k_split", "algorithmic_bytes_per_launch": float(np.mean(split_bytes))},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        seqs = list(range(min(args.cpu_seqs, w.B)))
+        v, cores, secs, desc = cpu_baseline(w, min(args.steps, 16), seqs)
+        result["cpu_baseline"] = {"value": v, "unit": "KV tokens/s", "cores": cores, "kind": "oracle",
+                                  "sample": desc, "seconds": secs}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

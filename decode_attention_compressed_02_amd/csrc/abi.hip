@@ -1,0 +1,329 @@
+// abi.hip -- the extern "C" entry points declared in swan.h: host-side
+// validation (before anything is enqueued), split planning and dispatch.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "swan_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+swan_status fail(swan_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+swan_status hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return SWAN_OK;
+    return fail(SWAN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int32_t row_stride(int32_t k)
+{
+    int32_t s = 8;
+    while (s < k) s *= 2;
+    return s;
+}
+
+swan_status check_dims(const swan_dims *d)
+{
+    if (!d) return fail(SWAN_ERR_INVALID_ARG, "dims is NULL");
+    if (d->d_h != swan::kD) return fail(SWAN_ERR_UNSUPPORTED, "d_h = %d, only 128 is supported", d->d_h);
+    if (d->B < 1 || d->N_h < 1 || d->H_kv < 1)
+        return fail(SWAN_ERR_INVALID_ARG, "B, N_h, H_kv must be >= 1 (got %d, %d, %d)", d->B, d->N_h, d->H_kv);
+    if (d->B > 65535 || d->H_kv > 65535) return fail(SWAN_ERR_INVALID_ARG, "B and H_kv must be <= 65535");
+    if (d->N_h % d->H_kv) return fail(SWAN_ERR_INVALID_ARG, "N_h = %d is not a multiple of H_kv = %d", d->N_h, d->H_kv);
+    const int g = d->N_h / d->H_kv;
+    if (g != 1 && g != 2 && g != 4 && g != 8)
+        return fail(SWAN_ERR_UNSUPPORTED, "GQA group g = %d, supported: 1, 2, 4, 8", g);
+    if (d->k < 1 || d->k > d->d_h) return fail(SWAN_ERR_INVALID_ARG, "k = %d outside 1..%d", d->k, d->d_h);
+    if (d->R < 0) return fail(SWAN_ERR_INVALID_ARG, "R = %d < 0", d->R);
+    if (d->block_size < 0) return fail(SWAN_ERR_INVALID_ARG, "block_size < 0");
+    if (d->block_size > 0) {
+        if (d->max_blocks < 1 || d->num_blocks < 1)
+            return fail(SWAN_ERR_INVALID_ARG, "paged layout needs max_blocks >= 1 and num_blocks >= 1");
+    } else if (d->n_cap < 0) {
+        return fail(SWAN_ERR_INVALID_ARG, "n_cap < 0");
+    }
+    if (d->split_tokens < 0 || d->split_tokens % 64)
+        return fail(SWAN_ERR_INVALID_ARG, "split_tokens = %d must be 0 or a positive multiple of 64", d->split_tokens);
+    return SWAN_OK;
+}
+
+int64_t row_cap(const swan_dims *d)
+{
+    return d->block_size > 0 ? (int64_t)d->max_blocks * d->block_size : (int64_t)d->n_cap;
+}
+
+swan_status check_cache(const swan_dims *d, const swan_cache *c, bool need_buf)
+{
+    if (!c) return fail(SWAN_ERR_INVALID_ARG, "cache is NULL");
+    if (!c->k_idx || !c->k_val || !c->v_idx || !c->v_val) return fail(SWAN_ERR_INVALID_ARG, "sparse plane is NULL");
+    if (need_buf && d->R > 0 && (!c->k_buf || !c->v_buf)) return fail(SWAN_ERR_INVALID_ARG, "dense buffer is NULL");
+    if (d->block_size > 0 && !c->block_table) return fail(SWAN_ERR_INVALID_ARG, "paged layout needs block_table");
+    return SWAN_OK;
+}
+
+swan::SparseGeom geom(const swan_dims *d, const swan_cache *c)
+{
+    swan::SparseGeom g;
+    g.H = d->H_kv;
+    g.ks = row_stride(d->k);
+    g.n_cap = d->n_cap;
+    g.bs = d->block_size;
+    g.max_blocks = d->max_blocks;
+    g.num_blocks = d->num_blocks;
+    g.bt = d->block_size > 0 ? c->block_table : nullptr;
+    return g;
+}
+
+struct Plan {
+    int S_sparse, S_dense, S, TPS;
+};
+
+// Split the sparse rows of the longest sequence into ranges of TPS rows and
+// the dense buffer into ranges of kDenseSplit tokens.  Automatic TPS aims at
+// about 2048 sparse waves (8 per CU) so that even short batches fill the chip.
+Plan plan(const swan_dims *d, int32_t max_pos)
+{
+    const int64_t ctx = (int64_t)max_pos + 1;
+    int64_t n_max = ctx > d->R ? ctx - d->R : 0;
+    if (n_max > row_cap(d)) n_max = row_cap(d);
+    const int64_t fill = ctx <= 0 ? 0 : (ctx < d->R ? ctx : d->R);
+    Plan p;
+    int64_t tps = d->split_tokens;
+    if (tps == 0) {
+        const int64_t units = (int64_t)d->B * d->H_kv;
+        tps = (n_max * units + 2047) / 2048;
+        tps = (tps + 63) / 64 * 64;
+        if (tps < 256) tps = 256;
+        if (tps > 16384) tps = 16384;
+    }
+    p.TPS = (int)tps;
+    p.S_sparse = (int)((n_max + tps - 1) / tps);
+    p.S_dense = (int)((fill + swan::kDenseSplit - 1) / swan::kDenseSplit);
+    p.S = p.S_sparse + p.S_dense;
+    if (p.S == 0) p.S = 1; // nothing to attend anywhere: one empty split
+    return p;
+}
+
+size_t workspace_bytes(const swan_dims *d, const Plan &p)
+{
+    return (size_t)d->B * d->N_h * p.S * (swan::kD + 2) * sizeof(float);
+}
+
+swan_status check_decode(const swan_dims *d, const swan_cache *c, const int32_t *pos, int32_t max_pos,
+                         const void *ws, size_t ws_bytes, Plan *out)
+{
+    swan_status st = check_dims(d);
+    if (st) return st;
+    if (c && (st = check_cache(d, c, true))) return st;
+    if (!pos) return fail(SWAN_ERR_INVALID_ARG, "pos is NULL");
+    const int64_t n_max = (int64_t)max_pos + 1 - d->R;
+    if (n_max > row_cap(d))
+        return fail(SWAN_ERR_CAPACITY, "max_pos = %d needs %lld sparse rows, capacity is %lld", max_pos,
+                    (long long)n_max, (long long)row_cap(d));
+    *out = plan(d, max_pos);
+    if (!ws) return fail(SWAN_ERR_INVALID_ARG, "workspace is NULL");
+    if (ws_bytes < workspace_bytes(d, *out))
+        return fail(SWAN_ERR_INVALID_ARG, "workspace of %zu bytes, need %zu", ws_bytes, workspace_bytes(d, *out));
+    return SWAN_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *swan_status_str(swan_status s)
+{
+    switch (s) {
+    case SWAN_OK: return "SWAN_OK";
+    case SWAN_ERR_INVALID_ARG: return "SWAN_ERR_INVALID_ARG";
+    case SWAN_ERR_UNSUPPORTED: return "SWAN_ERR_UNSUPPORTED";
+    case SWAN_ERR_CAPACITY: return "SWAN_ERR_CAPACITY";
+    case SWAN_ERR_HIP: return "SWAN_ERR_HIP";
+    }
+    return "SWAN_ERR_UNKNOWN";
+}
+
+const char *swan_last_error(void) { return g_err; }
+
+int32_t swan_row_stride(int32_t k) { return row_stride(k); }
+
+swan_status swan_cache_bytes(const swan_dims *d, size_t out[3])
+{
+    swan_status st = check_dims(d);
+    if (st) return st;
+    if (!out) return fail(SWAN_ERR_INVALID_ARG, "out is NULL");
+    const size_t ks = (size_t)row_stride(d->k);
+    const size_t rows = d->block_size > 0 ? (size_t)d->num_blocks * d->H_kv * d->block_size
+                                          : (size_t)d->B * d->H_kv * d->n_cap;
+    out[0] = rows * ks;
+    out[1] = rows * ks * 2;
+    out[2] = (size_t)d->B * d->H_kv * d->R * swan::kD * 2;
+    return SWAN_OK;
+}
+
+swan_status swan_project_qk(const swan_dims *d, const float *q, const float *k, const int32_t *pos,
+                            const float *P_qk, float rope_base, float *q_hat, uint16_t *k_hat, void *stream)
+{
+    swan_status st = check_dims(d);
+    if (st) return st;
+    if (!q || !k || !pos || !P_qk || !q_hat || !k_hat) return fail(SWAN_ERR_INVALID_ARG, "NULL array argument");
+    if (!(rope_base > 1.0f)) return fail(SWAN_ERR_INVALID_ARG, "rope_base must be > 1");
+    swan::ProjectArgs a{d->B, d->N_h, d->H_kv, q, k, pos, P_qk, rope_base, q_hat, k_hat};
+    return hip_status(swan::launch_project(a, (hipStream_t)stream), "swan_project_qk launch");
+}
+
+swan_status swan_append_evict(const swan_dims *d, const swan_cache *c, const int32_t *pos, int32_t max_pos,
+                              const uint16_t *k_hat, const float *v_hat, void *stream)
+{
+    swan_status st = check_dims(d);
+    if (st) return st;
+    if ((st = check_cache(d, c, true))) return st;
+    if (!pos || !k_hat || !v_hat) return fail(SWAN_ERR_INVALID_ARG, "NULL array argument");
+    const int64_t row = d->R > 0 ? (int64_t)max_pos - d->R : (int64_t)max_pos; // newest row written
+    if (row >= row_cap(d))
+        return fail(SWAN_ERR_CAPACITY, "max_pos = %d writes sparse row %lld, capacity is %lld", max_pos,
+                    (long long)row, (long long)row_cap(d));
+    swan::AppendArgs a;
+    a.B = d->B;
+    a.H = d->H_kv;
+    a.R = d->R;
+    a.k = d->k;
+    a.geom = geom(d, c);
+    a.kidx = c->k_idx;
+    a.vidx = c->v_idx;
+    a.kval = c->k_val;
+    a.vval = c->v_val;
+    a.kbuf = c->k_buf;
+    a.vbuf = c->v_buf;
+    a.pos = pos;
+    a.k_hat = k_hat;
+    a.v_hat = v_hat;
+    return hip_status(swan::launch_append(a, (hipStream_t)stream), "swan_append_evict launch");
+}
+
+size_t swan_decode_workspace_bytes(const swan_dims *d, int32_t max_pos)
+{
+    if (check_dims(d)) return 0;
+    return workspace_bytes(d, plan(d, max_pos));
+}
+
+int32_t swan_decode_num_splits(const swan_dims *d, int32_t max_pos)
+{
+    if (check_dims(d)) return -1;
+    return plan(d, max_pos).S;
+}
+
+static swan::SplitArgs split_args(const swan_dims *d, const swan_cache *c, const Plan &p, const int32_t *pos,
+                                  const float *q_hat, void *ws)
+{
+    swan::SplitArgs a;
+    a.B = d->B;
+    a.N_h = d->N_h;
+    a.H = d->H_kv;
+    a.R = d->R;
+    a.S_sparse = p.S_sparse;
+    a.S = p.S;
+    a.TPS = p.TPS;
+    a.row_cap = (int)row_cap(d);
+    a.geom = geom(d, c);
+    a.pos = pos;
+    a.q_hat = q_hat;
+    a.kidx = c->k_idx;
+    a.vidx = c->v_idx;
+    a.kval = c->k_val;
+    a.vval = c->v_val;
+    a.kbuf = c->k_buf;
+    a.vbuf = c->v_buf;
+    a.part_o = (float *)ws;
+    a.part_ml = (float *)ws + (size_t)d->B * d->N_h * p.S * swan::kD;
+    return a;
+}
+
+swan_status swan_decode_split(const swan_dims *d, const swan_cache *c, const int32_t *pos, int32_t max_pos,
+                              const float *q_hat, void *ws, size_t ws_bytes, void *stream)
+{
+    Plan p;
+    swan_status st = check_decode(d, c, pos, max_pos, ws, ws_bytes, &p);
+    if (st) return st;
+    if (!c) return fail(SWAN_ERR_INVALID_ARG, "cache is NULL");
+    if (!q_hat) return fail(SWAN_ERR_INVALID_ARG, "q_hat is NULL");
+    const swan::SplitArgs a = split_args(d, c, p, pos, q_hat, ws);
+    return hip_status(swan::launch_split(a, d->N_h / d->H_kv, (hipStream_t)stream), "swan_decode_split launch");
+}
+
+swan_status swan_decode_reduce(const swan_dims *d, const int32_t *pos, int32_t max_pos, const void *ws,
+                               size_t ws_bytes, float *o_hat, void *stream)
+{
+    Plan p;
+    swan_status st = check_decode(d, nullptr, pos, max_pos, ws, ws_bytes, &p);
+    if (st) return st;
+    if (!o_hat) return fail(SWAN_ERR_INVALID_ARG, "o_hat is NULL");
+    swan::ReduceArgs r;
+    r.B = d->B;
+    r.N_h = d->N_h;
+    r.S = p.S;
+    r.part_o = (const float *)ws;
+    r.part_ml = (const float *)ws + (size_t)d->B * d->N_h * p.S * swan::kD;
+    r.o_hat = o_hat;
+    return hip_status(swan::launch_reduce(r, (hipStream_t)stream), "swan_decode_reduce launch");
+}
+
+swan_status swan_decode_attn(const swan_dims *d, const swan_cache *c, const int32_t *pos, int32_t max_pos,
+                             const float *q_hat, float *o_hat, void *ws, size_t ws_bytes, void *stream)
+{
+    Plan p;
+    swan_status st = check_decode(d, c, pos, max_pos, ws, ws_bytes, &p);
+    if (st) return st;
+    if (!c) return fail(SWAN_ERR_INVALID_ARG, "cache is NULL");
+    if (!q_hat || !o_hat) return fail(SWAN_ERR_INVALID_ARG, "NULL array argument");
+    if ((st = swan_decode_split(d, c, pos, max_pos, q_hat, ws, ws_bytes, stream))) return st;
+    return swan_decode_reduce(d, pos, max_pos, ws, ws_bytes, o_hat, stream);
+}
+
+swan_status swan_prefill_convert(const swan_dims *d, const swan_cache *c, const int32_t *len, int32_t max_len,
+                                 int64_t T_stride, const float *k_raw, const float *v_hat, const float *P_qk,
+                                 float rope_base, void *stream)
+{
+    swan_status st = check_dims(d);
+    if (st) return st;
+    if ((st = check_cache(d, c, true))) return st;
+    if (!len || !k_raw || !v_hat || !P_qk) return fail(SWAN_ERR_INVALID_ARG, "NULL array argument");
+    if (max_len < 0 || T_stride < max_len)
+        return fail(SWAN_ERR_INVALID_ARG, "need 0 <= max_len <= T_stride (got %d, %lld)", max_len, (long long)T_stride);
+    if (!(rope_base > 1.0f)) return fail(SWAN_ERR_INVALID_ARG, "rope_base must be > 1");
+    if ((int64_t)max_len - d->R > row_cap(d))
+        return fail(SWAN_ERR_CAPACITY, "max_len = %d needs %lld sparse rows, capacity is %lld", max_len,
+                    (long long)((int64_t)max_len - d->R), (long long)row_cap(d));
+    if (max_len == 0) return SWAN_OK;
+    swan::PrefillArgs a;
+    a.B = d->B;
+    a.H = d->H_kv;
+    a.R = d->R;
+    a.k = d->k;
+    a.T_stride = T_stride;
+    a.max_len = max_len;
+    a.geom = geom(d, c);
+    a.kidx = c->k_idx;
+    a.vidx = c->v_idx;
+    a.kval = c->k_val;
+    a.vval = c->v_val;
+    a.kbuf = c->k_buf;
+    a.vbuf = c->v_buf;
+    a.len = len;
+    a.k_raw = k_raw;
+    a.v_hat = v_hat;
+    a.P = P_qk;
+    a.base = rope_base;
+    return hip_status(swan::launch_prefill(a, (hipStream_t)stream), "swan_prefill_convert launch");
+}
+
+} // extern "C"

@@ -1,0 +1,158 @@
+// swan_internal.h -- device helpers and launcher declarations shared by the
+// HIP translation units of libswan (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "swan.h"
+
+namespace swan {
+
+constexpr int kD = 128;          // head dimension (indices fit in 8 bits)
+constexpr int kWave = 64;        // CDNA wavefront
+constexpr int kDenseSplit = 256; // buffered tokens per dense split
+
+// log2(e) / sqrt(128): scores are kept in base-2 units so softmax uses exp2
+constexpr float kScoreScaleLog2 = 0.12751743074573063f;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+// round to nearest even (the default mode of v_cvt_f16_f32)
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// Where the sparse rows of one (sequence, kv head) live.
+struct SparseGeom {
+    int H;          // kv heads
+    int ks;         // entries per stored row
+    int n_cap;      // contiguous: rows per unit
+    int bs;         // paged: rows per block (0 = contiguous)
+    int max_blocks; // paged: block-table width
+    int num_blocks; // paged: blocks in the pool
+    const int32_t *bt;
+};
+
+// Entry offset of the start of sparse row r of unit (b, h), r below the
+// unit's row capacity.  Paged: -1 when the block-table entry is not a block
+// of the pool (a caller error), so kernels skip the row instead of
+// addressing outside the planes.
+template <bool PAGED>
+__device__ __forceinline__ int64_t row_offset(const SparseGeom &g, int b, int h, int r)
+{
+    if constexpr (PAGED) {
+        const int blk = g.bt[(int64_t)b * g.max_blocks + r / g.bs];
+        if (blk < 0 || blk >= g.num_blocks) return -1;
+        return (((int64_t)blk * g.H + h) * g.bs + (r % g.bs)) * g.ks;
+    } else {
+        return (((int64_t)b * g.H + h) * g.n_cap + r) * g.ks;
+    }
+}
+
+__device__ __forceinline__ int64_t row_offset_rt(const SparseGeom &g, int b, int h, int r)
+{
+    return g.bs > 0 ? row_offset<true>(g, b, h, r) : row_offset<false>(g, b, h, r);
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (lane == 0) ? 0ull : ((~0ull) >> (64 - lane)); }
+
+// Magnitude top-k of one 128-vector held by a full wave, two fp16 per lane
+// (coordinate lane in `lo`, coordinate lane + 64 in `hi`).  Coordinates are
+// ranked by (fp16 magnitude bits descending, index ascending); the k first
+// are written to the row with ascending indices, values copied bit for bit,
+// and entries k..ks-1 are zero padding.  Integer-only, so the selection is
+// exact.  Must be called by all 64 lanes.
+__device__ __forceinline__ void wave_prune_row(int lane, uint16_t lo, uint16_t hi, int k, int ks, uint8_t *idx_row,
+                                               uint16_t *val_row)
+{
+    const uint32_t mlo = lo & 0x7fffu, mhi = hi & 0x7fffu;
+    int rank_lo = 0, rank_hi = 0;
+#pragma unroll 8
+    for (int j = 0; j < 64; ++j) {
+        // coordinate j (lower half) against this lane's two coordinates
+        const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)mlo, j);
+        rank_lo += (a > mlo) | ((a == mlo) & (j < lane));
+        rank_hi += (a >= mhi);                       // j < lane + 64 always
+        // coordinate j + 64 (upper half)
+        const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)mhi, j);
+        rank_lo += (c > mlo);                        // j + 64 > lane always
+        rank_hi += (c > mhi) | ((c == mhi) & (j < lane));
+    }
+    const bool keep_lo = rank_lo < k, keep_hi = rank_hi < k;
+    const uint64_t blo = __ballot(keep_lo), bhi = __ballot(keep_hi);
+    const uint64_t lt = lanemask_lt(lane);
+    if (keep_lo) {
+        const int o = __popcll(blo & lt);
+        idx_row[o] = (uint8_t)lane;
+        val_row[o] = lo;
+    }
+    if (keep_hi) {
+        const int o = __popcll(blo) + __popcll(bhi & lt);
+        idx_row[o] = (uint8_t)(lane + 64);
+        val_row[o] = hi;
+    }
+    if (lane < ks - k) {
+        idx_row[k + lane] = 0;
+        val_row[k + lane] = 0;
+    }
+}
+
+// ---- launchers (defined in the .hip files; no validation, grids checked by caller)
+
+struct ProjectArgs {
+    int B, N_h, H;
+    const float *q, *k;
+    const int32_t *pos;
+    const float *P;
+    float base;
+    float *q_hat;
+    uint16_t *k_hat;
+};
+hipError_t launch_project(const ProjectArgs &a, hipStream_t s);
+
+struct AppendArgs {
+    int B, H, R, k;
+    SparseGeom geom;
+    uint8_t *kidx, *vidx;
+    uint16_t *kval, *vval, *kbuf, *vbuf;
+    const int32_t *pos;
+    const uint16_t *k_hat;
+    const float *v_hat;
+};
+hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+
+struct SplitArgs {
+    int B, N_h, H, R;
+    int S_sparse, S, TPS;
+    int row_cap; // sparse rows addressable per unit
+    SparseGeom geom;
+    const int32_t *pos;
+    const float *q_hat;
+    const uint8_t *kidx, *vidx;
+    const uint16_t *kval, *vval, *kbuf, *vbuf;
+    float *part_o;  // [B][N_h][S][128]
+    float *part_ml; // [B][N_h][S][2]
+};
+hipError_t launch_split(const SplitArgs &a, int g, hipStream_t s);
+
+struct ReduceArgs {
+    int B, N_h, S;
+    const float *part_o, *part_ml;
+    float *o_hat;
+};
+hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
+
+struct PrefillArgs {
+    int B, H, R, k;
+    int64_t T_stride;
+    int max_len;
+    SparseGeom geom;
+    uint8_t *kidx, *vidx;
+    uint16_t *kval, *vval, *kbuf, *vbuf;
+    const int32_t *len;
+    const float *k_raw, *v_hat, *P;
+    float base;
+};
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+
+} // namespace swan

@@ -1,0 +1,167 @@
+"""Python binding of libswan (include/swan.h): argument marshalling only.
+
+Every function has the name of its C entry point and takes torch tensors for
+the device arrays (PyTorch supplies device memory and streams; every step of
+the computation runs in the HIP kernels of libswan).  A non-OK status raises
+SwanError with the library's message.  The binding fails loudly when the
+library has not been built: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libswan.so")
+
+SWAN_OK, SWAN_ERR_INVALID_ARG, SWAN_ERR_UNSUPPORTED, SWAN_ERR_CAPACITY, SWAN_ERR_HIP = range(5)
+
+EXPORTS = ("swan_status_str", "swan_last_error", "swan_row_stride", "swan_cache_bytes", "swan_project_qk",
+           "swan_append_evict", "swan_decode_workspace_bytes", "swan_decode_num_splits", "swan_decode_attn",
+           "swan_decode_split", "swan_decode_reduce", "swan_prefill_convert")
+
+
+class SwanError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class swan_dims(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("B", "N_h", "H_kv", "d_h", "R", "k", "n_cap", "block_size", "max_blocks",
+                                         "num_blocks", "split_tokens")]
+
+    def __repr__(self):
+        return "swan_dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+class swan_cache(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("k_idx", "k_val", "v_idx", "v_val", "k_buf", "v_buf", "block_table")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libswan (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(hipcc for gfx950); there is no fallback path")
+        L = C.CDLL(LIB_PATH)
+        P, V, I32, I64, F, SZ = C.POINTER, C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+        D, Cc = P(swan_dims), P(swan_cache)
+        sig = {
+            "swan_status_str": ([C.c_int], C.c_char_p),
+            "swan_last_error": ([], C.c_char_p),
+            "swan_row_stride": ([I32], I32),
+            "swan_cache_bytes": ([D, P(SZ)], C.c_int),
+            "swan_project_qk": ([D, V, V, V, V, F, V, V, V], C.c_int),
+            "swan_append_evict": ([D, Cc, V, I32, V, V, V], C.c_int),
+            "swan_decode_workspace_bytes": ([D, I32], SZ),
+            "swan_decode_num_splits": ([D, I32], I32),
+            "swan_decode_attn": ([D, Cc, V, I32, V, V, V, SZ, V], C.c_int),
+            "swan_decode_split": ([D, Cc, V, I32, V, V, SZ, V], C.c_int),
+            "swan_decode_reduce": ([D, V, I32, V, SZ, V, V], C.c_int),
+            "swan_prefill_convert": ([D, Cc, V, I32, I64, V, V, V, F, V], C.c_int),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes, fn.restype = args, res
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != SWAN_OK:
+        L = lib()
+        raise SwanError(status, f"{L.swan_status_str(status).decode()}: {L.swan_last_error().decode()}")
+
+
+def _ptr(t, dtype=None, name="array"):
+    """Device pointer of a contiguous torch tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return C.c_void_p(getattr(stream, "cuda_stream", stream))
+
+
+def make_dims(B, N_h, H_kv, R, k, n_cap=0, d_h=128, block_size=0, max_blocks=0, num_blocks=0, split_tokens=0):
+    return swan_dims(B, N_h, H_kv, d_h, R, k, n_cap, block_size, max_blocks, num_blocks, split_tokens)
+
+
+def swan_row_stride(k: int) -> int:
+    return int(lib().swan_row_stride(k))
+
+
+def swan_cache_bytes(dims: swan_dims):
+    out = (C.c_size_t * 3)()
+    _check(lib().swan_cache_bytes(C.byref(dims), out))
+    return tuple(int(x) for x in out)
+
+
+def swan_decode_workspace_bytes(dims: swan_dims, max_pos: int) -> int:
+    return int(lib().swan_decode_workspace_bytes(C.byref(dims), int(max_pos)))
+
+
+def swan_decode_num_splits(dims: swan_dims, max_pos: int) -> int:
+    return int(lib().swan_decode_num_splits(C.byref(dims), int(max_pos)))
+
+
+def swan_project_qk(dims, q, k, pos, P_qk, rope_base, q_hat, k_hat, stream=None):
+    import torch
+    _check(lib().swan_project_qk(C.byref(dims), _ptr(q, torch.float32, "q"), _ptr(k, torch.float32, "k"),
+                                 _ptr(pos, torch.int32, "pos"), _ptr(P_qk, torch.float32, "P_qk"), float(rope_base),
+                                 _ptr(q_hat, torch.float32, "q_hat"), _ptr(k_hat, torch.float16, "k_hat"),
+                                 _stream(stream)))
+
+
+def swan_append_evict(dims, cache: "swan_cache", pos, max_pos, k_hat, v_hat, stream=None):
+    import torch
+    _check(lib().swan_append_evict(C.byref(dims), C.byref(cache), _ptr(pos, torch.int32, "pos"), int(max_pos),
+                                   _ptr(k_hat, torch.float16, "k_hat"), _ptr(v_hat, torch.float32, "v_hat"),
+                                   _stream(stream)))
+
+
+def swan_decode_attn(dims, cache, pos, max_pos, q_hat, o_hat, workspace, stream=None):
+    import torch
+    _check(lib().swan_decode_attn(C.byref(dims), C.byref(cache), _ptr(pos, torch.int32, "pos"), int(max_pos),
+                                  _ptr(q_hat, torch.float32, "q_hat"), _ptr(o_hat, torch.float32, "o_hat"),
+                                  _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+                                  _stream(stream)))
+
+
+def swan_decode_split(dims, cache, pos, max_pos, q_hat, workspace, stream=None):
+    import torch
+    _check(lib().swan_decode_split(C.byref(dims), C.byref(cache), _ptr(pos, torch.int32, "pos"), int(max_pos),
+                                   _ptr(q_hat, torch.float32, "q_hat"), _ptr(workspace, None, "workspace"),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def swan_decode_reduce(dims, pos, max_pos, workspace, o_hat, stream=None):
+    import torch
+    _check(lib().swan_decode_reduce(C.byref(dims), _ptr(pos, torch.int32, "pos"), int(max_pos),
+                                    _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+                                    _ptr(o_hat, torch.float32, "o_hat"), _stream(stream)))
+
+
+def swan_prefill_convert(dims, cache, length, max_len, k_raw, v_hat, P_qk, rope_base, stream=None):
+    import torch
+    T_stride = k_raw.shape[2]
+    if v_hat.shape != k_raw.shape:
+        raise ValueError("k_raw and v_hat must have the same shape [B][H_kv][T][128]")
+    _check(lib().swan_prefill_convert(C.byref(dims), C.byref(cache), _ptr(length, torch.int32, "len"), int(max_len),
+                                      int(T_stride), _ptr(k_raw, torch.float32, "k_raw"),
+                                      _ptr(v_hat, torch.float32, "v_hat"), _ptr(P_qk, torch.float32, "P_qk"),
+                                      float(rope_base), _stream(stream)))

@@ -1,0 +1,211 @@
+/*
+ * swan.h -- C ABI of the SWAN hybrid-cache decode step on gfx950 (MI355X).
+ *
+ * SWAN ("Sparse Winnowed Attention ... via Decompression-Free KV-Cache
+ * Compression", arXiv 2511.18936) keeps a small dense buffer of the R most
+ * recent rotated keys/values and a large sparse history in which every older
+ * rotated key and value keeps only its k largest-magnitude coordinates as
+ * (8-bit index, fp16 value) pairs.  One decode step (SWAN section 4.2):
+ *
+ *   1. swan_project_qk    q_hat = RoPE(q) P_QK, k_hat = RoPE(k) P_QK
+ *   2. swan_append_evict  put (k_hat, v_hat) in the dense buffer; the token
+ *                         that leaves the buffer is pruned to its top-k
+ *                         coordinates and appended to the sparse history
+ *   3. swan_decode_attn   scores of q_hat against sparse + dense keys, one
+ *                         softmax over both, output accumulated from sparse +
+ *                         dense values, in the rotated value basis
+ *
+ * plus swan_prefill_convert, which turns a prefilled history into the
+ * hybrid cache in one call.
+ *
+ * Conventions
+ * -----------
+ * - All array arguments are DEVICE pointers unless marked (host).  The
+ *   library allocates nothing and keeps no state between calls; the caller
+ *   owns every buffer.  Work is enqueued on `stream` (a hipStream_t; NULL is
+ *   the null stream) and returns without synchronising.
+ * - Host-side validation happens before any launch.  A failed call enqueues
+ *   nothing and returns a status != SWAN_OK; swan_last_error() (host,
+ *   thread-local) describes the failure.  A failed launch returns
+ *   SWAN_ERR_HIP.
+ * - d_h must be 128 (indices fit in 8 bits, SWAN memory section).  The GQA
+ *   group g = N_h / H_kv must be 1, 2, 4 or 8.  1 <= k <= d_h.
+ * - fp16 arrays hold IEEE binary16 bit patterns (uint16_t).
+ * - pos[b] (int32, device) is the position (0-based) of the token appended
+ *   by this step for sequence b.  After swan_append_evict the cache holds
+ *   tokens 0..pos[b]: n_b = max(0, pos[b] + 1 - R) sparse rows (row t = token
+ *   t) and min(pos[b] + 1, R) buffered tokens in slots t mod R (a circular
+ *   buffer, "Reuse, Evict, or Limit Earlier Context" section 3.2).  A
+ *   sequence with pos[b] < 0 is inactive: nothing is appended and its output
+ *   rows are zero.
+ * - max_pos (host) must be >= every pos[b]; it sizes grids and is checked
+ *   against the sparse capacity.  A device pos[b] above max_pos gives
+ *   undefined results for that sequence but no out-of-bounds access.
+ *
+ * Cache layout (all planes caller-allocated, sizes from swan_cache_bytes)
+ * ------------
+ * Each sparse row stores k_stride = swan_row_stride(k) entries (k rounded up
+ * to a power of two, at least 8, so a row splits evenly over 8-entry lane
+ * slices); entries k..k_stride-1 are padding with index 0 and value +0, which
+ * contribute nothing to scores or outputs.
+ *   contiguous (block_size == 0):
+ *     k_idx, v_idx  uint8   [B][H_kv][n_cap][k_stride]
+ *     k_val, v_val  fp16    [B][H_kv][n_cap][k_stride]
+ *   paged (block_size > 0, "Reuse, Evict, or Limit Earlier Context" 1.2):
+ *     k_idx, v_idx  uint8   [num_blocks][H_kv][block_size][k_stride]
+ *     k_val, v_val  fp16    [num_blocks][H_kv][block_size][k_stride]
+ *     block_table   int32   [B][max_blocks]: sparse row t of sequence b is
+ *                   slot t % block_size of block block_table[b][t / block_size]
+ *   dense buffer:
+ *     k_buf, v_buf  fp16    [B][H_kv][R][128], slot = position mod R
+ * Kept entries of a row are stored with ascending indices.
+ */
+#ifndef SWAN_H
+#define SWAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum swan_status {
+    SWAN_OK = 0,
+    SWAN_ERR_INVALID_ARG = 1, /* null pointer, inconsistent sizes, workspace too small */
+    SWAN_ERR_UNSUPPORTED = 2, /* d_h != 128, g not in {1,2,4,8} */
+    SWAN_ERR_CAPACITY = 3,    /* max_pos needs more sparse rows than the cache holds */
+    SWAN_ERR_HIP = 4          /* a HIP launch failed */
+} swan_status;
+
+/* Problem sizes, in the pages' notation (host struct, read during the call). */
+typedef struct swan_dims {
+    int32_t B;            /* sequences in the batch                               */
+    int32_t N_h;          /* query heads                                          */
+    int32_t H_kv;         /* kv heads; g = N_h / H_kv query heads share each one   */
+    int32_t d_h;          /* head dimension, must be 128                           */
+    int32_t R;            /* dense buffer capacity in tokens (0 = no buffer)       */
+    int32_t k;            /* coordinates kept per pruned vector, 1..d_h            */
+    int32_t n_cap;        /* contiguous layout: sparse rows per (sequence, kv head)*/
+    int32_t block_size;   /* 0 = contiguous sparse rows, >0 = rows per paged block */
+    int32_t max_blocks;   /* paged: block-table entries per sequence               */
+    int32_t num_blocks;   /* paged: blocks in the pool                             */
+    int32_t split_tokens; /* decode: sparse rows per split (multiple of 64), 0=auto*/
+} swan_dims;
+
+/* Caller-owned cache planes (host struct holding device pointers). */
+typedef struct swan_cache {
+    uint8_t *k_idx;
+    uint16_t *k_val;
+    uint8_t *v_idx;
+    uint16_t *v_val;
+    uint16_t *k_buf;
+    uint16_t *v_buf;
+    const int32_t *block_table; /* paged layout only; NULL when contiguous */
+} swan_cache;
+
+/* Human-readable name of a status (static string). */
+const char *swan_status_str(swan_status s);
+
+/* Detail of the last failed call on this host thread (static per thread). */
+const char *swan_last_error(void);
+
+/* Entries stored per sparse row: k rounded up to a power of two, >= 8. */
+int32_t swan_row_stride(int32_t k);
+
+/* Bytes of each cache plane for `dims` (host): out[0] = k_idx (= v_idx),
+ * out[1] = k_val (= v_val), out[2] = k_buf (= v_buf).  Returns the status of
+ * validating dims. */
+swan_status swan_cache_bytes(const swan_dims *dims, size_t out[3]);
+
+/*
+ * Step 1 -- runtime projection (SWAN section 4.1: RoPE cannot be absorbed
+ * into W_Q / W_K, so q -> RoPE(q) -> RoPE(q) P_QK runs every step).
+ *   q      float32 [B][N_h][128]   raw queries (before RoPE)
+ *   k      float32 [B][H_kv][128]  raw new keys (before RoPE)
+ *   pos    int32   [B]             rotation position of each sequence
+ *   P_qk   float32 [H_kv][128][128] row-vector convention: x_hat = x P,
+ *                                  element [h][c][j]; query head j uses
+ *                                  P_qk[j / g]
+ *   rope_base                      RoPE base (10000 for Llama-3)
+ *   q_hat  float32 [B][N_h][128]   out: rotated queries
+ *   k_hat  fp16    [B][H_kv][128]  out: rotated keys, rounded to nearest even
+ * RoPE rotates pair (i, i + 64) by pos * rope_base^(-i/64).  Sequences with
+ * pos < 0 are projected at position 0.
+ */
+swan_status swan_project_qk(const swan_dims *dims, const float *q, const float *k, const int32_t *pos,
+                            const float *P_qk, float rope_base, float *q_hat, uint16_t *k_hat, void *stream);
+
+/*
+ * Step 2 -- append the new token, evict and prune (SWAN section 4.2: when the
+ * buffer exceeds its capacity the oldest vectors are evicted, pruned to their
+ * top-k magnitude coordinates and appended to the sparse cache).
+ *   k_hat  fp16    [B][H_kv][128]  rotated new keys (from swan_project_qk)
+ *   v_hat  float32 [B][H_kv][128]  new values, already in the rotated basis
+ *                                  (P_VO absorbed into W_V, SWAN section 4.1);
+ *                                  rounded to fp16 (nearest even) on store
+ * For R > 0 the token at pos - R (if pos >= R) is read from slot pos mod R,
+ * pruned into sparse row pos - R, and the new token takes the slot.  For
+ * R == 0 the new token is pruned straight into sparse row pos.  Pruning keeps
+ * the k coordinates first in the order (|x| descending as fp16 magnitude,
+ * index ascending) and copies their values bit for bit.  In the paged layout
+ * the block holding the new row must be allocated and exclusively owned by
+ * the sequence (copy-on-write is the caller's job).
+ */
+swan_status swan_append_evict(const swan_dims *dims, const swan_cache *cache, const int32_t *pos, int32_t max_pos,
+                              const uint16_t *k_hat, const float *v_hat, void *stream);
+
+/* Bytes of scratch memory swan_decode_attn needs for max_pos (host); 0 if
+ * dims are invalid. */
+size_t swan_decode_workspace_bytes(const swan_dims *dims, int32_t max_pos);
+
+/* Number of splits (workgroups per (sequence, kv head)) swan_decode_attn
+ * launches for max_pos (host); -1 if dims are invalid. */
+int32_t swan_decode_num_splits(const swan_dims *dims, int32_t max_pos);
+
+/*
+ * Step 3 -- hybrid decode attention (SWAN section 4.2 and appendix A.2,
+ * steps 2-4).  For every query head of sequence b, over the n_b sparse and
+ * min(pos[b] + 1, R) buffered tokens of its kv head:
+ *   s_t = (sum_i q_hat[idx_t,i] val_t,i) / sqrt(128)  for sparse tokens
+ *   s_t = (q_hat . k_t) / sqrt(128)                    for buffered tokens
+ *   o_hat = sum_t softmax(s)_t v_t, sparse v_t scattered to its indices
+ *   q_hat  float32 [B][N_h][128]
+ *   o_hat  float32 [B][N_h][128]   out, in the rotated value basis
+ *   workspace  device scratch of at least swan_decode_workspace_bytes()
+ * Two kernels: a split kernel (one wavefront per (sequence, kv head, split)
+ * serving the g query heads of the group, online softmax) and a reduce
+ * kernel that merges the splits.
+ */
+swan_status swan_decode_attn(const swan_dims *dims, const swan_cache *cache, const int32_t *pos, int32_t max_pos,
+                             const float *q_hat, float *o_hat, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* The two halves of swan_decode_attn, for callers that time or schedule them
+ * separately: the split pass writes per-split partials to the workspace, the
+ * reduce pass merges them into o_hat.  Same arguments and checks. */
+swan_status swan_decode_split(const swan_dims *dims, const swan_cache *cache, const int32_t *pos, int32_t max_pos,
+                              const float *q_hat, void *workspace, size_t workspace_bytes, void *stream);
+swan_status swan_decode_reduce(const swan_dims *dims, const int32_t *pos, int32_t max_pos, const void *workspace,
+                               size_t workspace_bytes, float *o_hat, void *stream);
+
+/*
+ * Prefill -> hybrid cache.  Sequence b has len[b] prefilled tokens at
+ * positions 0..len[b]-1 (max_len host bound, 0 <= len[b] <= max_len):
+ *   k_raw  float32 [B][H_kv][T_stride][128]  raw keys (before RoPE)
+ *   v_hat  float32 [B][H_kv][T_stride][128]  values in the rotated basis
+ * Each key gets RoPE at its own position and P_qk; keys and values are
+ * rounded to fp16.  Tokens 0..len-R-1 are pruned into sparse rows, the last
+ * min(len, R) go to buffer slots t mod R -- the same state as appending the
+ * tokens one by one.  In the paged layout every block the rows fall in must
+ * be allocated.
+ */
+swan_status swan_prefill_convert(const swan_dims *dims, const swan_cache *cache, const int32_t *len, int32_t max_len,
+                                 int64_t T_stride, const float *k_raw, const float *v_hat, const float *P_qk,
+                                 float rope_base, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWAN_H */

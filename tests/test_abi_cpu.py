@@ -1,0 +1,140 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point
+include/swan.h declares, sizes its buffers, and rejects bad arguments with
+the documented status before enqueuing anything."""
+import ctypes as C
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+from decode_attention_compressed_02_amd import swan as S  # noqa: E402
+
+
+def declared_functions():
+    txt = open(os.path.join(ROOT, "include", "swan.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(swan_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(S.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = C.CDLL(S.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", out), f"{name} not exported as text symbol"
+
+
+def test_row_stride_and_sizes():
+    assert [S.swan_row_stride(k) for k in (1, 7, 8, 9, 16, 24, 32, 33, 64, 100, 128)] == \
+        [8, 8, 8, 16, 16, 32, 32, 64, 64, 128, 128]
+    d = S.make_dims(16, 32, 8, 256, 32, n_cap=32528)
+    n_idx, n_val, n_buf = S.swan_cache_bytes(d)
+    assert n_idx == 16 * 8 * 32528 * 32 and n_val == 2 * n_idx
+    assert n_buf == 16 * 8 * 256 * 128 * 2
+    dp = S.make_dims(32, 32, 8, 64, 64, block_size=16, max_blocks=1024, num_blocks=20000)
+    assert S.swan_cache_bytes(dp)[0] == 20000 * 8 * 16 * 64
+
+
+def test_split_plan():
+    d = S.make_dims(16, 32, 8, 256, 32, n_cap=40000)
+    # 32512 sparse rows + 256 buffered at the first config-3 step
+    S_ = S.swan_decode_num_splits(d, 32767)
+    assert S_ >= 2
+    assert S.swan_decode_workspace_bytes(d, 32767) == 16 * 32 * S_ * 130 * 4
+    d.split_tokens = 1024
+    assert S.swan_decode_num_splits(d, 32767) == 32 + 1  # 32512 / 1024 -> 32 sparse + 1 dense
+    d.R = 0
+    assert S.swan_decode_num_splits(d, 32767) == 32  # no buffer, no dense split
+    assert S.swan_decode_num_splits(S.make_dims(1, 1, 1, 128, 32, n_cap=0), -1) == 1
+
+
+ERROR_CASES = r'''
+import ctypes as C, sys
+sys.path.insert(0, ROOT)
+from decode_attention_compressed_02_amd import swan as S
+L = S.lib()
+F = C.c_void_p(0x1000)  # never dereferenced: every case below must fail validation
+N = None
+def dims(**kw):
+    d = S.make_dims(2, 8, 2, 16, 32, n_cap=100)
+    for k, v in kw.items(): setattr(d, k, v)
+    return d
+cache = S.swan_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None)
+nocache = S.swan_cache(0x1000, 0x1000, None, 0x1000, 0x1000, 0x1000, None)
+st = C.c_void_p(0)
+def proj(d, **kw):
+    a = dict(q=F, k=F, pos=F, P=F, base=10000.0, qh=F, kh=F); a.update(kw)
+    return L.swan_project_qk(C.byref(d), a['q'], a['k'], a['pos'], a['P'], a['base'], a['qh'], a['kh'], st)
+def app(d, c=cache, max_pos=50, **kw):
+    a = dict(pos=F, kh=F, vh=F); a.update(kw)
+    return L.swan_append_evict(C.byref(d), C.byref(c), a['pos'], max_pos, a['kh'], a['vh'], st)
+def dec(d, c=cache, max_pos=50, ws_bytes=1 << 30, **kw):
+    a = dict(pos=F, qh=F, oh=F, ws=F); a.update(kw)
+    return L.swan_decode_attn(C.byref(d), C.byref(c), a['pos'], max_pos, a['qh'], a['oh'], a['ws'], ws_bytes, st)
+def pre(d, c=cache, max_len=40, T=64, **kw):
+    a = dict(len=F, kr=F, vh=F, P=F); a.update(kw)
+    return L.swan_prefill_convert(C.byref(d), C.byref(c), a['len'], max_len, T, a['kr'], a['vh'], a['P'], 10000.0, st)
+E, U, CAP = S.SWAN_ERR_INVALID_ARG, S.SWAN_ERR_UNSUPPORTED, S.SWAN_ERR_CAPACITY
+cases = [
+    ("d_h 64", proj(dims(d_h=64)), U),
+    ("g = 3", proj(dims(N_h=6, H_kv=2)), U),
+    ("g = 16", proj(dims(N_h=32, H_kv=2)), U),
+    ("N_h % H_kv", proj(dims(N_h=7, H_kv=2)), E),
+    ("k = 0", proj(dims(k=0)), E),
+    ("k > d_h", proj(dims(k=129)), E),
+    ("R < 0", proj(dims(R=-1)), E),
+    ("B = 0", proj(dims(B=0)), E),
+    ("split_tokens not /64", dec(dims(split_tokens=100)), E),
+    ("null q", proj(dims(), q=N), E),
+    ("null k_hat out", proj(dims(), kh=N), E),
+    ("rope base 1", proj(dims(), base=1.0), E),
+    ("null dims", L.swan_project_qk(None, F, F, F, F, 10000.0, F, F, st), E),
+    ("append null plane", app(dims(), c=nocache), E),
+    ("append null pos", app(dims(), pos=N), E),
+    ("append capacity", app(dims(), max_pos=100 + 16), CAP),
+    ("append capacity R=0", app(dims(R=0), max_pos=100), CAP),
+    ("paged without table", app(dims(block_size=16, max_blocks=4, num_blocks=8)), E),
+    ("paged capacity", app(dims(block_size=16, max_blocks=4, num_blocks=8),
+                           c=S.swan_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000), max_pos=16 * 4 + 16), CAP),
+    ("decode capacity", dec(dims(), max_pos=100 + 16), CAP),
+    ("decode workspace small", dec(dims(), ws_bytes=16), E),
+    ("decode null workspace", dec(dims(), ws=N), E),
+    ("decode null q_hat", dec(dims(), qh=N), E),
+    ("decode null pos", dec(dims(), pos=N), E),
+    ("prefill capacity", pre(dims(), max_len=100 + 17, T=200), CAP),
+    ("prefill T_stride < max_len", pre(dims(), max_len=70, T=64), E),
+    ("prefill null raw keys", pre(dims(), kr=N), E),
+]
+bad = [(n, got, want) for n, got, want in cases if got != want]
+for n, got, want in bad: print("MISMATCH", n, got, want)
+print("OK" if not bad else "FAIL", len(cases))
+msg = L.swan_last_error().decode()
+assert msg, "no error message recorded"
+'''
+
+
+def test_validation_errors_before_any_launch():
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
+    r = subprocess.run([sys.executable, "-c", f"ROOT = {ROOT!r}\n" + ERROR_CASES], env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.strip().splitlines()[-1].startswith("OK"), r.stdout
+
+
+def test_status_strings():
+    L = S.lib()
+    assert L.swan_status_str(0) == b"SWAN_OK"
+    assert L.swan_status_str(3) == b"SWAN_ERR_CAPACITY"
+    with pytest.raises(S.SwanError) as e:
+        S.swan_cache_bytes(S.make_dims(1, 1, 1, 0, 32, d_h=64))
+    assert e.value.status == S.SWAN_ERR_UNSUPPORTED and "d_h" in str(e.value)
