@@ -84,32 +84,41 @@ swan::SparseGeom geom(const swan_dims *d, const swan_cache *c)
 }
 
 struct Plan {
-    int S_sparse, S_dense, S, TPS;
+    int S, TPS, DPS; // splits; sparse rows and buffered tokens per split
 };
 
-// Split the sparse rows of the longest sequence into ranges of TPS rows and
-// the dense buffer into ranges of kDenseSplit tokens.  Automatic TPS aims at
-// about 2048 sparse waves (8 per CU) so that even short batches fill the chip.
+// Split the sparse rows of the longest sequence into S ranges of TPS rows and
+// spread the buffered tokens over the same S splits (DPS each), so that every
+// wave streams about the same number of bytes.  The automatic TPS sizes the
+// grid to one wave per resident-wave slot of the chip (the split kernel's LDS
+// footprint decides how many fit on a CU).
 Plan plan(const swan_dims *d, int32_t max_pos)
 {
     const int64_t ctx = (int64_t)max_pos + 1;
     int64_t n_max = ctx > d->R ? ctx - d->R : 0;
     if (n_max > row_cap(d)) n_max = row_cap(d);
     const int64_t fill = ctx <= 0 ? 0 : (ctx < d->R ? ctx : d->R);
+    const int g = d->N_h / d->H_kv, ks = row_stride(d->k);
     Plan p;
     int64_t tps = d->split_tokens;
     if (tps == 0) {
+        int per_cu = swan::kLdsPerCU / swan::split_lds_bytes(g, ks);
+        if (per_cu > 8) per_cu = 8;
+        if (per_cu < 1) per_cu = 1;
         const int64_t units = (int64_t)d->B * d->H_kv;
-        tps = (n_max * units + 2047) / 2048;
+        tps = (n_max * units + (int64_t)swan::kCUs * per_cu - 1) / ((int64_t)swan::kCUs * per_cu);
+        const int64_t floor_tps = (n_max + swan::kMaxSplits - 1) / swan::kMaxSplits;
+        if (tps < floor_tps) tps = floor_tps;
         tps = (tps + 63) / 64 * 64;
-        if (tps < 256) tps = 256;
-        if (tps > 16384) tps = 16384;
+        if (tps < 64) tps = 64;
     }
     p.TPS = (int)tps;
-    p.S_sparse = (int)((n_max + tps - 1) / tps);
-    p.S_dense = (int)((fill + swan::kDenseSplit - 1) / swan::kDenseSplit);
-    p.S = p.S_sparse + p.S_dense;
-    if (p.S == 0) p.S = 1; // nothing to attend anywhere: one empty split
+    int64_t S = (n_max + tps - 1) / tps;
+    const int64_t s_dense = (fill + swan::kDenseMinSplit - 1) / swan::kDenseMinSplit;
+    if (S < s_dense) S = s_dense;
+    if (S < 1) S = 1; // nothing to attend anywhere: one empty split
+    p.S = (int)(S > INT32_MAX ? INT32_MAX : S);
+    p.DPS = (int)((fill + S - 1) / S);
     return p;
 }
 
@@ -130,6 +139,9 @@ swan_status check_decode(const swan_dims *d, const swan_cache *c, const int32_t 
         return fail(SWAN_ERR_CAPACITY, "max_pos = %d needs %lld sparse rows, capacity is %lld", max_pos,
                     (long long)n_max, (long long)row_cap(d));
     *out = plan(d, max_pos);
+    if (out->S > swan::kMaxSplits)
+        return fail(SWAN_ERR_INVALID_ARG, "split_tokens = %d gives %d splits, at most %d are supported", d->split_tokens,
+                    out->S, swan::kMaxSplits);
     if (!ws) return fail(SWAN_ERR_INVALID_ARG, "workspace is NULL");
     if (ws_bytes < workspace_bytes(d, *out))
         return fail(SWAN_ERR_INVALID_ARG, "workspace of %zu bytes, need %zu", ws_bytes, workspace_bytes(d, *out));
@@ -230,9 +242,10 @@ static swan::SplitArgs split_args(const swan_dims *d, const swan_cache *c, const
     a.N_h = d->N_h;
     a.H = d->H_kv;
     a.R = d->R;
-    a.S_sparse = p.S_sparse;
     a.S = p.S;
     a.TPS = p.TPS;
+    a.DPS = p.DPS;
+    a.k = d->k;
     a.row_cap = (int)row_cap(d);
     a.geom = geom(d, c);
     a.pos = pos;

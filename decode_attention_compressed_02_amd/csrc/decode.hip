@@ -4,60 +4,76 @@
 // the output accumulated from sparse values (scatter-add at the stored
 // indices) and dense values.
 //
-// Pass 1 (k_split): one wavefront per (split, kv head, sequence).  The wave
-// serves all g query heads of the GQA group, so every sparse row streamed
-// from HBM is used g times.  Splits 0..S_sparse-1 cover consecutive ranges
-// of sparse rows; the remaining splits cover the dense buffer.  Each wave
-// keeps an online softmax (running max m, running sum l) and writes
-// (m, l, unnormalised output) per query head.
+// Pass 1 (k_split): one wavefront per (split, kv head, sequence), serving all
+// g query heads of the GQA group, so every row streamed from HBM is used g
+// times.  Split s covers sparse rows [s TPS, (s+1) TPS) and buffered tokens
+// [s DPS, (s+1) DPS) of its sequence; it keeps an online softmax (running max
+// m, running sum l) and writes (m, l, unnormalised output) per query head.
 //
-// Sparse streaming layout: a row is k_stride entries, 8 entries per lane,
-// LPT = k_stride / 8 lanes per token, 64 / LPT tokens per wave iteration.
-// Lane i of the wave loads bytes [8i, 8i+8) of the iteration's index block
-// and bytes [16i, 16i+16) of its value block, so each wave load instruction
-// reads one contiguous 512 B / 1 KiB span of a plane.
+// Sparse stream: a stored row is KS entries (uint8 index, fp16 value).  A
+// lane loads E consecutive entries of one row from each of the four planes
+// (K index, K value, V index, V value), KS / E lanes share a row and TPI =
+// 64 E / KS rows are in flight per wave iteration, so each wave load
+// instruction reads one contiguous span of a plane.  Loads run D iterations
+// ahead of the arithmetic (a register ring), which keeps enough bytes in
+// flight per wave to cover HBM latency at two waves per SIMD.
 //
-// The scaled q_hat of the group sits in LDS as qs[c][g] (one 16-byte read per
-// gathered index for g = 4).  The output accumulator sits in LDS as
-// acc[c][g] and is updated with LDS float atomics, since lanes of different
-// tokens may hit the same coordinate in one instruction.  Scores are in
-// base-2 units (q_hat pre-scaled by log2(e)/sqrt(d_h)).  The running max is
-// raised only when a score exceeds it by more than kRescaleSlack, so the
-// accumulator rescale (a pass over LDS) is rare; weights stay below
-// 2^kRescaleSlack.
+// LDS holds the scaled q_hat of the group as qs[c][g] (one 16-byte gather per
+// stored key index for g = 4) and TPI private copies of the output
+// accumulator acc[slot][c][g], one per row slot of an iteration.  The indices
+// of one row are distinct and different slots write different copies, so the
+// value scatter is a plain read-modify-write of 16 bytes per entry with no
+// two lanes of an instruction touching the same address: no LDS atomics
+// (floating-point LDS atomics are an order of magnitude slower than plain
+// accesses on gfx950).  Partial sums over the lanes of a row use DPP row
+// permutes, not LDS.
+//
+// Scores are in base-2 units (q_hat pre-scaled by log2(e)/sqrt(d_h)).  The
+// running max is raised only when a score exceeds it by more than
+// kRescaleSlack, so the accumulator rescale (a pass over LDS) is rare; weights
+// stay below 2^kRescaleSlack.
+//
+// Buffered tokens: 16 lanes per token (8 coordinates each), 4 tokens per
+// iteration, output accumulated in registers and folded into accumulator
+// copy 0 before the sparse rows start.
 //
 // Pass 2 (k_reduce): one workgroup per (query head, sequence) merges the S
-// partials with the usual log-sum-exp weights.
+// partials with log-sum-exp weights.
 #include "swan_internal.h"
 
 namespace swan {
 
 constexpr float kRescaleSlack = 8.0f;
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-template <int G>
-__device__ __forceinline__ void lds_q(const float *__restrict__ qs, int c, float (&q)[G])
+// ---------------------------------------------------------------------------
+// lane-group reductions and small LDS vector accessors
+// ---------------------------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
 {
-    if constexpr (G == 1) {
-        q[0] = qs[c];
-    } else if constexpr (G == 2) {
-        const f32x2 t = *(const f32x2 *)(qs + 2 * c);
-        q[0] = t.x;
-        q[1] = t.y;
-    } else if constexpr (G == 4) {
-        const f32x4 t = *(const f32x4 *)(qs + 4 * c);
-        q[0] = t.x;
-        q[1] = t.y;
-        q[2] = t.z;
-        q[3] = t.w;
-    } else {
-        const f32x4 t0 = *(const f32x4 *)(qs + 8 * c), t1 = *(const f32x4 *)(qs + 8 * c + 4);
-        q[0] = t0.x; q[1] = t0.y; q[2] = t0.z; q[3] = t0.w;
-        q[4] = t1.x; q[5] = t1.y; q[6] = t1.z; q[7] = t1.w;
-    }
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of L consecutive lanes; every lane of a group gets
+// the group's sum.  quad_perm [1,0,3,2] and [2,3,0,1] are xor 1 and xor 2;
+// once each quad holds its sum, the half-row mirror pairs the two quads of
+// an 8-lane group and the row mirror pairs the two halves of a 16-lane row.
+template <int L>
+__device__ __forceinline__ float group_sum(float x)
+{
+    if constexpr (L >= 2) x += dpp<0xB1>(x);
+    if constexpr (L >= 4) x += dpp<0x4E>(x);
+    if constexpr (L >= 8) x += dpp<0x141>(x);
+    if constexpr (L >= 16) x += dpp<0x140>(x);
+    if constexpr (L >= 32) x += __shfl_xor(x, 16);
+    if constexpr (L >= 64) x += __shfl_xor(x, 32);
+    return x;
 }
 
 __device__ __forceinline__ float wave_max(float x)
@@ -74,35 +90,144 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
-__device__ __forceinline__ void lds_add(float *p, float v)
+// G consecutive floats of LDS at p (16-byte aligned for G >= 4)
+template <int G>
+__device__ __forceinline__ void lds_get(const float *p, float (&v)[G])
 {
-    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if constexpr (G == 1) {
+        v[0] = p[0];
+    } else if constexpr (G == 2) {
+        const f32x2 t = *(const f32x2 *)p;
+        v[0] = t.x;
+        v[1] = t.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < G; i += 4) {
+            const f32x4 t = *(const f32x4 *)(p + i);
+            v[i] = t.x;
+            v[i + 1] = t.y;
+            v[i + 2] = t.z;
+            v[i + 3] = t.w;
+        }
+    }
 }
 
-struct Chunk {
-    uint64_t ki, vi;
-    u32x4 kv, vv;
+template <int G>
+__device__ __forceinline__ void lds_put(float *p, const float (&v)[G])
+{
+    if constexpr (G == 1) {
+        p[0] = v[0];
+    } else if constexpr (G == 2) {
+        *(f32x2 *)p = (f32x2){v[0], v[1]};
+    } else {
+#pragma unroll
+        for (int i = 0; i < G; i += 4) *(f32x4 *)(p + i) = (f32x4){v[i], v[i + 1], v[i + 2], v[i + 3]};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// streaming loads of NB bytes into 32-bit words (non-temporal: every byte of
+// the history is read once per step)
+// ---------------------------------------------------------------------------
+
+template <int NB>
+struct Words {
+    static constexpr int N = NB < 4 ? 1 : NB / 4;
+    uint32_t w[N];
 };
 
-template <int G, int LPT, bool PAGED>
+template <int NB>
+__device__ __forceinline__ void load_words(const void *p, Words<NB> &o)
+{
+    if constexpr (NB == 1) {
+        o.w[0] = __builtin_nontemporal_load((const uint8_t *)p);
+    } else if constexpr (NB == 2) {
+        o.w[0] = __builtin_nontemporal_load((const uint16_t *)p);
+    } else if constexpr (NB == 4) {
+        o.w[0] = __builtin_nontemporal_load((const uint32_t *)p);
+    } else if constexpr (NB == 8) {
+        const u32x2 t = __builtin_nontemporal_load((const u32x2 *)p);
+        o.w[0] = t.x;
+        o.w[1] = t.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < NB / 16; ++i) {
+            const u32x4 t = __builtin_nontemporal_load((const u32x4 *)p + i);
+            o.w[4 * i] = t.x;
+            o.w[4 * i + 1] = t.y;
+            o.w[4 * i + 2] = t.z;
+            o.w[4 * i + 3] = t.w;
+        }
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ int byte_at(const Words<NB> &o, int e)
+{
+    return (int)((o.w[e >> 2] >> ((e & 3) * 8)) & 0xffu);
+}
+
+template <int NB>
+__device__ __forceinline__ float half_at(const Words<NB> &o, int e)
+{
+    return h2f((uint16_t)(o.w[e >> 1] >> ((e & 1) * 16)));
+}
+
+// E entries of one sparse row from the four planes
+template <int E>
+struct Stage {
+    Words<E> ki, vi;
+    Words<2 * E> kv, vv;
+    bool ok; // the row's block-table entry is a block of the pool
+};
+
+// ---------------------------------------------------------------------------
+// pass 1
+// ---------------------------------------------------------------------------
+
+// Ring depth of the sparse stream: about kInflightBytes per lane in flight
+// (6 E bytes per row slice), between 2 and 8 slots.
+#ifndef SWAN_INFLIGHT_BYTES
+#define SWAN_INFLIGHT_BYTES 192
+#endif
+__host__ __device__ constexpr int split_depth(int E)
+{
+    const int d = (SWAN_INFLIGHT_BYTES + 6 * E - 1) / (6 * E);
+    return d < 2 ? 2 : (d > 8 ? 8 : d);
+}
+
+template <int G, int KS, bool PAGED>
 __global__ __launch_bounds__(64) void k_split(SplitArgs a)
 {
-    constexpr int TPC = kWave / LPT; // tokens per wave iteration
+    constexpr int E = split_entries(G, KS);
+    constexpr int LPT = KS / E;     // lanes per row
+    constexpr int TPI = kWave / LPT; // rows per iteration = accumulator copies
+    constexpr int D = split_depth(E);
+    constexpr int NACC = TPI * kD * G;
+    static_assert(LPT * E == KS && TPI * LPT == kWave, "bad split shape");
+    static_assert(split_lds_bytes(G, KS) == 4 * (kD * G + NACC), "host and device disagree on LDS size");
+
+    __shared__ __attribute__((aligned(16))) float qs[kD * G];
+    __shared__ __attribute__((aligned(16))) float acc[NACC];
+
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
-    __shared__ __attribute__((aligned(16))) float qs[kD * G];
-    __shared__ __attribute__((aligned(16))) float acc[kD * G];
-
     const int ctx = a.pos[b] + 1; // tokens attended; <= 0 for an inactive sequence
     const int n = min(ctx > a.R ? ctx - a.R : 0, a.row_cap);
     const int fill = max(0, min(ctx, a.R));
 
     const float *qsrc = a.q_hat + ((int64_t)b * a.N_h + h * G) * kD;
-    for (int i = lane; i < kD * G; i += kWave) {
-        const int hh = i / kD, c = i % kD;
-        qs[c * G + hh] = qsrc[i] * kScoreScaleLog2;
-        acc[i] = 0.f;
+    {
+        float qv[2 * G]; // all loads first, then the LDS writes
+#pragma unroll
+        for (int j = 0; j < 2 * G; ++j) qv[j] = qsrc[lane + j * kWave];
+#pragma unroll
+        for (int j = 0; j < 2 * G; ++j) {
+            const int i = lane + j * kWave, hh = i / kD, c = i % kD;
+            qs[c * G + hh] = qv[j] * kScoreScaleLog2;
+        }
     }
+    for (int i = lane * 4; i < NACC; i += kWave * 4) *(f32x4 *)(acc + i) = (f32x4){0.f, 0.f, 0.f, 0.f};
     __syncthreads();
 
     float m[G], l[G];
@@ -111,106 +236,12 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
         m[hh] = -INFINITY;
         l[hh] = 0.f;
     }
-    // partial (b, h*G + hh, split) lives at index pbase + hh * S
-    const int64_t pbase = ((int64_t)b * a.N_h + h * G) * a.S + split;
 
-    if (split < a.S_sparse) {
-        const int t0 = split * a.TPS, t1 = min(t0 + a.TPS, n);
-        const int tl = lane / LPT, sub = lane % LPT;
-        auto load = [&](int r0, Chunk &c) {
-            const int r = r0 + tl;
-            const int64_t off = r < t1 ? row_offset<PAGED>(a.geom, b, h, r) : -1;
-            if (off >= 0) {
-                const int64_t e = off + sub * 8;
-                c.ki = *(const uint64_t *)(a.kidx + e);
-                c.kv = *(const u32x4 *)(a.kval + e);
-                c.vi = *(const uint64_t *)(a.vidx + e);
-                c.vv = *(const u32x4 *)(a.vval + e);
-            } else {
-                c.ki = c.vi = 0;
-                c.kv = c.vv = (u32x4){0u, 0u, 0u, 0u};
-            }
-        };
-        Chunk nx;
-        if (t0 < t1) load(t0, nx);
-        for (int r0 = t0; r0 < t1; r0 += TPC) {
-            const Chunk cur = nx;
-            if (r0 + TPC < t1) load(r0 + TPC, nx);
-            const bool valid = r0 + tl < t1;
-
-            // scores: gather q_hat at the stored key indices
-            float s[G];
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) s[hh] = 0.f;
-            const half8 kvh = __builtin_bit_cast(half8, cur.kv);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int c = (int)((cur.ki >> (8 * i)) & 0xffu);
-                float q[G];
-                lds_q<G>(qs, c, q);
-                const float v = (float)kvh[i];
-#pragma unroll
-                for (int hh = 0; hh < G; ++hh) s[hh] = fmaf(q[hh], v, s[hh]);
-            }
-#pragma unroll
-            for (int o = 1; o < LPT; o <<= 1)
-#pragma unroll
-                for (int hh = 0; hh < G; ++hh) s[hh] += __shfl_xor(s[hh], o);
-            bool need = false;
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                if (!valid) s[hh] = -INFINITY;
-                need |= s[hh] > m[hh] + kRescaleSlack;
-            }
-            if (__any(need)) { // wave-uniform
-                float f[G];
-#pragma unroll
-                for (int hh = 0; hh < G; ++hh) {
-                    const float mn = fmaxf(m[hh], wave_max(s[hh]));
-                    f[hh] = exp2f(m[hh] - mn);
-                    m[hh] = mn;
-                    l[hh] *= f[hh];
-                }
-                float fl = f[0];
-#pragma unroll
-                for (int hh = 1; hh < G; ++hh)
-                    if (lane % G == hh) fl = f[hh];
-                __syncthreads();
-                for (int i = lane; i < kD * G; i += kWave) acc[i] *= fl; // i % G == lane % G
-                __syncthreads();
-            }
-            float w[G];
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                w[hh] = exp2f(s[hh] - m[hh]);
-                if (sub == 0) l[hh] += w[hh];
-            }
-            // outputs: scatter-add weighted values at the stored value indices
-            if (valid) {
-                const half8 vvh = __builtin_bit_cast(half8, cur.vv);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int c = (int)((cur.vi >> (8 * i)) & 0xffu);
-                    const float v = (float)vvh[i];
-#pragma unroll
-                    for (int hh = 0; hh < G; ++hh) lds_add(acc + c * G + hh, w[hh] * v);
-                }
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            const float lt = wave_sum(l[hh]);
-            if (lane == 0) {
-                a.part_ml[(pbase + hh * a.S) * 2] = m[hh];
-                a.part_ml[(pbase + hh * a.S) * 2 + 1] = lt;
-            }
-            for (int c = lane; c < kD; c += kWave) a.part_o[(pbase + hh * a.S) * kD + c] = acc[c * G + hh];
-        }
-    } else {
-        // dense buffer: 16 lanes per token, 8 coordinates per lane, 4 tokens per iteration
-        const int t0 = (split - a.S_sparse) * kDenseSplit, t1 = min(t0 + kDenseSplit, fill);
-        const int tl = lane / 16, c0 = (lane % 16) * 8;
+    // ---- buffered tokens [d0, d1)
+    const int d0 = split * a.DPS, d1 = min(d0 + a.DPS, fill);
+    if (d0 < d1) {
+        constexpr int DD = 4;
+        const int tl = lane >> 4, c0 = (lane & 15) * 8;
         float qr[8][G], ar[8][G];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -220,49 +251,60 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
                 ar[i][hh] = 0.f;
             }
         const int64_t ub = ((int64_t)b * a.H + h) * a.R * kD + c0;
-        for (int t = t0; t < t1; t += 4) {
-            const int tok = t + tl;
-            const bool valid = tok < t1;
-            u32x4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-            if (valid) {
-                kk = *(const u32x4 *)(a.kbuf + ub + (int64_t)tok * kD);
-                vv = *(const u32x4 *)(a.vbuf + ub + (int64_t)tok * kD);
-            }
-            const half8 kh = __builtin_bit_cast(half8, kk), vh = __builtin_bit_cast(half8, vv);
-            float s[G];
+        u32x4 kst[DD], vst[DD];
+        auto dload = [&](int t, u32x4 &kk, u32x4 &vv) {
+            const int tok = min(t + tl, d1 - 1);
+            kk = __builtin_nontemporal_load((const u32x4 *)(a.kbuf + ub + (int64_t)tok * kD));
+            vv = __builtin_nontemporal_load((const u32x4 *)(a.vbuf + ub + (int64_t)tok * kD));
+        };
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                s[hh] = 0.f;
+        for (int d = 0; d < DD; ++d) {
+            dload(d0 + 4 * d, kst[d], vst[d]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // steps past d1 run fully masked; each ring slot is consumed before
+        // it is reloaded so the loop carries no register copies
+        for (int tb = d0; tb < d1; tb += 4 * DD) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) s[hh] = fmaf(qr[i][hh], (float)kh[i], s[hh]);
-            }
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1)
-#pragma unroll
-                for (int hh = 0; hh < G; ++hh) s[hh] += __shfl_xor(s[hh], o);
-            bool need = false;
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                if (!valid) s[hh] = -INFINITY;
-                need |= s[hh] > m[hh] + kRescaleSlack;
-            }
-            if (__any(need)) {
+            for (int d = 0; d < DD; ++d) {
+                const int t = tb + 4 * d;
+                const half8 kh = __builtin_bit_cast(half8, kst[d]), vh = __builtin_bit_cast(half8, vst[d]);
+                const bool valid = t + tl < d1;
+                float s[G];
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) {
-                    const float mn = fmaxf(m[hh], wave_max(s[hh]));
-                    const float f = exp2f(m[hh] - mn);
-                    m[hh] = mn;
-                    l[hh] *= f;
+                    s[hh] = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) ar[i][hh] *= f;
+                    for (int i = 0; i < 8; ++i) s[hh] = fmaf(qr[i][hh], (float)kh[i], s[hh]);
+                    s[hh] = group_sum<16>(s[hh]);
                 }
-            }
+                bool need = false;
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                const float w = exp2f(s[hh] - m[hh]);
-                if ((lane % 16) == 0) l[hh] += w;
+                for (int hh = 0; hh < G; ++hh) {
+                    if (!valid) s[hh] = -INFINITY;
+                    need |= s[hh] > m[hh] + kRescaleSlack;
+                }
+                if (__any(need)) { // wave-uniform
 #pragma unroll
-                for (int i = 0; i < 8; ++i) ar[i][hh] = fmaf(w, (float)vh[i], ar[i][hh]);
+                    for (int hh = 0; hh < G; ++hh) {
+                        const float mn = fmaxf(m[hh], wave_max(s[hh]));
+                        const float f = exp2f(m[hh] - mn);
+                        m[hh] = mn;
+                        l[hh] *= f;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) ar[i][hh] *= f;
+                    }
+                }
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) {
+                    const float w = valid ? exp2f(s[hh] - m[hh]) : 0.f;
+                    if ((lane & 15) == 0) l[hh] += w;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) ar[i][hh] = fmaf(w, (float)vh[i], ar[i][hh]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                dload(t + 4 * DD, kst[d], vst[d]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
@@ -272,54 +314,204 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
                 ar[i][hh] += __shfl_xor(ar[i][hh], 16);
                 ar[i][hh] += __shfl_xor(ar[i][hh], 32);
             }
+        if (tl == 0) { // lanes 0..15 own coordinates c0..c0+7 of copy 0 (still zero)
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            const float lt = wave_sum(l[hh]);
-            if (lane == 0) {
-                a.part_ml[(pbase + hh * a.S) * 2] = m[hh];
-                a.part_ml[(pbase + hh * a.S) * 2 + 1] = lt;
-            }
-            if (tl == 0) {
-                float *dst = a.part_o + (pbase + hh * a.S) * kD + c0;
-                *(f32x4 *)dst = (f32x4){ar[0][hh], ar[1][hh], ar[2][hh], ar[3][hh]};
-                *(f32x4 *)(dst + 4) = (f32x4){ar[4][hh], ar[5][hh], ar[6][hh], ar[7][hh]};
+            for (int i = 0; i < 8; ++i) lds_put<G>(acc + (c0 + i) * G, ar[i]);
+        }
+        __syncthreads();
+    }
+
+    // ---- sparse rows [t0, t1)
+    const int t0 = split * a.TPS, t1 = min(t0 + a.TPS, n);
+    if (t0 < t1) {
+        const int tl = lane / LPT, sub = lane % LPT;
+        float *my_acc = acc + tl * kD * G;
+        // entries at row positions >= k are padding (index 0, value +0): they
+        // add nothing to a score, but their write-back could overwrite the
+        // update of a kept entry at index 0, so they are not written
+        const int kept = a.k - sub * E;
+        auto load = [&](int r0, Stage<E> &st) {
+            const int r = min(r0 + tl, t1 - 1); // rows past t1 re-read the last row (masked below)
+            int64_t off = row_offset<PAGED>(a.geom, b, h, r);
+            st.ok = off >= 0;
+            if (!st.ok) off = 0; // a caller error: read a harmless in-pool address, drop the row
+            const int64_t e = off + sub * E;
+            load_words<E>(a.kidx + e, st.ki);
+            load_words<2 * E>(a.kval + e, st.kv);
+            load_words<E>(a.vidx + e, st.vi);
+            load_words<2 * E>(a.vval + e, st.vv);
+        };
+        // Loads must reach the memory pipeline in ring order: the wait
+        // counter is in-order, so the scheduler barriers keep the compiler
+        // from reordering (or sinking) them, which would turn the waits for
+        // the oldest slot into waits for every load in flight.
+        Stage<E> ring[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            load(t0 + d * TPI, ring[d]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // steps past t1 run fully masked (at most D - 1 per split); each ring
+        // slot is consumed before it is reloaded so the loop carries no
+        // register copies and the loads stay D - 1 steps ahead
+        for (int rb = t0; rb < t1; rb += D * TPI) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int r0 = rb + d * TPI;
+                const Stage<E> &cur = ring[d];
+                const bool valid = (r0 + tl < t1) && cur.ok;
+
+                // scores: gather q_hat at the stored key indices
+                float s[G];
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) s[hh] = 0.f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    float q[G];
+                    lds_get<G>(qs + byte_at(cur.ki, e) * G, q);
+                    const float v = half_at(cur.kv, e);
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) s[hh] = fmaf(q[hh], v, s[hh]);
+                }
+                bool need = false;
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) {
+                    s[hh] = group_sum<LPT>(s[hh]);
+                    if (!valid) s[hh] = -INFINITY;
+                    need |= s[hh] > m[hh] + kRescaleSlack;
+                }
+                if (__any(need)) { // wave-uniform: raise the max, rescale every copy
+                    float f[G];
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) {
+                        const float mn = fmaxf(m[hh], wave_max(s[hh]));
+                        f[hh] = exp2f(m[hh] - mn);
+                        m[hh] = mn;
+                        l[hh] *= f[hh];
+                    }
+                    // a 4-float group at index i covers heads (i + j) % G; i % 8 is (lane & 1) * 4
+                    f32x4 fv;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float x = f[j % G];
+                        if constexpr (G == 8) x = (lane & 1) ? f[4 + j] : f[j];
+                        fv[j] = x;
+                    }
+                    for (int i = lane * 4; i < NACC; i += kWave * 4) *(f32x4 *)(acc + i) *= fv;
+                }
+                float w[G];
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) {
+                    w[hh] = valid ? exp2f(s[hh] - m[hh]) : 0.f; // m may still be -inf
+                    if (sub == 0) l[hh] += w[hh];
+                }
+                // outputs: scatter-add weighted values at the stored value
+                // indices of this row's private accumulator copy
+                float o[E][G];
+#pragma unroll
+                for (int e = 0; e < E; ++e) lds_get<G>(my_acc + byte_at(cur.vi, e) * G, o[e]);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float v = half_at(cur.vv, e);
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) o[e][hh] = fmaf(w[hh], v, o[e][hh]);
+                }
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if (e < kept) lds_put<G>(my_acc + byte_at(cur.vi, e) * G, o[e]);
+                __builtin_amdgcn_sched_barrier(0);
+                load(r0 + D * TPI, ring[d]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+    }
+    __syncthreads();
+
+    // ---- partials: (m, l) and the sum of the accumulator copies
+    const int64_t pbase = ((int64_t)b * a.N_h + h * G) * a.S + split; // + hh * S per head
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        const float lt = wave_sum(l[hh]);
+        if (lane == 0) {
+            a.part_ml[(pbase + hh * a.S) * 2] = m[hh];
+            a.part_ml[(pbase + hh * a.S) * 2 + 1] = lt;
+        }
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int c = lane + half * kWave;
+        float o[G], t[G];
+        lds_get<G>(acc + c * G, o);
+#pragma unroll
+        for (int cp = 1; cp < TPI; ++cp) {
+            lds_get<G>(acc + (cp * kD + c) * G, t);
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) o[hh] += t[hh];
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) a.part_o[(pbase + hh * a.S) * kD + c] = o[hh];
     }
 }
 
-// Merge the S partials of one (query head, sequence).  Thread c owns output
-// coordinate c.  An all-empty head (inactive sequence) yields zeros.
+// ---------------------------------------------------------------------------
+// pass 2: merge the S partials of one (query head, sequence).  Thread c owns
+// output coordinate c.  An all-empty head (inactive sequence) yields zeros.
+// ---------------------------------------------------------------------------
+
 __global__ __launch_bounds__(128) void k_reduce(ReduceArgs a)
 {
-    const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+    __shared__ float wsh[kMaxSplits];
+    __shared__ float red[4];
+    const int hq = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
     const int64_t base = ((int64_t)b * a.N_h + hq) * a.S;
+
     float mx = -INFINITY;
-    for (int s = 0; s < a.S; ++s) mx = fmaxf(mx, a.part_ml[(base + s) * 2]);
-    float o = 0.f, L = 0.f;
-    if (mx != -INFINITY) {
-        for (int s = 0; s < a.S; ++s) {
-            const float ms = a.part_ml[(base + s) * 2];
-            if (ms == -INFINITY) continue;
-            const float w = exp2f(ms - mx);
-            L = fmaf(w, a.part_ml[(base + s) * 2 + 1], L);
-            o = fmaf(w, a.part_o[(base + s) * kD + c], o);
-        }
-        o /= L;
+    for (int s = t; s < a.S; s += 128) mx = fmaxf(mx, a.part_ml[(base + s) * 2]);
+    mx = wave_max(mx);
+    if ((t & 63) == 0) red[t >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(red[0], red[1]);
+
+    float L = 0.f;
+    for (int s = t; s < a.S; s += 128) {
+        const float ms = a.part_ml[(base + s) * 2];
+        const float w = ms == -INFINITY ? 0.f : exp2f(ms - mx);
+        wsh[s] = w;
+        L = fmaf(w, a.part_ml[(base + s) * 2 + 1], L);
     }
-    a.o_hat[((int64_t)b * a.N_h + hq) * kD + c] = o;
+    L = wave_sum(L);
+    if ((t & 63) == 0) red[2 + (t >> 6)] = L;
+    __syncthreads();
+    L = red[2] + red[3];
+
+    const float *po = a.part_o + base * kD + t;
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    int s = 0;
+    for (; s + 4 <= a.S; s += 4) {
+        o0 = fmaf(wsh[s], po[(int64_t)s * kD], o0);
+        o1 = fmaf(wsh[s + 1], po[(int64_t)(s + 1) * kD], o1);
+        o2 = fmaf(wsh[s + 2], po[(int64_t)(s + 2) * kD], o2);
+        o3 = fmaf(wsh[s + 3], po[(int64_t)(s + 3) * kD], o3);
+    }
+    for (; s < a.S; ++s) o0 = fmaf(wsh[s], po[(int64_t)s * kD], o0);
+    const float o = (o0 + o1) + (o2 + o3);
+    a.o_hat[((int64_t)b * a.N_h + hq) * kD + t] = mx == -INFINITY ? 0.f : o / L;
 }
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
 
 template <int G, bool PAGED>
 static hipError_t launch_split_g(const SplitArgs &a, hipStream_t s)
 {
     const dim3 grid(a.S, a.H, a.B), block(kWave);
-    switch (a.geom.ks / 8) {
-    case 1: hipLaunchKernelGGL((k_split<G, 1, PAGED>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_split<G, 2, PAGED>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_split<G, 4, PAGED>), grid, block, 0, s, a); break;
+    switch (a.geom.ks) {
     case 8: hipLaunchKernelGGL((k_split<G, 8, PAGED>), grid, block, 0, s, a); break;
     case 16: hipLaunchKernelGGL((k_split<G, 16, PAGED>), grid, block, 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_split<G, 32, PAGED>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_split<G, 64, PAGED>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((k_split<G, 128, PAGED>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -339,6 +531,7 @@ hipError_t launch_split(const SplitArgs &a, int g, hipStream_t s)
 
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s)
 {
+    if (a.S > kMaxSplits) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_reduce, dim3(a.N_h, a.B), dim3(kD), 0, s, a);
     return hipGetLastError();
 }

@@ -11,7 +11,10 @@ namespace swan {
 
 constexpr int kD = 128;          // head dimension (indices fit in 8 bits)
 constexpr int kWave = 64;        // CDNA wavefront
-constexpr int kDenseSplit = 256; // buffered tokens per dense split
+constexpr int kCUs = 256;          // MI355X compute units (launch sizing only)
+constexpr int kLdsPerCU = 160 * 1024;
+constexpr int kMaxSplits = 1024;   // splits per (sequence, kv head) in one decode
+constexpr int kDenseMinSplit = 64; // buffered tokens per split when there are few sparse rows
 
 // log2(e) / sqrt(128): scores are kept in base-2 units so softmax uses exp2
 constexpr float kScoreScaleLog2 = 0.12751743074573063f;
@@ -121,10 +124,30 @@ struct AppendArgs {
 };
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 
+// Shape of the sparse stream in the split kernel for GQA group G and stored
+// row width KS: every lane loads E consecutive entries of one row per
+// iteration, KS / E lanes share a row, and 64 E / KS rows (tokens) are in
+// flight per wave iteration.  Each of those token slots owns a private copy
+// of the output accumulator in LDS, so value scatter-adds never collide
+// within one instruction and need no atomics.
+__host__ __device__ constexpr int split_entries(int G, int KS)
+{
+    const int slots = G <= 2 ? 16 : (G == 4 ? 8 : 4);
+    const int e = KS * slots / 64;
+    return e < 1 ? 1 : (e > 16 ? 16 : e);
+}
+__host__ __device__ constexpr int split_token_slots(int G, int KS) { return 64 * split_entries(G, KS) / KS; }
+// LDS bytes of one split workgroup: the scaled queries plus the accumulator copies
+__host__ __device__ constexpr int split_lds_bytes(int G, int KS)
+{
+    return 4 * kD * G * (1 + split_token_slots(G, KS));
+}
+
 struct SplitArgs {
     int B, N_h, H, R;
-    int S_sparse, S, TPS;
-    int row_cap; // sparse rows addressable per unit
+    int S, TPS, DPS; // splits; sparse rows and buffered tokens per split
+    int k;           // kept entries per row; entries k..ks-1 are padding
+    int row_cap;     // sparse rows addressable per unit
     SparseGeom geom;
     const int32_t *pos;
     const float *q_hat;

@@ -58,7 +58,9 @@
  *                   slot t % block_size of block block_table[b][t / block_size]
  *   dense buffer:
  *     k_buf, v_buf  fp16    [B][H_kv][R][128], slot = position mod R
- * Kept entries of a row are stored with ascending indices.
+ * Kept entries of a row are stored with ascending, distinct indices (as
+ * swan_append_evict and swan_prefill_convert write them); swan_decode_attn
+ * relies on the indices of a row being distinct.
  */
 #ifndef SWAN_H
 #define SWAN_H

@@ -47,15 +47,22 @@ def test_row_stride_and_sizes():
 
 def test_split_plan():
     d = S.make_dims(16, 32, 8, 256, 32, n_cap=40000)
-    # 32512 sparse rows + 256 buffered at the first config-3 step
+    # 32512 sparse rows + 256 buffered at the first step of the batch-16 32K
+    # workload: one wave per resident slot (8 per CU on 256 CUs) -> 2048
+    # waves over 128 (sequence, kv head) units -> 16 splits of 2048 rows
     S_ = S.swan_decode_num_splits(d, 32767)
-    assert S_ >= 2
+    assert S_ == 16
     assert S.swan_decode_workspace_bytes(d, 32767) == 16 * 32 * S_ * 130 * 4
     d.split_tokens = 1024
-    assert S.swan_decode_num_splits(d, 32767) == 32 + 1  # 32512 / 1024 -> 32 sparse + 1 dense
+    assert S.swan_decode_num_splits(d, 32767) == 32  # 32512 / 1024; buffered tokens ride along (8 per split)
     d.R = 0
-    assert S.swan_decode_num_splits(d, 32767) == 32  # no buffer, no dense split
+    assert S.swan_decode_num_splits(d, 32767) == 32
     assert S.swan_decode_num_splits(S.make_dims(1, 1, 1, 128, 32, n_cap=0), -1) == 1
+    # only buffered tokens (context <= R): 64 per split
+    assert S.swan_decode_num_splits(S.make_dims(2, 8, 2, 256, 32, n_cap=10), 199) == 4
+    # a split count above the supported maximum is refused
+    d2 = S.make_dims(1, 1, 1, 0, 32, n_cap=1 << 20, split_tokens=64)
+    assert S.swan_decode_num_splits(d2, (1 << 20) - 1) == (1 << 20) // 64
 
 
 ERROR_CASES = r'''
@@ -111,6 +118,7 @@ cases = [
     ("decode null workspace", dec(dims(), ws=N), E),
     ("decode null q_hat", dec(dims(), qh=N), E),
     ("decode null pos", dec(dims(), pos=N), E),
+    ("decode too many splits", dec(dims(split_tokens=64, n_cap=1 << 20), max_pos=(1 << 20) - 1), E),
     ("prefill capacity", pre(dims(), max_len=100 + 17, T=200), CAP),
     ("prefill T_stride < max_len", pre(dims(), max_len=70, T=64), E),
     ("prefill null raw keys", pre(dims(), kr=N), E),
