@@ -20,13 +20,15 @@
 //
 // LDS holds the scaled q_hat of the group as qs[c][g] (one 16-byte gather per
 // stored key index for g = 4) and TPI private copies of the output
-// accumulator acc[slot][c][g], one per row slot of an iteration.  The indices
-// of one row are distinct and different slots write different copies, so the
-// value scatter is a plain read-modify-write of 16 bytes per entry with no
-// two lanes of an instruction touching the same address: no LDS atomics
-// (floating-point LDS atomics are an order of magnitude slower than plain
-// accesses on gfx950).  Partial sums over the lanes of a row use DPP row
-// permutes, not LDS.
+// accumulator, one per row slot of an iteration, interleaved as
+// acc[c][slot][g].  The indices of one row are distinct and different slots
+// write different copies, so the value scatter is a plain read-modify-write
+// of 16 bytes per entry with no two lanes of an instruction touching the same
+// address: no LDS atomics (floating-point LDS atomics are an order of
+// magnitude slower than plain accesses on gfx950).  Lane l serves slot
+// l % TPI; with TPI = 16 the 16 lanes of each 128-bit LDS phase fall in 16
+// different bank quads, so the scatter has no bank conflicts.  Partial sums
+// over the lanes of a row use DPP and the gfx950 permlane swaps, not LDS.
 //
 // Scores are in base-2 units (q_hat pre-scaled by log2(e)/sqrt(d_h)).  The
 // running max is raised only when a score exceeds it by more than
@@ -74,6 +76,35 @@ __device__ __forceinline__ float group_sum(float x)
     if constexpr (L >= 32) x += __shfl_xor(x, 16);
     if constexpr (L >= 64) x += __shfl_xor(x, 32);
     return x;
+}
+
+// Sum over the lanes that share lane % TPI (TPI = 8 or 16): row_ror:8 pairs
+// lanes 8 apart inside a 16-lane row, the permlane swaps pair rows 16 and 32
+// lanes apart.  Every lane of a group adds the same operands in the same
+// order, so all of them hold the bit-identical sum.
+//
+// __builtin_bit_cast applied directly to an element of the returned vector
+// reads element 0 whatever the index, so the elements are copied out first.
+__device__ __forceinline__ float swap_sum16(float x)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const unsigned a = r[0], b = r[1];
+    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float swap_sum32(float x)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const unsigned a = r[0], b = r[1];
+    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+template <int TPI>
+__device__ __forceinline__ float slot_sum(float x)
+{
+    static_assert(TPI == 8 || TPI == 16, "slot_sum covers 8 or 16 slots");
+    if constexpr (TPI == 8) x += dpp<0x128>(x);
+    return swap_sum32(swap_sum16(x));
 }
 
 __device__ __forceinline__ float wave_max(float x)
@@ -173,13 +204,32 @@ __device__ __forceinline__ float half_at(const Words<NB> &o, int e)
     return h2f((uint16_t)(o.w[e >> 1] >> ((e & 1) * 16)));
 }
 
-// E entries of one sparse row from the four planes
+// E entries of one sparse row: the key planes and the value planes are
+// separate ring slots (consumed in different phases)
 template <int E>
-struct Stage {
-    Words<E> ki, vi;
-    Words<2 * E> kv, vv;
+struct KSlot {
+    Words<E> ki;
+    Words<2 * E> kv;
     bool ok; // the row's block-table entry is a block of the pool
 };
+template <int E>
+struct VSlot {
+    Words<E> vi;
+    Words<2 * E> vv;
+};
+
+// 2^x with the hardware instruction: arguments are <= kRescaleSlack, and
+// results that would be denormal (x < -126) only ever weigh a token that is
+// 2^-126 of the running max, so flushing them to zero is harmless
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// running-max value meaning "no score yet": finite, so exp2(-inf - kNoScore)
+// is 0 rather than NaN, and far below any real score
+constexpr float kNoScore = -1e30f;
+
+// sched_barrier mask: ALU, transcendental and LDS instructions may move
+// across, global loads may not (keeps ring loads in issue order)
+constexpr int kKeepLoadOrder = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0x200 | 0x400;
 
 // ---------------------------------------------------------------------------
 // pass 1
@@ -196,7 +246,7 @@ __host__ __device__ constexpr int split_depth(int E)
     return d < 2 ? 2 : (d > 8 ? 8 : d);
 }
 
-template <int G, int KS, bool PAGED>
+template <int G, int KS, bool PAGED, bool PAD>
 __global__ __launch_bounds__(64) void k_split(SplitArgs a)
 {
     constexpr int E = split_entries(G, KS);
@@ -230,11 +280,16 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
     for (int i = lane * 4; i < NACC; i += kWave * 4) *(f32x4 *)(acc + i) = (f32x4){0.f, 0.f, 0.f, 0.f};
     __syncthreads();
 
-    float m[G], l[G];
+    // Running max per head, kept finite (kNoScore) so that exp2(s - m) of a
+    // masked score (-inf) is 0 without a NaN guard; ls counts the sparse
+    // weights once per lane of a row (divided by LPT at the end), ld the
+    // buffered weights once per token.
+    float m[G], ls[G], ld[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-        m[hh] = -INFINITY;
-        l[hh] = 0.f;
+        m[hh] = kNoScore;
+        ls[hh] = 0.f;
+        ld[hh] = 0.f;
     }
 
     // ---- buffered tokens [d0, d1)
@@ -260,7 +315,7 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
 #pragma unroll
         for (int d = 0; d < DD; ++d) {
             dload(d0 + 4 * d, kst[d], vst[d]);
-            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
         }
         // steps past d1 run fully masked; each ring slot is consumed before
         // it is reloaded so the loop carries no register copies
@@ -270,41 +325,37 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
                 const int t = tb + 4 * d;
                 const half8 kh = __builtin_bit_cast(half8, kst[d]), vh = __builtin_bit_cast(half8, vst[d]);
                 const bool valid = t + tl < d1;
-                float s[G];
+                float s[G], dm = -INFINITY;
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) {
                     s[hh] = 0.f;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) s[hh] = fmaf(qr[i][hh], (float)kh[i], s[hh]);
-                    s[hh] = group_sum<16>(s[hh]);
+                    const float gs = group_sum<16>(s[hh]); // all lanes take part in the permutes
+                    s[hh] = valid ? gs : -INFINITY;
+                    dm = fmaxf(dm, s[hh] - m[hh]);
                 }
-                bool need = false;
-#pragma unroll
-                for (int hh = 0; hh < G; ++hh) {
-                    if (!valid) s[hh] = -INFINITY;
-                    need |= s[hh] > m[hh] + kRescaleSlack;
-                }
-                if (__any(need)) { // wave-uniform
+                if (__any(dm > kRescaleSlack)) { // wave-uniform
 #pragma unroll
                     for (int hh = 0; hh < G; ++hh) {
                         const float mn = fmaxf(m[hh], wave_max(s[hh]));
-                        const float f = exp2f(m[hh] - mn);
+                        const float f = fast_exp2(m[hh] - mn);
                         m[hh] = mn;
-                        l[hh] *= f;
+                        ld[hh] *= f;
 #pragma unroll
                         for (int i = 0; i < 8; ++i) ar[i][hh] *= f;
                     }
                 }
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) {
-                    const float w = valid ? exp2f(s[hh] - m[hh]) : 0.f;
-                    if ((lane & 15) == 0) l[hh] += w;
+                    const float w = fast_exp2(s[hh] - m[hh]);
+                    if ((lane & 15) == 0) ld[hh] += w;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) ar[i][hh] = fmaf(w, (float)vh[i], ar[i][hh]);
                 }
-                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
                 dload(t + 4 * DD, kst[d], vst[d]);
-                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
             }
         }
 #pragma unroll
@@ -314,114 +365,153 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
                 ar[i][hh] += __shfl_xor(ar[i][hh], 16);
                 ar[i][hh] += __shfl_xor(ar[i][hh], 32);
             }
-        if (tl == 0) { // lanes 0..15 own coordinates c0..c0+7 of copy 0 (still zero)
+        if (tl == 0) { // lanes 0..15 own coordinates c0..c0+7 of slot 0 (still zero)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) lds_put<G>(acc + (c0 + i) * G, ar[i]);
+            for (int i = 0; i < 8; ++i) lds_put<G>(acc + (c0 + i) * TPI * G, ar[i]);
         }
         __syncthreads();
     }
 
     // ---- sparse rows [t0, t1)
+    // Each pass over the ring runs in two phases: scores of all D slots
+    // (K planes; each K slot is reloaded as soon as it is consumed), one
+    // rescale test for the whole pass, then the value scatter of all D
+    // slots (V planes, reloaded likewise).  Neither phase branches, so the
+    // gathers of one slot overlap the arithmetic of the previous one.
     const int t0 = split * a.TPS, t1 = min(t0 + a.TPS, n);
     if (t0 < t1) {
-        const int tl = lane / LPT, sub = lane % LPT;
-        float *my_acc = acc + tl * kD * G;
+        const int tl = lane % TPI, sub = lane / TPI;
+        float *my_acc = acc + tl * G; // coordinate c of this slot: my_acc[c * TPI * G]
+        const uint8_t *kidx = a.kidx, *vidx = a.vidx;
+        const uint16_t *kval = a.kval, *vval = a.vval;
+        if constexpr (!PAGED) { // per-unit base in scalar registers, 32-bit lane offsets
+            const int64_t ub = ((int64_t)b * a.H + h) * a.geom.n_cap * KS;
+            kidx += ub;
+            vidx += ub;
+            kval += ub;
+            vval += ub;
+        }
+        // entry offset of this lane's slice of row r0 + tl (rows past t1
+        // re-read the last row and are masked); paged rows whose block-table
+        // entry is not a block of the pool read block 0 and are dropped
+        auto slice = [&](int r0, bool &ok) -> uint32_t {
+            const int r = min(r0 + tl, t1 - 1);
+            if constexpr (PAGED) {
+                const int blk = a.geom.bt[(int64_t)b * a.geom.max_blocks + r / a.geom.bs];
+                ok = blk >= 0 && blk < a.geom.num_blocks;
+                const int bb = ok ? blk : 0;
+                return (uint32_t)(((bb * a.H + h) * a.geom.bs + r % a.geom.bs) * KS + sub * E);
+            } else {
+                ok = true;
+                return (uint32_t)(r * KS + sub * E);
+            }
+        };
+        KSlot<E> rk[D];
+        VSlot<E> rv[D];
+        auto load_k = [&](int r0, KSlot<E> &st) {
+            const uint32_t o = slice(r0, st.ok);
+            load_words<E>(kidx + o, st.ki);
+            load_words<2 * E>(kval + o, st.kv);
+        };
+        auto load_v = [&](int r0, VSlot<E> &st) {
+            bool ok;
+            const uint32_t o = slice(r0, ok);
+            load_words<E>(vidx + o, st.vi);
+            load_words<2 * E>(vval + o, st.vv);
+        };
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            load_k(t0 + d * TPI, rk[d]);
+            __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            load_v(t0 + d * TPI, rv[d]);
+            __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+        }
         // entries at row positions >= k are padding (index 0, value +0): they
         // add nothing to a score, but their write-back could overwrite the
         // update of a kept entry at index 0, so they are not written
         const int kept = a.k - sub * E;
-        auto load = [&](int r0, Stage<E> &st) {
-            const int r = min(r0 + tl, t1 - 1); // rows past t1 re-read the last row (masked below)
-            int64_t off = row_offset<PAGED>(a.geom, b, h, r);
-            st.ok = off >= 0;
-            if (!st.ok) off = 0; // a caller error: read a harmless in-pool address, drop the row
-            const int64_t e = off + sub * E;
-            load_words<E>(a.kidx + e, st.ki);
-            load_words<2 * E>(a.kval + e, st.kv);
-            load_words<E>(a.vidx + e, st.vi);
-            load_words<2 * E>(a.vval + e, st.vv);
-        };
-        // Loads must reach the memory pipeline in ring order: the wait
-        // counter is in-order, so the scheduler barriers keep the compiler
-        // from reordering (or sinking) them, which would turn the waits for
-        // the oldest slot into waits for every load in flight.
-        Stage<E> ring[D];
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            load(t0 + d * TPI, ring[d]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // steps past t1 run fully masked (at most D - 1 per split); each ring
-        // slot is consumed before it is reloaded so the loop carries no
-        // register copies and the loads stay D - 1 steps ahead
+
         for (int rb = t0; rb < t1; rb += D * TPI) {
+            // phase 1: scores (gather q_hat at the stored key indices)
+            float sc[D][G];
+            float dm = -INFINITY;
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 const int r0 = rb + d * TPI;
-                const Stage<E> &cur = ring[d];
-                const bool valid = (r0 + tl < t1) && cur.ok;
-
-                // scores: gather q_hat at the stored key indices
+                const bool valid = (r0 + tl < t1) && rk[d].ok;
                 float s[G];
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) s[hh] = 0.f;
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     float q[G];
-                    lds_get<G>(qs + byte_at(cur.ki, e) * G, q);
-                    const float v = half_at(cur.kv, e);
+                    lds_get<G>(qs + byte_at(rk[d].ki, e) * G, q);
+                    const float v = half_at(rk[d].kv, e);
 #pragma unroll
                     for (int hh = 0; hh < G; ++hh) s[hh] = fmaf(q[hh], v, s[hh]);
                 }
-                bool need = false;
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) {
-                    s[hh] = group_sum<LPT>(s[hh]);
-                    if (!valid) s[hh] = -INFINITY;
-                    need |= s[hh] > m[hh] + kRescaleSlack;
+                    const float gs = slot_sum<TPI>(s[hh]); // all lanes take part in the permutes
+                    sc[d][hh] = valid ? gs : -INFINITY;
+                    dm = fmaxf(dm, sc[d][hh] - m[hh]);
                 }
-                if (__any(need)) { // wave-uniform: raise the max, rescale every copy
-                    float f[G];
+                __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+                load_k(r0 + D * TPI, rk[d]);
+                __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+            }
+            if (__any(dm > kRescaleSlack)) { // wave-uniform and rare: raise the max, rescale
+                float f[G];
 #pragma unroll
-                    for (int hh = 0; hh < G; ++hh) {
-                        const float mn = fmaxf(m[hh], wave_max(s[hh]));
-                        f[hh] = exp2f(m[hh] - mn);
-                        m[hh] = mn;
-                        l[hh] *= f[hh];
-                    }
-                    // a 4-float group at index i covers heads (i + j) % G; i % 8 is (lane & 1) * 4
-                    f32x4 fv;
+                for (int hh = 0; hh < G; ++hh) {
+                    float mx = sc[0][hh];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float x = f[j % G];
-                        if constexpr (G == 8) x = (lane & 1) ? f[4 + j] : f[j];
-                        fv[j] = x;
-                    }
-                    for (int i = lane * 4; i < NACC; i += kWave * 4) *(f32x4 *)(acc + i) *= fv;
+                    for (int d = 1; d < D; ++d) mx = fmaxf(mx, sc[d][hh]);
+                    const float mn = fmaxf(m[hh], wave_max(mx));
+                    f[hh] = fast_exp2(m[hh] - mn);
+                    m[hh] = mn;
+                    ls[hh] *= f[hh];
+                    ld[hh] *= f[hh];
                 }
+                // a 4-float group at index i covers heads (i + j) % G; i % 8 is (lane & 1) * 4
+                f32x4 fv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float x = f[j % G];
+                    if constexpr (G == 8) x = (lane & 1) ? f[4 + j] : f[j];
+                    fv[j] = x;
+                }
+                for (int i = lane * 4; i < NACC; i += kWave * 4) *(f32x4 *)(acc + i) *= fv;
+            }
+            // phase 2: scatter-add weighted values at the stored value
+            // indices of each row's private accumulator copy
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int r0 = rb + d * TPI;
                 float w[G];
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) {
-                    w[hh] = valid ? exp2f(s[hh] - m[hh]) : 0.f; // m may still be -inf
-                    if (sub == 0) l[hh] += w[hh];
+                    w[hh] = fast_exp2(sc[d][hh] - m[hh]);
+                    ls[hh] += w[hh];
                 }
-                // outputs: scatter-add weighted values at the stored value
-                // indices of this row's private accumulator copy
                 float o[E][G];
 #pragma unroll
-                for (int e = 0; e < E; ++e) lds_get<G>(my_acc + byte_at(cur.vi, e) * G, o[e]);
+                for (int e = 0; e < E; ++e) lds_get<G>(my_acc + byte_at(rv[d].vi, e) * (TPI * G), o[e]);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float v = half_at(cur.vv, e);
+                    const float v = half_at(rv[d].vv, e);
 #pragma unroll
                     for (int hh = 0; hh < G; ++hh) o[e][hh] = fmaf(w[hh], v, o[e][hh]);
                 }
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    if (e < kept) lds_put<G>(my_acc + byte_at(cur.vi, e) * G, o[e]);
-                __builtin_amdgcn_sched_barrier(0);
-                load(r0 + D * TPI, ring[d]);
-                __builtin_amdgcn_sched_barrier(0);
+                    if (!PAD || e < kept) lds_put<G>(my_acc + byte_at(rv[d].vi, e) * (TPI * G), o[e]);
+                __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+                load_v(r0 + D * TPI, rv[d]);
+                __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
             }
         }
     }
@@ -431,7 +521,7 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
     const int64_t pbase = ((int64_t)b * a.N_h + h * G) * a.S + split; // + hh * S per head
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-        const float lt = wave_sum(l[hh]);
+        const float lt = wave_sum(ls[hh]) * (1.0f / LPT) + wave_sum(ld[hh]);
         if (lane == 0) {
             a.part_ml[(pbase + hh * a.S) * 2] = m[hh];
             a.part_ml[(pbase + hh * a.S) * 2 + 1] = lt;
@@ -439,12 +529,14 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
+        // lane walks the slots of its coordinate starting at slot lane % TPI,
+        // so the 16 lanes of an LDS phase read 16 different bank quads
         const int c = lane + half * kWave;
         float o[G], t[G];
-        lds_get<G>(acc + c * G, o);
+        lds_get<G>(acc + (c * TPI + lane % TPI) * G, o);
 #pragma unroll
         for (int cp = 1; cp < TPI; ++cp) {
-            lds_get<G>(acc + (cp * kD + c) * G, t);
+            lds_get<G>(acc + (c * TPI + (lane + cp) % TPI) * G, t);
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) o[hh] += t[hh];
         }
@@ -475,7 +567,7 @@ __global__ __launch_bounds__(128) void k_reduce(ReduceArgs a)
     float L = 0.f;
     for (int s = t; s < a.S; s += 128) {
         const float ms = a.part_ml[(base + s) * 2];
-        const float w = ms == -INFINITY ? 0.f : exp2f(ms - mx);
+        const float w = exp2f(ms - mx);
         wsh[s] = w;
         L = fmaf(w, a.part_ml[(base + s) * 2 + 1], L);
     }
@@ -495,23 +587,32 @@ __global__ __launch_bounds__(128) void k_reduce(ReduceArgs a)
     }
     for (; s < a.S; ++s) o0 = fmaf(wsh[s], po[(int64_t)s * kD], o0);
     const float o = (o0 + o1) + (o2 + o3);
-    a.o_hat[((int64_t)b * a.N_h + hq) * kD + t] = mx == -INFINITY ? 0.f : o / L;
+    a.o_hat[((int64_t)b * a.N_h + hq) * kD + t] = L > 0.f ? o / L : 0.f;
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
+template <int G, int KS, bool PAGED>
+static void launch_split_k(const SplitArgs &a, hipStream_t s)
+{
+    const dim3 grid(a.S, a.H, a.B), block(kWave);
+    if (a.k < KS)
+        hipLaunchKernelGGL((k_split<G, KS, PAGED, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_split<G, KS, PAGED, false>), grid, block, 0, s, a);
+}
+
 template <int G, bool PAGED>
 static hipError_t launch_split_g(const SplitArgs &a, hipStream_t s)
 {
-    const dim3 grid(a.S, a.H, a.B), block(kWave);
     switch (a.geom.ks) {
-    case 8: hipLaunchKernelGGL((k_split<G, 8, PAGED>), grid, block, 0, s, a); break;
-    case 16: hipLaunchKernelGGL((k_split<G, 16, PAGED>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((k_split<G, 32, PAGED>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_split<G, 64, PAGED>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((k_split<G, 128, PAGED>), grid, block, 0, s, a); break;
+    case 8: launch_split_k<G, 8, PAGED>(a, s); break;
+    case 16: launch_split_k<G, 16, PAGED>(a, s); break;
+    case 32: launch_split_k<G, 32, PAGED>(a, s); break;
+    case 64: launch_split_k<G, 64, PAGED>(a, s); break;
+    case 128: launch_split_k<G, 128, PAGED>(a, s); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -125,19 +125,21 @@ struct AppendArgs {
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 
 // Shape of the sparse stream in the split kernel for GQA group G and stored
-// row width KS: every lane loads E consecutive entries of one row per
-// iteration, KS / E lanes share a row, and 64 E / KS rows (tokens) are in
-// flight per wave iteration.  Each of those token slots owns a private copy
-// of the output accumulator in LDS, so value scatter-adds never collide
-// within one instruction and need no atomics.
+// row width KS.  TPI rows (tokens) are in flight per wave iteration, one per
+// accumulator slot, and lane l works on row slot l % TPI; KS / E lanes share
+// a row, each loading E consecutive entries.  A 128-bit LDS access is served
+// in 16-lane phases over 16 bank quads, and the accumulators are laid out as
+// acc[c][slot][g], so with 16 slots the 16 lanes of a phase always hit 16
+// different quads: the value scatter runs without bank conflicts whatever
+// the indices are.  G = 8 keeps 8 slots (LDS size), and very wide rows cap E.
 __host__ __device__ constexpr int split_entries(int G, int KS)
 {
-    const int slots = G <= 2 ? 16 : (G == 4 ? 8 : 4);
+    const int slots = G <= 4 ? 16 : 8;
     const int e = KS * slots / 64;
     return e < 1 ? 1 : (e > 16 ? 16 : e);
 }
 __host__ __device__ constexpr int split_token_slots(int G, int KS) { return 64 * split_entries(G, KS) / KS; }
-// LDS bytes of one split workgroup: the scaled queries plus the accumulator copies
+// LDS bytes of one split workgroup: the scaled queries plus the accumulator slots
 __host__ __device__ constexpr int split_lds_bytes(int G, int KS)
 {
     return 4 * kD * G * (1 + split_token_slots(G, KS));
