@@ -373,11 +373,10 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
     }
 
     // ---- sparse rows [t0, t1)
-    // Each pass over the ring runs in two phases: scores of all D slots
-    // (K planes; each K slot is reloaded as soon as it is consumed), one
-    // rescale test for the whole pass, then the value scatter of all D
-    // slots (V planes, reloaded likewise).  Neither phase branches, so the
-    // gathers of one slot overlap the arithmetic of the previous one.
+    // Rows go in passes of D ring slots x TPI rows.  Key and value planes
+    // sit in separate ring slots: a pass's scores come from the K slots, one
+    // rescale test covers the whole pass, then its values are scattered from
+    // the V slots.  Slots are reloaded as soon as they are consumed.
     const int t0 = split * a.TPS, t1 = min(t0 + a.TPS, n);
     if (t0 < t1) {
         const int tl = lane % TPI, sub = lane / TPI;
@@ -419,6 +418,38 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
             load_words<E>(vidx + o, st.vi);
             load_words<2 * E>(vval + o, st.vv);
         };
+        // entries at row positions >= k are padding (index 0, value +0): they
+        // add nothing to a score, but their write-back could overwrite the
+        // update of a kept entry at index 0, so they are not written
+        const int kept = a.k - sub * E;
+
+        // scores of one ring slot (gather q_hat at the stored key indices);
+        // rows past t1 get -inf
+        auto score = [&](int r0, const KSlot<E> &st, float (&sc)[G]) {
+            const bool valid = (r0 + tl < t1) && st.ok;
+            float q[E][G], s[G]; // all gathers in flight before the first product
+#pragma unroll
+            for (int e = 0; e < E; ++e) lds_get<G>(qs + byte_at(st.ki, e) * G, q[e]);
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) s[hh] = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float v = half_at(st.kv, e);
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) s[hh] = fmaf(q[e][hh], v, s[hh]);
+            }
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+                const float gs = slot_sum<TPI>(s[hh]); // all lanes take part in the permutes
+                sc[hh] = valid ? gs : -INFINITY;
+            }
+        };
+        // Software pipeline over passes of D * TPI rows: while the values of
+        // pass i are scattered, the scores of pass i + 1 are gathered, so the
+        // LDS and memory waits of one overlap the arithmetic of the other.
+        // Ring loads are issued in the order they are consumed (K slot d for
+        // two passes ahead, then V slot d for one pass ahead).
+        constexpr int P = D * TPI;
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             load_k(t0 + d * TPI, rk[d]);
@@ -429,41 +460,23 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
             load_v(t0 + d * TPI, rv[d]);
             __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
         }
-        // entries at row positions >= k are padding (index 0, value +0): they
-        // add nothing to a score, but their write-back could overwrite the
-        // update of a kept entry at index 0, so they are not written
-        const int kept = a.k - sub * E;
+        float sc[D][G];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            score(t0 + d * TPI, rk[d], sc[d]);
+            __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+            load_k(t0 + P + d * TPI, rk[d]);
+            __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+        }
 
-        for (int rb = t0; rb < t1; rb += D * TPI) {
-            // phase 1: scores (gather q_hat at the stored key indices)
-            float sc[D][G];
+        for (int rb = t0; rb < t1; rb += P) {
+            // rescale test for pass rb (wave-uniform, rare)
             float dm = -INFINITY;
 #pragma unroll
-            for (int d = 0; d < D; ++d) {
-                const int r0 = rb + d * TPI;
-                const bool valid = (r0 + tl < t1) && rk[d].ok;
-                float s[G];
+            for (int d = 0; d < D; ++d)
 #pragma unroll
-                for (int hh = 0; hh < G; ++hh) s[hh] = 0.f;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    float q[G];
-                    lds_get<G>(qs + byte_at(rk[d].ki, e) * G, q);
-                    const float v = half_at(rk[d].kv, e);
-#pragma unroll
-                    for (int hh = 0; hh < G; ++hh) s[hh] = fmaf(q[hh], v, s[hh]);
-                }
-#pragma unroll
-                for (int hh = 0; hh < G; ++hh) {
-                    const float gs = slot_sum<TPI>(s[hh]); // all lanes take part in the permutes
-                    sc[d][hh] = valid ? gs : -INFINITY;
-                    dm = fmaxf(dm, sc[d][hh] - m[hh]);
-                }
-                __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-                load_k(r0 + D * TPI, rk[d]);
-                __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-            }
-            if (__any(dm > kRescaleSlack)) { // wave-uniform and rare: raise the max, rescale
+                for (int hh = 0; hh < G; ++hh) dm = fmaxf(dm, sc[d][hh] - m[hh]);
+            if (__any(dm > kRescaleSlack)) {
                 float f[G];
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) {
@@ -486,33 +499,61 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
                 }
                 for (int i = lane * 4; i < NACC; i += kWave * 4) *(f32x4 *)(acc + i) *= fv;
             }
-            // phase 2: scatter-add weighted values at the stored value
-            // indices of each row's private accumulator copy
+            float sn[D][G];
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                const int r0 = rb + d * TPI;
+                // both LDS batches in flight before any arithmetic: the value
+                // reads of pass rb and the key gathers of pass rb + P
+                const KSlot<E> &ks = rk[d];
+                const VSlot<E> &vs = rv[d];
+                float o[E][G], q[E][G];
+#pragma unroll
+                for (int e = 0; e < E; ++e) lds_get<G>(my_acc + byte_at(vs.vi, e) * (TPI * G), o[e]);
+#pragma unroll
+                for (int e = 0; e < E; ++e) lds_get<G>(qs + byte_at(ks.ki, e) * G, q[e]);
+                // values of pass rb
                 float w[G];
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) {
                     w[hh] = fast_exp2(sc[d][hh] - m[hh]);
                     ls[hh] += w[hh];
                 }
-                float o[E][G];
-#pragma unroll
-                for (int e = 0; e < E; ++e) lds_get<G>(my_acc + byte_at(rv[d].vi, e) * (TPI * G), o[e]);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float v = half_at(rv[d].vv, e);
+                    const float v = half_at(vs.vv, e);
 #pragma unroll
                     for (int hh = 0; hh < G; ++hh) o[e][hh] = fmaf(w[hh], v, o[e][hh]);
                 }
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    if (!PAD || e < kept) lds_put<G>(my_acc + byte_at(rv[d].vi, e) * (TPI * G), o[e]);
+                    if (!PAD || e < kept) lds_put<G>(my_acc + byte_at(vs.vi, e) * (TPI * G), o[e]);
+                // scores of pass rb + P
+                const int r1 = rb + P + d * TPI;
+                const bool valid = (r1 + tl < t1) && ks.ok;
+                float sk[G];
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) sk[hh] = 0.f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float v = half_at(ks.kv, e);
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) sk[hh] = fmaf(q[e][hh], v, sk[hh]);
+                }
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) {
+                    const float gs = slot_sum<TPI>(sk[hh]); // all lanes take part in the permutes
+                    sn[d][hh] = valid ? gs : -INFINITY;
+                }
                 __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-                load_v(r0 + D * TPI, rv[d]);
+                load_k(rb + 2 * P + d * TPI, rk[d]);
+                __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+                load_v(rb + P + d * TPI, rv[d]);
                 __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
             }
+#pragma unroll
+            for (int d = 0; d < D; ++d)
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) sc[d][hh] = sn[d][hh];
         }
     }
     __syncthreads();
