@@ -1,0 +1,119 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept with the
+benchmark: per-kernel duration statistics, and HBM traffic per launch of a
+kernel from the FETCH_SIZE / WRITE_SIZE counters.
+
+The counters report KiB per dispatch.  They are calibrated against a plain
+device copy of known size run in the same process (``bench.py
+--copy-calibration-mib``): the scale factor is (bytes the copy must move) /
+(bytes the counter reports for it), separately for reads and writes.
+
+Usage (after the rocprofv3 runs listed in the summary itself):
+  python -m decode_attention_compressed_02_amd.profiling stats <kernel_stats.csv>
+  python -m decode_attention_compressed_02_amd.profiling traffic \\
+      --fetch <fetch counter_collection.csv> --write <write counter_collection.csv> \\
+      --kernel k_split --copy-mib 512 --workload "..." --out profiles/split_kernel_traffic.json
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+# sources that define the split kernel; a traffic figure is valid only for them
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_compressed_02_amd", "csrc", f)
+                  for f in ("decode.hip", "swan_internal.h")]
+COPY_KERNEL_HINT = "copy"  # torch's device-to-device copy kernel names contain this
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stats_table(path: str, top: int = 12) -> str:
+    """Markdown table of a rocprofv3 kernel_stats.csv."""
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = ["| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in rows[:top]:
+        out.append("| {} | {} | {:.2f} | {:.2f} | {:.2f} | {:.1f} |".format(
+            r["Name"][:80].replace("|", "/"), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return "\n".join(out)
+
+
+def _counter_values(path: str, counter: str):
+    """{kernel name: [value per dispatch]} for one counter."""
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def _pick(vals, needle):
+    hits = [v for k, v in vals.items() if needle in k]
+    if not hits:
+        raise SystemExit(f"no kernel matching {needle!r} in counter file")
+    return [x for v in hits for x in v]
+
+
+def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_mib: float, workload: str) -> dict:
+    fetch, write = _counter_values(fetch_csv, "FETCH_SIZE"), _counter_values(write_csv, "WRITE_SIZE")
+    k_fetch, k_write = _pick(fetch, kernel), _pick(write, kernel)
+    copy_bytes = copy_mib * 2 ** 20
+
+    def calib(vals):
+        # the calibration copies are the copy dispatches whose counter is
+        # within a factor 4 of the copy size (setup copies are far smaller)
+        kib = copy_bytes / 1024.0
+        hits = [v for v in _pick(vals, COPY_KERNEL_HINT) if kib / 4 <= v <= kib * 4]
+        if not hits:
+            raise SystemExit("no calibration copy found in counter file")
+        return statistics.mean(hits) * 1024.0
+
+    s_fetch, s_write = copy_bytes / calib(fetch), copy_bytes / calib(write)
+    fb = statistics.mean(k_fetch) * 1024.0 * s_fetch
+    wb = statistics.mean(k_write) * 1024.0 * s_write
+    return {"kernel": kernel, "workload": workload, "kernel_source_sha": kernel_source_hash(),
+            "dispatches": len(k_fetch), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+            "hbm_bytes_per_launch": fb + wb, "copy_calibration_bytes": copy_bytes,
+            "fetch_scale": s_fetch, "write_scale": s_write}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("csv")
+    a.add_argument("--top", type=int, default=12)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", default="k_split")
+    t.add_argument("--copy-mib", type=float, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--out")
+    args = ap.parse_args(argv)
+    if args.cmd == "stats":
+        print(stats_table(args.csv, args.top))
+    else:
+        res = traffic(args.fetch, args.write, args.kernel, args.copy_mib, args.workload)
+        txt = json.dumps(res, indent=1)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(txt + "\n")
+        print(txt)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
