@@ -107,6 +107,63 @@ __device__ __forceinline__ float slot_sum(float x)
     return swap_sum32(swap_sum16(x));
 }
 
+// Transposed row sums for g = 4 and 16 row slots.  Lane l holds partial
+// scores s0..s3 (one per query head) of row slot l % 16; the four lanes of a
+// slot sit in the four 16-lane rows.  Three swaps leave every lane with the
+// full score of one head of its slot: row 0 -> head 0, row 1 -> head 2,
+// row 2 -> head 1, row 3 -> head 3 (transposed_head).  The swap pairs
+// (s0, s2) and (s1, s3) so that each half of a row pair keeps what the other
+// half sends: no selects and no copies.
+__device__ __forceinline__ int transposed_head(int lane)
+{
+    const int row = lane >> 4;
+    return ((row & 1) << 1) | (row >> 1);
+}
+__device__ __forceinline__ float swap16_add(float a, float b)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
+                                                    false, false);
+    const unsigned x = r[0], y = r[1];
+    return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float swap32_add(float a, float b)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
+                                                    false, false);
+    const unsigned x = r[0], y = r[1];
+    return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float transposed_sum4(float s0, float s1, float s2, float s3)
+{
+    // even rows: s0 of the row pair, odd rows: s2; likewise (s1, s3)
+    const float u = swap16_add(s0, s2), v = swap16_add(s1, s3);
+    // lower half keeps u (heads 0 / 2), upper half keeps v (heads 1 / 3)
+    return swap32_add(u, v);
+}
+// Inverse of the transposition: every lane gets the values of heads 0..3 of
+// its row slot from the four lanes that hold them.
+__device__ __forceinline__ void transposed_broadcast4(float x, float (&o)[4])
+{
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false); // (row 2k, row 2k+1)
+    const unsigned a0 = a[0], a1 = a[1];
+    const auto b = __builtin_amdgcn_permlane32_swap(a0, a0, false, false); // heads 0, 1
+    const auto c = __builtin_amdgcn_permlane32_swap(a1, a1, false, false); // heads 2, 3
+    const unsigned b0 = b[0], b1 = b[1], c0 = c[0], c1 = c[1];
+    o[0] = __builtin_bit_cast(float, b0);
+    o[1] = __builtin_bit_cast(float, b1);
+    o[2] = __builtin_bit_cast(float, c0);
+    o[3] = __builtin_bit_cast(float, c1);
+}
+// max over the 16 lanes of a row (every lane gets it)
+__device__ __forceinline__ float row_max16(float x)
+{
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    x = fmaxf(x, dpp<0x141>(x));
+    return fmaxf(x, dpp<0x140>(x));
+}
+
 __device__ __forceinline__ float wave_max(float x)
 {
 #pragma unroll
@@ -256,6 +313,9 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
     constexpr int NACC = TPI * kD * G;
     static_assert(LPT * E == KS && TPI * LPT == kWave, "bad split shape");
     static_assert(split_lds_bytes(G, KS) == 4 * (kD * G + NACC), "host and device disagree on LDS size");
+    // g = 4 with 16 row slots keeps sparse scores transposed, one (row slot,
+    // head) per lane; otherwise every lane of a row slot holds all g scores
+    constexpr bool kT = (G == 4 && TPI == 16);
 
     __shared__ __attribute__((aligned(16))) float qs[kD * G];
     __shared__ __attribute__((aligned(16))) float acc[NACC];
@@ -423,6 +483,34 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
         // update of a kept entry at index 0, so they are not written
         const int kept = a.k - sub * E;
 
+        // Software pipeline over passes of D * TPI rows: while the values of
+        // pass i are scattered, the scores of pass i + 1 are gathered, so the
+        // LDS and memory waits of one overlap the arithmetic of the other.
+        // Ring loads are issued in the order they are consumed (K slot d for
+        // two passes ahead, then V slot d for one pass ahead).
+        constexpr int P = D * TPI;
+        // g = 4 with 16 slots keeps scores transposed (one head per lane):
+        // m_me / ls_me are the running max and weight sum of head hme of
+        // this lane's row slot
+        const int hme = transposed_head(lane);
+        float m_me = kNoScore, ls_me = 0.f;
+        if constexpr (kT) {
+            m_me = m[0];
+#pragma unroll
+            for (int hh = 1; hh < G; ++hh) m_me = hme == hh ? m[hh] : m_me;
+        }
+        auto reduce_scores = [&](float (&sk)[G], bool valid, float (&out)[G]) {
+            if constexpr (kT) {
+                const float t = transposed_sum4(sk[0], sk[1], sk[2], sk[3]);
+                out[0] = valid ? t : -INFINITY;
+            } else {
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) {
+                    const float gs = slot_sum<TPI>(sk[hh]); // all lanes take part in the permutes
+                    out[hh] = valid ? gs : -INFINITY;
+                }
+            }
+        };
         // scores of one ring slot (gather q_hat at the stored key indices);
         // rows past t1 get -inf
         auto score = [&](int r0, const KSlot<E> &st, float (&sc)[G]) {
@@ -438,18 +526,8 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) s[hh] = fmaf(q[e][hh], v, s[hh]);
             }
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                const float gs = slot_sum<TPI>(s[hh]); // all lanes take part in the permutes
-                sc[hh] = valid ? gs : -INFINITY;
-            }
+            reduce_scores(s, valid, sc);
         };
-        // Software pipeline over passes of D * TPI rows: while the values of
-        // pass i are scattered, the scores of pass i + 1 are gathered, so the
-        // LDS and memory waits of one overlap the arithmetic of the other.
-        // Ring loads are issued in the order they are consumed (K slot d for
-        // two passes ahead, then V slot d for one pass ahead).
-        constexpr int P = D * TPI;
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             load_k(t0 + d * TPI, rk[d]);
@@ -473,10 +551,31 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
             // rescale test for pass rb (wave-uniform, rare)
             float dm = -INFINITY;
 #pragma unroll
-            for (int d = 0; d < D; ++d)
+            for (int d = 0; d < D; ++d) {
+                if constexpr (kT) {
+                    dm = fmaxf(dm, sc[d][0] - m_me);
+                } else {
 #pragma unroll
-                for (int hh = 0; hh < G; ++hh) dm = fmaxf(dm, sc[d][hh] - m[hh]);
-            if (__any(dm > kRescaleSlack)) {
+                    for (int hh = 0; hh < G; ++hh) dm = fmaxf(dm, sc[d][hh] - m[hh]);
+                }
+            }
+            if constexpr (kT) {
+                if (__any(dm > kRescaleSlack)) {
+                    float mx = sc[0][0];
+#pragma unroll
+                    for (int d = 1; d < D; ++d) mx = fmaxf(mx, sc[d][0]);
+                    const float mn = fmaxf(m_me, row_max16(mx)); // a row holds one head
+                    const float f_me = fast_exp2(m_me - mn);
+                    m_me = mn;
+                    ls_me *= f_me;
+                    float f[4];
+                    transposed_broadcast4(f_me, f);
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) ld[hh] *= f[hh];
+                    const f32x4 fv = {f[0], f[1], f[2], f[3]};
+                    for (int i = lane * 4; i < NACC; i += kWave * 4) *(f32x4 *)(acc + i) *= fv;
+                }
+            } else if (__any(dm > kRescaleSlack)) {
                 float f[G];
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) {
@@ -513,10 +612,16 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
                 for (int e = 0; e < E; ++e) lds_get<G>(qs + byte_at(ks.ki, e) * G, q[e]);
                 // values of pass rb
                 float w[G];
+                if constexpr (kT) {
+                    const float w_me = fast_exp2(sc[d][0] - m_me);
+                    ls_me += w_me;
+                    transposed_broadcast4(w_me, w);
+                } else {
 #pragma unroll
-                for (int hh = 0; hh < G; ++hh) {
-                    w[hh] = fast_exp2(sc[d][hh] - m[hh]);
-                    ls[hh] += w[hh];
+                    for (int hh = 0; hh < G; ++hh) {
+                        w[hh] = fast_exp2(sc[d][hh] - m[hh]);
+                        ls[hh] += w[hh];
+                    }
                 }
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
@@ -539,11 +644,7 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
 #pragma unroll
                     for (int hh = 0; hh < G; ++hh) sk[hh] = fmaf(q[e][hh], v, sk[hh]);
                 }
-#pragma unroll
-                for (int hh = 0; hh < G; ++hh) {
-                    const float gs = slot_sum<TPI>(sk[hh]); // all lanes take part in the permutes
-                    sn[d][hh] = valid ? gs : -INFINITY;
-                }
+                reduce_scores(sk, valid, sn[d]);
                 __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
                 load_k(rb + 2 * P + d * TPI, rk[d]);
                 __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
@@ -555,6 +656,18 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh) sc[d][hh] = sn[d][hh];
         }
+        if constexpr (kT) {
+            // back to per-head registers: a row holds one head; its 16 lanes
+            // hold the weight sums of the 16 row slots (once each)
+            float mh[4], lh[4];
+            transposed_broadcast4(m_me, mh);
+            transposed_broadcast4(group_sum<16>(ls_me), lh);
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+                m[hh] = mh[hh];
+                ls[hh] = lh[hh]; // the head's whole sum, in every lane
+            }
+        }
     }
     __syncthreads();
 
@@ -562,7 +675,10 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
     const int64_t pbase = ((int64_t)b * a.N_h + h * G) * a.S + split; // + hh * S per head
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-        const float lt = wave_sum(ls[hh]) * (1.0f / LPT) + wave_sum(ld[hh]);
+        // generic path: every lane of a row slot added the slot's weights, so
+        // the wave sum counts each LPT times (exactly: LPT is a power of two)
+        const float lsum = kT ? ls[hh] : wave_sum(ls[hh]) * (1.0f / LPT);
+        const float lt = lsum + wave_sum(ld[hh]);
         if (lane == 0) {
             a.part_ml[(pbase + hh * a.S) * 2] = m[hh];
             a.part_ml[(pbase + hh * a.S) * 2 + 1] = lt;
