@@ -249,10 +249,55 @@ __device__ __forceinline__ void load_words(const void *p, Words<NB> &o)
     }
 }
 
+// NB bytes at byte offset off of a buffer resource (raw, non-temporal).
+// Offsets at or past the resource's size read zeros without touching memory.
+template <int NB>
+__device__ __forceinline__ void buffer_words(__amdgpu_buffer_rsrc_t r, uint32_t off, Words<NB> &o)
+{
+    constexpr int kNT = 2; // cache policy: non-temporal
+    if constexpr (NB == 1) {
+        o.w[0] = __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, kNT);
+    } else if constexpr (NB == 2) {
+        o.w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kNT);
+    } else if constexpr (NB == 4) {
+        o.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNT);
+    } else if constexpr (NB == 8) {
+        const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNT);
+        o.w[0] = t.x;
+        o.w[1] = t.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < NB / 16; ++i) {
+            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, kNT);
+            o.w[4 * i] = t.x;
+            o.w[4 * i + 1] = t.y;
+            o.w[4 * i + 2] = t.z;
+            o.w[4 * i + 3] = t.w;
+        }
+    }
+}
+
+// raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 template <int NB>
 __device__ __forceinline__ int byte_at(const Words<NB> &o, int e)
 {
     return (int)((o.w[e >> 2] >> ((e & 3) * 8)) & 0xffu);
+}
+
+// (index byte e of the row) * 256 + slot_off, for slot_off < 256: one
+// v_perm_b32 puts the index byte in byte 1 and slot_off in byte 0 (bytes 2-3
+// zero).  With acc[c][16 slots][4 heads] of fp32, entry c of slot s sits at
+// byte c * 256 + s * 16.
+template <int NB>
+__device__ __forceinline__ uint32_t acc_offset_256(const Words<NB> &o, int e, uint32_t slot_off)
+{
+    const uint32_t sel = 0x0c0c0000u | ((uint32_t)(4 + (e & 3)) << 8);
+    return __builtin_amdgcn_perm(o.w[e >> 2], slot_off, sel);
 }
 
 template <int NB>
@@ -467,16 +512,34 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
         };
         KSlot<E> rk[D];
         VSlot<E> rv[D];
+        // Contiguous rows: a buffer resource per plane covers rows r0 .. t1-1
+        // (scalar arithmetic); each lane reads its slice at a fixed offset and
+        // rows past t1 read zeros (masked by valid).  Paged rows go through the
+        // block table one row at a time.
+        const uint32_t lane_off = (uint32_t)(tl * KS + sub * E);
         auto load_k = [&](int r0, KSlot<E> &st) {
-            const uint32_t o = slice(r0, st.ok);
-            load_words<E>(kidx + o, st.ki);
-            load_words<2 * E>(kval + o, st.kv);
+            if constexpr (PAGED) {
+                const uint32_t o = slice(r0, st.ok);
+                load_words<E>(kidx + o, st.ki);
+                load_words<2 * E>(kval + o, st.kv);
+            } else {
+                const uint32_t rows = (uint32_t)max(t1 - r0, 0);
+                st.ok = true;
+                buffer_words<E>(buffer_rsrc(kidx + (int64_t)r0 * KS, rows * KS), lane_off, st.ki);
+                buffer_words<2 * E>(buffer_rsrc(kval + (int64_t)r0 * KS, rows * KS * 2), 2 * lane_off, st.kv);
+            }
         };
         auto load_v = [&](int r0, VSlot<E> &st) {
-            bool ok;
-            const uint32_t o = slice(r0, ok);
-            load_words<E>(vidx + o, st.vi);
-            load_words<2 * E>(vval + o, st.vv);
+            if constexpr (PAGED) {
+                bool ok;
+                const uint32_t o = slice(r0, ok);
+                load_words<E>(vidx + o, st.vi);
+                load_words<2 * E>(vval + o, st.vv);
+            } else {
+                const uint32_t rows = (uint32_t)max(t1 - r0, 0);
+                buffer_words<E>(buffer_rsrc(vidx + (int64_t)r0 * KS, rows * KS), lane_off, st.vi);
+                buffer_words<2 * E>(buffer_rsrc(vval + (int64_t)r0 * KS, rows * KS * 2), 2 * lane_off, st.vv);
+            }
         };
         // entries at row positions >= k are padding (index 0, value +0): they
         // add nothing to a score, but their write-back could overwrite the
@@ -606,8 +669,16 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
                 const KSlot<E> &ks = rk[d];
                 const VSlot<E> &vs = rv[d];
                 float o[E][G], q[E][G];
+                float *vaddr[E];
 #pragma unroll
-                for (int e = 0; e < E; ++e) lds_get<G>(my_acc + byte_at(vs.vi, e) * (TPI * G), o[e]);
+                for (int e = 0; e < E; ++e) {
+                    if constexpr (TPI * G * 4 == 256) // 16 slots x 4 heads: one v_perm per address
+                        vaddr[e] = (float *)((char *)acc + acc_offset_256(vs.vi, e, (uint32_t)(tl * G * 4)));
+                    else
+                        vaddr[e] = my_acc + byte_at(vs.vi, e) * (TPI * G);
+                }
+#pragma unroll
+                for (int e = 0; e < E; ++e) lds_get<G>(vaddr[e], o[e]);
 #pragma unroll
                 for (int e = 0; e < E; ++e) lds_get<G>(qs + byte_at(ks.ki, e) * G, q[e]);
                 // values of pass rb
@@ -631,7 +702,7 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
                 }
 #pragma unroll
                 for (int e = 0; e < E; ++e)
-                    if (!PAD || e < kept) lds_put<G>(my_acc + byte_at(vs.vi, e) * (TPI * G), o[e]);
+                    if (!PAD || e < kept) lds_put<G>(vaddr[e], o[e]);
                 // scores of pass rb + P
                 const int r1 = rb + P + d * TPI;
                 const bool valid = (r1 + tl < t1) && ks.ok;
