@@ -50,6 +50,15 @@ def stats_table(path: str, top: int = 12) -> str:
     return "\n".join(out)
 
 
+def last_dispatches(trace_csv: str, kernel: str, last: int):
+    """(mean, min, max) duration in us of the last `last` dispatches of a
+    kernel in a rocprofv3 kernel_trace.csv (in start order)."""
+    rows = [r for r in csv.DictReader(open(trace_csv)) if kernel in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows[-last:]]
+    return statistics.mean(d), min(d), max(d), len(rows)
+
+
 def _counter_values(path: str, counter: str):
     """{kernel name: [value per dispatch]} for one counter."""
     vals = {}
@@ -96,6 +105,10 @@ def main(argv=None):
     a = sub.add_parser("stats")
     a.add_argument("csv")
     a.add_argument("--top", type=int, default=12)
+    l = sub.add_parser("last")
+    l.add_argument("csv", help="kernel_trace.csv")
+    l.add_argument("--kernel", default="k_split")
+    l.add_argument("--n", type=int, default=36, help="dispatches at the end of the run (timed + back-to-back)")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -106,6 +119,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         print(stats_table(args.csv, args.top))
+    elif args.cmd == "last":
+        mean, lo, hi, total = last_dispatches(args.csv, args.kernel, args.n)
+        print(f"{args.kernel}: last {args.n} of {total} dispatches: mean {mean:.2f} us, min {lo:.2f}, max {hi:.2f}")
     else:
         res = traffic(args.fetch, args.write, args.kernel, args.copy_mib, args.workload)
         txt = json.dumps(res, indent=1)
