@@ -3,6 +3,7 @@ cache and the per-step buffers, allocated with torch (device memory only)
 and handed to libswan as raw pointers.  All computation is in libswan."""
 from __future__ import annotations
 
+import numpy as np
 import torch
 
 from . import swan as S
@@ -104,3 +105,148 @@ class SwanDecoder:
         self.project(q, k, pos, stream)
         self.append(pos, max_pos, v_hat, stream)
         return self.decode(pos, max_pos, stream)
+
+
+class PoolExhausted(RuntimeError):
+    """The paged pool has no free block left."""
+
+
+class PagedPool:
+    """Host bookkeeping of a paged sparse pool ("Reuse, Evict, or Limit
+    Earlier Context" sections 1.2-1.4): physical blocks handed out from a free
+    list, a reference count per block (0 free, 1 owned by one sequence, > 1
+    shared and read-only), and one block table per sequence mapping logical
+    block t // block_size to a physical block (-1 = not mapped).
+
+    A write into a shared block is preceded by copy-on-write: a fresh block is
+    taken from the free list, the old block's count drops by one, and the
+    writer's table points to the fresh block; the caller copies the bytes
+    (swan_copy_blocks) before the write."""
+
+    def __init__(self, num_blocks: int, B: int, max_blocks: int, block_size: int, order=None):
+        self.num_blocks, self.B, self.max_blocks, self.block_size = num_blocks, B, max_blocks, block_size
+        self.ref = np.zeros(num_blocks, np.int32)
+        order = np.arange(num_blocks) if order is None else np.asarray(order)
+        if sorted(order.tolist()) != list(range(num_blocks)):
+            raise ValueError("order must be a permutation of the pool's block ids")
+        self._free = [int(x) for x in order[::-1]]  # pop() hands out order[0] first
+        self.table = np.full((B, max_blocks), -1, np.int32)
+        self.version = 0  # bumped whenever a table entry changes
+
+    @property
+    def free_blocks(self) -> int:
+        return len(self._free)
+
+    def alloc(self) -> int:
+        if not self._free:
+            raise PoolExhausted(f"all {self.num_blocks} blocks are in use")
+        blk = self._free.pop()
+        assert self.ref[blk] == 0
+        self.ref[blk] = 1
+        return blk
+
+    def _decref(self, blk: int):
+        self.ref[blk] -= 1
+        assert self.ref[blk] >= 0
+        if self.ref[blk] == 0:
+            self._free.append(int(blk))
+
+    def map_new(self, b: int, logical: int) -> int:
+        """Give sequence b a fresh block for logical block `logical`."""
+        if self.table[b, logical] >= 0:
+            raise ValueError(f"logical block {logical} of sequence {b} is already mapped")
+        blk = self.alloc()
+        self.table[b, logical] = blk
+        self.version += 1
+        return blk
+
+    def share(self, src: int, dst: int, nblocks: int):
+        """Map logical blocks 0..nblocks-1 of sequence dst to the physical
+        blocks of sequence src (a shared prefix); their counts go up."""
+        for lb in range(nblocks):
+            blk = int(self.table[src, lb])
+            if blk < 0:
+                raise ValueError(f"logical block {lb} of sequence {src} is not mapped")
+            if self.table[dst, lb] >= 0:
+                raise ValueError(f"logical block {lb} of sequence {dst} is already mapped")
+            self.table[dst, lb] = blk
+            self.ref[blk] += 1
+        self.version += 1
+
+    def prepare_write(self, b: int, row: int):
+        """Make sparse row `row` of sequence b writable.  Returns (src, dst)
+        when a copy-on-write is needed (the caller must copy block src to dst
+        before writing), else None."""
+        lb = row // self.block_size
+        if lb >= self.max_blocks:
+            raise PoolExhausted(f"row {row} is past the block table ({self.max_blocks} blocks)")
+        blk = int(self.table[b, lb])
+        if blk < 0:
+            self.map_new(b, lb)
+            return None
+        if self.ref[blk] == 1:
+            return None
+        new = self.alloc()  # may raise before anything changed
+        self._decref(blk)
+        self.table[b, lb] = new
+        self.version += 1
+        return blk, new
+
+    def release(self, b: int):
+        """Sequence b finished: drop its references; blocks nobody holds return
+        to the free list."""
+        for lb in range(self.max_blocks):
+            blk = int(self.table[b, lb])
+            if blk >= 0:
+                self._decref(blk)
+                self.table[b, lb] = -1
+        self.version += 1
+
+
+class PagedSwanDecoder(SwanDecoder):
+    """SwanDecoder over a paged pool: before each step the rows the step will
+    append are made writable (block allocation or copy-on-write, copies
+    enqueued with swan_copy_blocks) and the block table is refreshed on the
+    device; then project -> append/evict -> decode as usual."""
+
+    def __init__(self, dims: S.swan_dims, P_qk: torch.Tensor, pool: PagedPool, rope_base: float = 10000.0,
+                 device="cuda"):
+        if dims.block_size != pool.block_size or dims.max_blocks != pool.max_blocks or \
+                dims.num_blocks != pool.num_blocks or dims.B != pool.B:
+            raise ValueError("dims and pool disagree on the paged geometry")
+        self.pool = pool
+        self._bt_version = -1
+        bt = torch.from_numpy(pool.table.copy()).to(device)
+        super().__init__(dims, P_qk, rope_base, device, block_table=bt)
+        self._bt_version = pool.version
+
+    def sync_table(self):
+        if self._bt_version != self.pool.version:
+            self.cache.block_table.copy_(torch.from_numpy(self.pool.table))
+            self._bt_version = self.pool.version
+
+    def prepare_step(self, pos_host, stream=None):
+        """Host side of a step at positions pos_host[b]: returns the number of
+        copy-on-write block copies enqueued."""
+        R = self.dims.R
+        pairs = []
+        for b, p in enumerate(pos_host):
+            p = int(p)
+            if p < 0:
+                continue
+            row = p - R if R > 0 else p
+            if row < 0:
+                continue
+            cp = self.pool.prepare_write(b, row)
+            if cp is not None:
+                pairs.append(cp)
+        if pairs:
+            src = torch.tensor([a for a, _ in pairs], dtype=torch.int32, device=self.device)
+            dst = torch.tensor([c for _, c in pairs], dtype=torch.int32, device=self.device)
+            S.swan_copy_blocks(self.dims, self.cache.struct(), src, dst, stream)
+        self.sync_table()
+        return len(pairs)
+
+    def step_paged(self, q, k, v_hat, pos, pos_host, stream=None):
+        self.prepare_step(pos_host, stream)
+        return self.step(q, k, v_hat, pos, int(max(pos_host)), stream)

@@ -339,4 +339,31 @@ swan_status swan_prefill_convert(const swan_dims *d, const swan_cache *c, const 
     return hip_status(swan::launch_prefill(a, (hipStream_t)stream), "swan_prefill_convert launch");
 }
 
+swan_status swan_copy_blocks(const swan_dims *d, const swan_cache *c, const int32_t *src, const int32_t *dst,
+                             int32_t count, void *stream)
+{
+    swan_status st = check_dims(d);
+    if (st) return st;
+    if (d->block_size <= 0) return fail(SWAN_ERR_INVALID_ARG, "swan_copy_blocks needs the paged layout (block_size > 0)");
+    if ((st = check_cache(d, c, false))) return st;
+    if (count < 0) return fail(SWAN_ERR_INVALID_ARG, "count = %d < 0", count);
+    if (count == 0) return SWAN_OK;
+    if (!src || !dst) return fail(SWAN_ERR_INVALID_ARG, "NULL block id array");
+    if (count > 65535) return fail(SWAN_ERR_INVALID_ARG, "count = %d > 65535", count);
+    if (((int64_t)d->H_kv * d->block_size * row_stride(d->k)) % 16)
+        return fail(SWAN_ERR_UNSUPPORTED, "a block of an index plane (H_kv * block_size * k_stride bytes) must be a "
+                                          "multiple of 16 bytes");
+    swan::CopyBlocksArgs a;
+    a.count = count;
+    a.num_blocks = d->num_blocks;
+    a.block_bytes_idx = (int64_t)d->H_kv * d->block_size * row_stride(d->k);
+    a.kidx = c->k_idx;
+    a.vidx = c->v_idx;
+    a.kval = c->k_val;
+    a.vval = c->v_val;
+    a.src = src;
+    a.dst = dst;
+    return hip_status(swan::launch_copy_blocks(a, (hipStream_t)stream), "swan_copy_blocks launch");
+}
+
 } // extern "C"

@@ -180,4 +180,13 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 
+struct CopyBlocksArgs {
+    int count, num_blocks;
+    int64_t block_bytes_idx; // bytes of one block of an index plane (value planes: twice)
+    uint8_t *kidx, *vidx;
+    uint16_t *kval, *vval;
+    const int32_t *src, *dst;
+};
+hipError_t launch_copy_blocks(const CopyBlocksArgs &a, hipStream_t s);
+
 } // namespace swan

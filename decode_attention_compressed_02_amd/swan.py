@@ -18,7 +18,7 @@ SWAN_OK, SWAN_ERR_INVALID_ARG, SWAN_ERR_UNSUPPORTED, SWAN_ERR_CAPACITY, SWAN_ERR
 
 EXPORTS = ("swan_status_str", "swan_last_error", "swan_row_stride", "swan_cache_bytes", "swan_project_qk",
            "swan_append_evict", "swan_decode_workspace_bytes", "swan_decode_num_splits", "swan_decode_attn",
-           "swan_decode_split", "swan_decode_reduce", "swan_prefill_convert")
+           "swan_decode_split", "swan_decode_reduce", "swan_prefill_convert", "swan_copy_blocks")
 
 
 class SwanError(RuntimeError):
@@ -65,6 +65,7 @@ def lib():
             "swan_decode_split": ([D, Cc, V, I32, V, V, SZ, V], C.c_int),
             "swan_decode_reduce": ([D, V, I32, V, SZ, V, V], C.c_int),
             "swan_prefill_convert": ([D, Cc, V, I32, I64, V, V, V, F, V], C.c_int),
+            "swan_copy_blocks": ([D, Cc, V, V, I32, V], C.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -165,3 +166,12 @@ def swan_prefill_convert(dims, cache, length, max_len, k_raw, v_hat, P_qk, rope_
                                       int(T_stride), _ptr(k_raw, torch.float32, "k_raw"),
                                       _ptr(v_hat, torch.float32, "v_hat"), _ptr(P_qk, torch.float32, "P_qk"),
                                       float(rope_base), _stream(stream)))
+
+
+def swan_copy_blocks(dims, cache, src, dst, stream=None):
+    """Copy paged blocks src[i] -> dst[i] (int32 device tensors of equal length)."""
+    import torch
+    if src.numel() != dst.numel():
+        raise ValueError("src and dst must have the same length")
+    _check(lib().swan_copy_blocks(C.byref(dims), C.byref(cache), _ptr(src, torch.int32, "src"),
+                                  _ptr(dst, torch.int32, "dst"), int(src.numel()), _stream(stream)))

@@ -58,6 +58,7 @@
  *                   slot t % block_size of block block_table[b][t / block_size]
  *   dense buffer:
  *     k_buf, v_buf  fp16    [B][H_kv][R][128], slot = position mod R
+ * Every plane must be 16-byte aligned.
  * Kept entries of a row are stored with ascending, distinct indices (as
  * swan_append_evict and swan_prefill_convert write them); swan_decode_attn
  * relies on the indices of a row being distinct.
@@ -205,6 +206,24 @@ swan_status swan_decode_reduce(const swan_dims *dims, const int32_t *pos, int32_
 swan_status swan_prefill_convert(const swan_dims *dims, const swan_cache *cache, const int32_t *len, int32_t max_len,
                                  int64_t T_stride, const float *k_raw, const float *v_hat, const float *P_qk,
                                  float rope_base, void *stream);
+
+/*
+ * Copy-on-write support for the paged layout ("Reuse, Evict, or Limit
+ * Earlier Context" sections 1.3 and 1.4: a block referenced by more than one
+ * sequence is never written; a writer first copies it to a block it owns).
+ * Copies blocks src[i] -> dst[i], i < count, in all four sparse planes:
+ *   src, dst   int32 [count] (device) block ids of the pool
+ * Reference counts, the free list and the block tables are the caller's
+ * (host) bookkeeping; this call only moves the bytes, asynchronously on
+ * stream.  A pair with an id outside 0..num_blocks-1 or src == dst is
+ * skipped.  The dst blocks must not be read or written by other work on
+ * the stream until the copy is done (stream order guarantees this).
+ * Errors: INVALID_ARG for a contiguous layout, count < 0 or > 65535, or
+ * NULL arrays (count > 0); UNSUPPORTED when H_kv * block_size * k_stride is
+ * not a multiple of 16 (blocks are moved in 16-byte units).
+ */
+swan_status swan_copy_blocks(const swan_dims *dims, const swan_cache *cache, const int32_t *src, const int32_t *dst,
+                             int32_t count, void *stream);
 
 #ifdef __cplusplus
 }

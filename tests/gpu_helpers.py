@@ -23,8 +23,11 @@ def dims_for(oc, split_tokens=0, block_size=0, max_blocks=0, num_blocks=0):
                        split_tokens=split_tokens)
 
 
-def upload(cache: HybridCache, oc, block_table: np.ndarray | None = None):
-    """Write the oracle state `oc` (logical rows) into the GPU planes."""
+def upload(cache: HybridCache, oc, block_table: np.ndarray | None = None, rows=None):
+    """Write the oracle state `oc` (logical rows) into the GPU planes.  In the
+    paged layout only rows < rows[b] of sequence b are written (default: all
+    ncap), so that a short sequence sharing blocks with a longer one does not
+    overwrite the longer one's rows."""
     d, ks, k = cache.dims, cache.k_stride, oc.k
     planes = cache.sparse_views()
     src = (oc.kidx, oc.kval.astype(np.float16), oc.vidx, oc.vval.astype(np.float16))
@@ -35,7 +38,7 @@ def upload(cache: HybridCache, oc, block_table: np.ndarray | None = None):
         else:
             bs = d.block_size
             for b in range(oc.B):
-                for r in range(oc.ncap):
+                for r in range(oc.ncap if rows is None else rows[b]):
                     blk = block_table[b, r // bs]
                     if blk >= 0:
                         host[blk, :, r % bs, :k] = s[b, :, r]

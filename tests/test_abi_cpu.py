@@ -123,6 +123,16 @@ cases = [
     ("prefill capacity", pre(dims(), max_len=100 + 17, T=200), CAP),
     ("prefill T_stride < max_len", pre(dims(), max_len=70, T=64), E),
     ("prefill null raw keys", pre(dims(), kr=N), E),
+    ("copy blocks contiguous", L.swan_copy_blocks(C.byref(dims()), C.byref(cache), F, F, 1, st), E),
+    ("copy blocks count < 0", L.swan_copy_blocks(C.byref(dims(block_size=16, max_blocks=4, num_blocks=8)),
+                                                 C.byref(S.swan_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)),
+                                                 F, F, -1, st), E),
+    ("copy blocks null ids", L.swan_copy_blocks(C.byref(dims(block_size=16, max_blocks=4, num_blocks=8)),
+                                                C.byref(S.swan_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)),
+                                                N, F, 2, st), E),
+    ("copy blocks odd block bytes", L.swan_copy_blocks(C.byref(dims(H_kv=1, N_h=1, k=8, block_size=1, max_blocks=4, num_blocks=8)),
+                                                       C.byref(S.swan_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)),
+                                                       F, F, 1, st), U),
 ]
 bad = [(n, got, want) for n, got, want in cases if got != want]
 for n, got, want in bad: print("MISMATCH", n, got, want)
