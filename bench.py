@@ -40,14 +40,25 @@ def build_state(w, split_tokens: int):
     import torch
     from decode_attention_compressed_02_amd import swan as S
     from decode_attention_compressed_02_amd import workloads as wl
-    from decode_attention_compressed_02_amd.cache import SwanDecoder
+    from decode_attention_compressed_02_amd.cache import PagedSwanDecoder, SwanDecoder, shared_prefix_pool
 
     B, H = w.B, w.H_kv
     T = [w.history_len(b) for b in range(B)]
     Tm = max(T)
-    dims = S.make_dims(w.B, w.N_h, w.H_kv, w.R, w.k, n_cap=w.n_cap() + 64, split_tokens=split_tokens)
     P = torch.from_numpy(wl.projection_qk(w)).cuda()
-    dec = SwanDecoder(dims, P, w.rope_base)
+    if w.block_size > 0:
+        # paged pool: the shared prefix's blocks are mapped by every sequence
+        rows = [max(0, t - w.R) for t in T]
+        pool = shared_prefix_pool(B, rows, w.steps, w.block_size, w.shared_prefix, lambda n: wl.pool_order(w, n),
+                                  w.pool_slack)
+        dims = S.make_dims(w.B, w.N_h, w.H_kv, w.R, w.k, block_size=w.block_size, max_blocks=pool.max_blocks,
+                           num_blocks=pool.num_blocks, split_tokens=split_tokens)
+        dec = PagedSwanDecoder(dims, P, pool, w.rope_base)
+        log(f"paged pool: {pool.num_blocks} blocks of {w.block_size} rows, "
+            f"{int((pool.ref > 1).sum())} shared (reference count {int(pool.ref.max())})")
+    else:
+        dims = S.make_dims(w.B, w.N_h, w.H_kv, w.R, w.k, n_cap=w.n_cap() + 64, split_tokens=split_tokens)
+        dec = SwanDecoder(dims, P, w.rope_base)
     K = torch.empty((B, H, Tm, 128), dtype=torch.float32, device="cuda")
     V = torch.empty_like(K)
     t0 = time.time()
@@ -105,7 +116,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed steps first (replaying the step sequence); the GPU's power "
                          "management needs ~20 ms of sustained load to settle")
-    ap.add_argument("--config", type=int, default=3, help="workload number (1-4); 3 is the headline")
+    ap.add_argument("--config", type=int, default=3, help="workload number (1-5); 3 is the headline")
     ap.add_argument("--split-tokens", type=int, default=0, help="sparse rows per split (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the oracle sample")
@@ -134,10 +145,15 @@ def main():
     log(f"device {torch.cuda.get_device_name(0)}; dims {dec.dims}")
 
     # step inputs for every step, resident in HBM before timing
-    inputs = []
+    inputs, pos_host = [], []
     for s in range(args.steps):
         q, kr, vn, pos = wl.step_inputs(w, s)
         inputs.append(tuple(torch.from_numpy(a).cuda() for a in (q, kr, vn, pos)) + (int(pos.max()),))
+        pos_host.append(pos)
+    paged = w.block_size > 0
+    if paged:
+        import copy
+        pool0 = copy.deepcopy(dec.pool)
     max_pos_all = max(x[4] for x in inputs)
     dec.ensure_workspace(max_pos_all)
     kb0, vb0 = dec.cache.k_buf.clone(), dec.cache.v_buf.clone()
@@ -145,8 +161,10 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def run_step(x, ev=None):
+    def run_step(x, ev=None, ph=None):
         q, kr, vn, pos, mp = x
+        if paged:  # host bookkeeping + copy-on-write copies + table refresh
+            dec.prepare_step(ph)
         dec.project(q, kr, pos)
         dec.append(pos, mp, vn)
         if ev is not None:
@@ -157,15 +175,20 @@ def main():
         S.swan_decode_reduce(dec.dims, pos, mp, dec.workspace, dec.o_hat)
 
     def restore():
-        # back to the initial state: the steps only changed the ring and rows past n
+        # back to the initial state: the steps only changed the ring and rows
+        # past n (and, paged, the pool's tables and counts)
         dec.cache.k_buf.copy_(kb0)
         dec.cache.v_buf.copy_(vb0)
+        if paged:
+            dec.pool = copy.deepcopy(pool0)
+            dec._bt_version = -1
+            dec.sync_table()
 
     # warm-up: replay the step sequence from the initial state, cyclically
     for s in range(args.warmup):
         if s % args.steps == 0:
             restore()
-        run_step(inputs[s % args.steps])
+        run_step(inputs[s % args.steps], ph=pos_host[s % args.steps])
     torch.cuda.synchronize()
     restore()
     torch.cuda.synchronize()
@@ -174,7 +197,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        run_step(inputs[s], evs[s])
+        run_step(inputs[s], evs[s], ph=pos_host[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -241,7 +264,7 @@ def main():
         "data": "synthetic (seeded N(0,1) raw keys/queries, stored-basis values, random orthogonal P_QK)",
         "config": {"workload": f"config {args.config}: {w.name}", "B": w.B, "N_h": w.N_h, "H_kv": w.H_kv,
                    "d_h": w.d_h, "ctx_first_step": int(w.ctx[0]), "R": w.R, "k": w.k,
-                   "storage": "fp16 values, uint8 indices, fp16 dense buffer", "splits": nsplit,
+                   "storage": "fp16 values, uint8 indices, fp16 dense buffer", "split_waves": nsplit,
                    "split_tokens": dec.dims.split_tokens or "auto"},
         "step_hbm_GBps": float(np.mean(dec_bytes)) / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": float(np.mean(dec_bytes)) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,

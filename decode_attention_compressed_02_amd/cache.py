@@ -220,9 +220,19 @@ class PagedSwanDecoder(SwanDecoder):
         super().__init__(dims, P_qk, rope_base, device, block_table=bt)
         self._bt_version = pool.version
 
+    def _to_device(self, arr, out=None):
+        # pinned staging + asynchronous copy: the step does not wait for the
+        # host; the caching host allocator keeps a staging buffer alive until
+        # its copy has run
+        staging = torch.from_numpy(np.ascontiguousarray(arr)).pin_memory()
+        if out is None:
+            out = torch.empty(staging.shape, dtype=staging.dtype, device=self.device)
+        out.copy_(staging, non_blocking=True)
+        return out
+
     def sync_table(self):
         if self._bt_version != self.pool.version:
-            self.cache.block_table.copy_(torch.from_numpy(self.pool.table))
+            self._to_device(self.pool.table, self.cache.block_table)
             self._bt_version = self.pool.version
 
     def prepare_step(self, pos_host, stream=None):
@@ -241,12 +251,35 @@ class PagedSwanDecoder(SwanDecoder):
             if cp is not None:
                 pairs.append(cp)
         if pairs:
-            src = torch.tensor([a for a, _ in pairs], dtype=torch.int32, device=self.device)
-            dst = torch.tensor([c for _, c in pairs], dtype=torch.int32, device=self.device)
-            S.swan_copy_blocks(self.dims, self.cache.struct(), src, dst, stream)
+            ids = self._to_device(np.array(pairs, np.int32).T.copy())
+            S.swan_copy_blocks(self.dims, self.cache.struct(), ids[0], ids[1], stream)
         self.sync_table()
         return len(pairs)
 
     def step_paged(self, q, k, v_hat, pos, pos_host, stream=None):
         self.prepare_step(pos_host, stream)
         return self.step(q, k, v_hat, pos, int(max(pos_host)), stream)
+
+
+def shared_prefix_pool(B: int, rows, steps: int, block_size: int, prefix_rows: int, order_fn, slack: int = 0):
+    """A pool for B sequences holding rows[b] sparse rows each, whose first
+    prefix_rows rows are the same tokens in every sequence: sequence 0 owns
+    the prefix blocks and every other sequence maps them too (reference count
+    B); all other blocks are private.  Blocks come from the permutation
+    order_fn(num_blocks) of the pool.  The pool has room for `steps` more rows
+    per sequence (plus copy-on-write of one prefix block each) and `slack`
+    spare blocks."""
+    bs = block_size
+    prefix_blocks = -(-prefix_rows // bs) if prefix_rows > 0 else 0
+    have = [-(-int(r) // bs) for r in rows]
+    need = [-(-(int(r) + steps) // bs) for r in rows]
+    max_blocks = max(1, max(need))
+    num_blocks = prefix_blocks + sum(max(0, n - prefix_blocks) for n in need) + B + slack
+    pool = PagedPool(num_blocks, B, max_blocks, bs, order=order_fn(num_blocks))
+    for lb in range(max(have[0], min(prefix_blocks, max_blocks))):
+        pool.map_new(0, lb)
+    for b in range(1, B):
+        pool.share(0, b, min(prefix_blocks, have[b], have[0]))
+        for lb in range(min(prefix_blocks, have[b], have[0]), have[b]):
+            pool.map_new(b, lb)
+    return pool

@@ -84,47 +84,43 @@ swan::SparseGeom geom(const swan_dims *d, const swan_cache *c)
 }
 
 struct Plan {
-    int S, TPS, DPS; // splits; sparse rows and buffered tokens per split
+    int W; // waves of the split pass
 };
 
-// Split the sparse rows of the longest sequence into S ranges of TPS rows and
-// spread the buffered tokens over the same S splits (DPS each), so that every
-// wave streams about the same number of bytes.  The automatic TPS sizes the
-// grid to one wave per resident-wave slot of the chip (the split kernel's LDS
-// footprint decides how many fit on a CU).
+// The split pass runs W waves over nearly equal ranges of the batch's work
+// rows (unit_work: sparse rows plus buffered tokens weighted by their bytes);
+// max_pos bounds every unit, and the kernels use active_waves() <= W of them
+// for the batch at hand.  The automatic plan launches one wave per
+// resident-wave slot of the chip (the split kernel's LDS footprint decides
+// how many fit on a CU), fewer when the longest batch max_pos allows has
+// under kMinWaveRows work rows per wave; split_tokens sets the rows per wave
+// instead.
 Plan plan(const swan_dims *d, int32_t max_pos)
 {
-    const int64_t ctx = (int64_t)max_pos + 1;
-    int64_t n_max = ctx > d->R ? ctx - d->R : 0;
-    if (n_max > row_cap(d)) n_max = row_cap(d);
-    const int64_t fill = ctx <= 0 ? 0 : (ctx < d->R ? ctx : d->R);
     const int g = d->N_h / d->H_kv, ks = row_stride(d->k);
-    Plan p;
-    int64_t tps = d->split_tokens;
-    if (tps == 0) {
+    const int64_t total_max = (int64_t)d->B * d->H_kv * swan::unit_work(max_pos, d->R, row_cap(d), ks).len;
+    int slots = INT32_MAX;
+    if (d->split_tokens == 0) {
         int per_cu = swan::kLdsPerCU / swan::split_lds_bytes(g, ks);
         if (per_cu > 8) per_cu = 8;
         if (per_cu < 1) per_cu = 1;
-        const int64_t units = (int64_t)d->B * d->H_kv;
-        tps = (n_max * units + (int64_t)swan::kCUs * per_cu - 1) / ((int64_t)swan::kCUs * per_cu);
-        const int64_t floor_tps = (n_max + swan::kMaxSplits - 1) / swan::kMaxSplits;
-        if (tps < floor_tps) tps = floor_tps;
-        tps = (tps + 63) / 64 * 64;
-        if (tps < 64) tps = 64;
+        slots = swan::kCUs * per_cu;
     }
-    p.TPS = (int)tps;
-    int64_t S = (n_max + tps - 1) / tps;
-    const int64_t s_dense = (fill + swan::kDenseMinSplit - 1) / swan::kDenseMinSplit;
-    if (S < s_dense) S = s_dense;
-    if (S < 1) S = 1; // nothing to attend anywhere: one empty split
-    p.S = (int)(S > INT32_MAX ? INT32_MAX : S);
-    p.DPS = (int)((fill + S - 1) / S);
+    Plan p;
+    p.W = (int)swan::active_waves(total_max, slots, d->split_tokens);
     return p;
+}
+
+// partials: one per (piece, query head of the group); a piece is a wave's
+// share of one unit, and there are at most W + B H_kv of them
+size_t partial_count(const swan_dims *d, const Plan &p)
+{
+    return ((size_t)p.W + (size_t)d->B * d->H_kv) * (size_t)(d->N_h / d->H_kv);
 }
 
 size_t workspace_bytes(const swan_dims *d, const Plan &p)
 {
-    return (size_t)d->B * d->N_h * p.S * (swan::kD + 2) * sizeof(float);
+    return partial_count(d, p) * (swan::kD + 2) * sizeof(float);
 }
 
 swan_status check_decode(const swan_dims *d, const swan_cache *c, const int32_t *pos, int32_t max_pos,
@@ -139,9 +135,9 @@ swan_status check_decode(const swan_dims *d, const swan_cache *c, const int32_t 
         return fail(SWAN_ERR_CAPACITY, "max_pos = %d needs %lld sparse rows, capacity is %lld", max_pos,
                     (long long)n_max, (long long)row_cap(d));
     *out = plan(d, max_pos);
-    if (out->S > swan::kMaxSplits)
-        return fail(SWAN_ERR_INVALID_ARG, "split_tokens = %d gives %d splits, at most %d are supported", d->split_tokens,
-                    out->S, swan::kMaxSplits);
+    if (out->W > swan::kMaxWaves)
+        return fail(SWAN_ERR_INVALID_ARG, "split_tokens = %d gives %d waves, at most %d are supported", d->split_tokens,
+                    out->W, swan::kMaxWaves);
     if (!ws) return fail(SWAN_ERR_INVALID_ARG, "workspace is NULL");
     if (ws_bytes < workspace_bytes(d, *out))
         return fail(SWAN_ERR_INVALID_ARG, "workspace of %zu bytes, need %zu", ws_bytes, workspace_bytes(d, *out));
@@ -231,7 +227,7 @@ size_t swan_decode_workspace_bytes(const swan_dims *d, int32_t max_pos)
 int32_t swan_decode_num_splits(const swan_dims *d, int32_t max_pos)
 {
     if (check_dims(d)) return -1;
-    return plan(d, max_pos).S;
+    return plan(d, max_pos).W;
 }
 
 static swan::SplitArgs split_args(const swan_dims *d, const swan_cache *c, const Plan &p, const int32_t *pos,
@@ -242,9 +238,8 @@ static swan::SplitArgs split_args(const swan_dims *d, const swan_cache *c, const
     a.N_h = d->N_h;
     a.H = d->H_kv;
     a.R = d->R;
-    a.S = p.S;
-    a.TPS = p.TPS;
-    a.DPS = p.DPS;
+    a.W = p.W;
+    a.split_tokens = d->split_tokens;
     a.k = d->k;
     a.row_cap = (int)row_cap(d);
     a.geom = geom(d, c);
@@ -257,7 +252,7 @@ static swan::SplitArgs split_args(const swan_dims *d, const swan_cache *c, const
     a.kbuf = c->k_buf;
     a.vbuf = c->v_buf;
     a.part_o = (float *)ws;
-    a.part_ml = (float *)ws + (size_t)d->B * d->N_h * p.S * swan::kD;
+    a.part_ml = (float *)ws + partial_count(d, p) * swan::kD;
     return a;
 }
 
@@ -283,9 +278,15 @@ swan_status swan_decode_reduce(const swan_dims *d, const int32_t *pos, int32_t m
     swan::ReduceArgs r;
     r.B = d->B;
     r.N_h = d->N_h;
-    r.S = p.S;
+    r.H = d->H_kv;
+    r.R = d->R;
+    r.W = p.W;
+    r.split_tokens = d->split_tokens;
+    r.ks = row_stride(d->k);
+    r.row_cap = (int)row_cap(d);
+    r.pos = pos;
     r.part_o = (const float *)ws;
-    r.part_ml = (const float *)ws + (size_t)d->B * d->N_h * p.S * swan::kD;
+    r.part_ml = (const float *)ws + partial_count(d, p) * swan::kD;
     r.o_hat = o_hat;
     return hip_status(swan::launch_reduce(r, (hipStream_t)stream), "swan_decode_reduce launch");
 }

@@ -178,6 +178,32 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
+// value of lane l (wave-uniform l), in scalar registers
+__device__ __forceinline__ int64_t lane_value(int64_t v, int l)
+{
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l), hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// inclusive prefix sum over the lanes of the wave
+__device__ __forceinline__ int64_t wave_scan(int64_t v)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int64_t t = __shfl_up(v, d);
+        if (lane >= d) v += t;
+    }
+    return v;
+}
+
+// work rows of the units of sequences [0, B) (per kv head), summed over the
+// lanes of a wave or a block's waves alike
+__device__ __forceinline__ int64_t seq_work(const int32_t *pos, int b, int R, int64_t row_cap, int ks)
+{
+    return unit_work(pos[b], R, row_cap, ks).len;
+}
+
 // G consecutive floats of LDS at p (16-byte aligned for G >= 4)
 template <int G>
 __device__ __forceinline__ void lds_get(const float *p, float (&v)[G])
@@ -365,457 +391,580 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
     __shared__ __attribute__((aligned(16))) float qs[kD * G];
     __shared__ __attribute__((aligned(16))) float acc[NACC];
 
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x;
-    const int ctx = a.pos[b] + 1; // tokens attended; <= 0 for an inactive sequence
-    const int n = min(ctx > a.R ? ctx - a.R : 0, a.row_cap);
-    const int fill = max(0, min(ctx, a.R));
+    const int64_t w = blockIdx.x;
 
-    const float *qsrc = a.q_hat + ((int64_t)b * a.N_h + h * G) * kD;
+    // ---- this wave's work rows [x0, x1) of the batch.  Lane l holds
+    // sequence base + l; the first 64 sequences stay in registers for the
+    // search below (one pass when B <= 64).
+    const int32_t pos0 = lane < a.B ? a.pos[lane] : -1;
+    const int64_t len0 = lane < a.B ? unit_work(pos0, a.R, a.row_cap, KS).len * a.H : 0;
+    const int64_t end0 = wave_scan(len0);
+    int64_t total = lane_value(end0, kWave - 1);
+    for (int base = kWave; base < a.B; base += kWave) {
+        const int bb = base + lane;
+        total += lane_value(wave_scan(bb < a.B ? seq_work(a.pos, bb, a.R, a.row_cap, KS) * a.H : 0), kWave - 1);
+    }
+    const int64_t V = active_waves(total, a.W, a.split_tokens);
+    if (w >= V) return;
+    const int64_t x0 = w * total / V, x1 = (w + 1) * total / V;
+    if (x0 >= x1) return;
+    // first sequence whose units reach past x0, and the work row they start at
+    int b = 0;
+    int64_t P = 0;
     {
-        float qv[2 * G]; // all loads first, then the LDS writes
-#pragma unroll
-        for (int j = 0; j < 2 * G; ++j) qv[j] = qsrc[lane + j * kWave];
-#pragma unroll
-        for (int j = 0; j < 2 * G; ++j) {
-            const int i = lane + j * kWave, hh = i / kD, c = i % kD;
-            qs[c * G + hh] = qv[j] * kScoreScaleLog2;
+        const uint64_t hit = __ballot(lane < a.B && end0 > x0);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            b = l;
+            P = lane_value(end0 - len0, l);
+        } else {
+            int64_t run = lane_value(end0, kWave - 1);
+            for (int base = kWave; base < a.B; base += kWave) {
+                const int bb = base + lane;
+                const int64_t len = bb < a.B ? seq_work(a.pos, bb, a.R, a.row_cap, KS) * a.H : 0;
+                const int64_t end = run + wave_scan(len);
+                const uint64_t hit2 = __ballot(bb < a.B && end > x0);
+                if (hit2) {
+                    const int l = __builtin_ctzll(hit2);
+                    b = base + l;
+                    P = lane_value(end - len, l);
+                    break;
+                }
+                run = lane_value(end, kWave - 1);
+            }
         }
     }
-    for (int i = lane * 4; i < NACC; i += kWave * 4) *(f32x4 *)(acc + i) = (f32x4){0.f, 0.f, 0.f, 0.f};
-    __syncthreads();
+    for (; b < a.B && P < x1; ++b) {
+        const int32_t pb = b < kWave ? __builtin_amdgcn_readlane(pos0, b) : __builtin_amdgcn_readfirstlane(a.pos[b]);
+        const UnitWork uw = unit_work(pb, a.R, a.row_cap, KS);
+        for (int h = (uw.len > 0 && x0 > P) ? (int)((x0 - P) / uw.len) : 0;
+             uw.len > 0 && h < a.H && P + h * uw.len < x1; ++h) {
+            // the piece [lo, hi) of unit (b, h): sparse rows [t0, t1) and buffered tokens [d0, d1)
+            const int64_t us = P + h * uw.len, lo = max(x0, us) - us, hi = min(x1, us + uw.len) - us;
+            const int t0 = (int)sparse_split(lo, uw), t1 = (int)sparse_split(hi, uw);
+            const int d0 = (int)dense_split(lo, uw), d1 = (int)dense_split(hi, uw);
+            const int64_t piece = (int64_t)w + (int64_t)b * a.H + h;
 
-    // Running max per head, kept finite (kNoScore) so that exp2(s - m) of a
-    // masked score (-inf) is 0 without a NaN guard; ls counts the sparse
-    // weights once per lane of a row (divided by LPT at the end), ld the
-    // buffered weights once per token.
-    float m[G], ls[G], ld[G];
+            const float *qsrc = a.q_hat + ((int64_t)b * a.N_h + h * G) * kD;
+            {
+                float qv[2 * G]; // all loads first, then the LDS writes
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        m[hh] = kNoScore;
-        ls[hh] = 0.f;
-        ld[hh] = 0.f;
-    }
+                for (int j = 0; j < 2 * G; ++j) qv[j] = qsrc[lane + j * kWave];
+#pragma unroll
+                for (int j = 0; j < 2 * G; ++j) {
+                    const int i = lane + j * kWave, hh = i / kD, c = i % kD;
+                    qs[c * G + hh] = qv[j] * kScoreScaleLog2;
+                }
+            }
+            for (int i = lane * 4; i < NACC; i += kWave * 4) *(f32x4 *)(acc + i) = (f32x4){0.f, 0.f, 0.f, 0.f};
+            __syncthreads();
 
-    // ---- buffered tokens [d0, d1)
-    const int d0 = split * a.DPS, d1 = min(d0 + a.DPS, fill);
-    if (d0 < d1) {
-        constexpr int DD = 4;
-        const int tl = lane >> 4, c0 = (lane & 15) * 8;
-        float qr[8][G], ar[8][G];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
+            // Running max per head, kept finite (kNoScore) so that exp2(s - m) of a
+            // masked score (-inf) is 0 without a NaN guard; ls counts the sparse
+            // weights once per lane of a row (divided by LPT at the end), ld the
+            // buffered weights once per token.
+            float m[G], ls[G], ld[G];
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) {
-                qr[i][hh] = qs[(c0 + i) * G + hh];
-                ar[i][hh] = 0.f;
+                m[hh] = kNoScore;
+                ls[hh] = 0.f;
+                ld[hh] = 0.f;
             }
-        const int64_t ub = ((int64_t)b * a.H + h) * a.R * kD + c0;
-        u32x4 kst[DD], vst[DD];
-        auto dload = [&](int t, u32x4 &kk, u32x4 &vv) {
-            const int tok = min(t + tl, d1 - 1);
-            kk = __builtin_nontemporal_load((const u32x4 *)(a.kbuf + ub + (int64_t)tok * kD));
-            vv = __builtin_nontemporal_load((const u32x4 *)(a.vbuf + ub + (int64_t)tok * kD));
-        };
+
+            // ---- buffered tokens [d0, d1)
+            if (d0 < d1) {
+                constexpr int DD = 4;
+                const int tl = lane >> 4, c0 = (lane & 15) * 8;
+                float qr[8][G], ar[8][G];
 #pragma unroll
-        for (int d = 0; d < DD; ++d) {
-            dload(d0 + 4 * d, kst[d], vst[d]);
-            __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-        }
-        // steps past d1 run fully masked; each ring slot is consumed before
-        // it is reloaded so the loop carries no register copies
-        for (int tb = d0; tb < d1; tb += 4 * DD) {
-#pragma unroll
-            for (int d = 0; d < DD; ++d) {
-                const int t = tb + 4 * d;
-                const half8 kh = __builtin_bit_cast(half8, kst[d]), vh = __builtin_bit_cast(half8, vst[d]);
-                const bool valid = t + tl < d1;
-                float s[G], dm = -INFINITY;
-#pragma unroll
-                for (int hh = 0; hh < G; ++hh) {
-                    s[hh] = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) s[hh] = fmaf(qr[i][hh], (float)kh[i], s[hh]);
-                    const float gs = group_sum<16>(s[hh]); // all lanes take part in the permutes
-                    s[hh] = valid ? gs : -INFINITY;
-                    dm = fmaxf(dm, s[hh] - m[hh]);
-                }
-                if (__any(dm > kRescaleSlack)) { // wave-uniform
+                for (int i = 0; i < 8; ++i)
 #pragma unroll
                     for (int hh = 0; hh < G; ++hh) {
-                        const float mn = fmaxf(m[hh], wave_max(s[hh]));
-                        const float f = fast_exp2(m[hh] - mn);
-                        m[hh] = mn;
-                        ld[hh] *= f;
+                        qr[i][hh] = qs[(c0 + i) * G + hh];
+                        ar[i][hh] = 0.f;
+                    }
+                const int64_t ub = ((int64_t)b * a.H + h) * a.R * kD + c0;
+                u32x4 kst[DD], vst[DD];
+                auto dload = [&](int t, u32x4 &kk, u32x4 &vv) {
+                    const int tok = min(t + tl, d1 - 1);
+                    kk = __builtin_nontemporal_load((const u32x4 *)(a.kbuf + ub + (int64_t)tok * kD));
+                    vv = __builtin_nontemporal_load((const u32x4 *)(a.vbuf + ub + (int64_t)tok * kD));
+                };
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) ar[i][hh] *= f;
+                for (int d = 0; d < DD; ++d) {
+                    dload(d0 + 4 * d, kst[d], vst[d]);
+                    __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+                }
+                // steps past d1 run fully masked; each ring slot is consumed before
+                // it is reloaded so the loop carries no register copies
+                for (int tb = d0; tb < d1; tb += 4 * DD) {
+#pragma unroll
+                    for (int d = 0; d < DD; ++d) {
+                        const int t = tb + 4 * d;
+                        const half8 kh = __builtin_bit_cast(half8, kst[d]), vh = __builtin_bit_cast(half8, vst[d]);
+                        const bool valid = t + tl < d1;
+                        float s[G], dm = -INFINITY;
+#pragma unroll
+                        for (int hh = 0; hh < G; ++hh) {
+                            s[hh] = 0.f;
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) s[hh] = fmaf(qr[i][hh], (float)kh[i], s[hh]);
+                            const float gs = group_sum<16>(s[hh]); // all lanes take part in the permutes
+                            s[hh] = valid ? gs : -INFINITY;
+                            dm = fmaxf(dm, s[hh] - m[hh]);
+                        }
+                        if (__any(dm > kRescaleSlack)) { // wave-uniform
+#pragma unroll
+                            for (int hh = 0; hh < G; ++hh) {
+                                const float mn = fmaxf(m[hh], wave_max(s[hh]));
+                                const float f = fast_exp2(m[hh] - mn);
+                                m[hh] = mn;
+                                ld[hh] *= f;
+#pragma unroll
+                                for (int i = 0; i < 8; ++i) ar[i][hh] *= f;
+                            }
+                        }
+#pragma unroll
+                        for (int hh = 0; hh < G; ++hh) {
+                            const float w = fast_exp2(s[hh] - m[hh]);
+                            if ((lane & 15) == 0) ld[hh] += w;
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) ar[i][hh] = fmaf(w, (float)vh[i], ar[i][hh]);
+                        }
+                        __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+                        dload(t + 4 * DD, kst[d], vst[d]);
+                        __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
                     }
                 }
 #pragma unroll
-                for (int hh = 0; hh < G; ++hh) {
-                    const float w = fast_exp2(s[hh] - m[hh]);
-                    if ((lane & 15) == 0) ld[hh] += w;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) ar[i][hh] = fmaf(w, (float)vh[i], ar[i][hh]);
-                }
-                __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-                dload(t + 4 * DD, kst[d], vst[d]);
-                __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                ar[i][hh] += __shfl_xor(ar[i][hh], 16);
-                ar[i][hh] += __shfl_xor(ar[i][hh], 32);
-            }
-        if (tl == 0) { // lanes 0..15 own coordinates c0..c0+7 of slot 0 (still zero)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) lds_put<G>(acc + (c0 + i) * TPI * G, ar[i]);
-        }
-        __syncthreads();
-    }
-
-    // ---- sparse rows [t0, t1)
-    // Rows go in passes of D ring slots x TPI rows.  Key and value planes
-    // sit in separate ring slots: a pass's scores come from the K slots, one
-    // rescale test covers the whole pass, then its values are scattered from
-    // the V slots.  Slots are reloaded as soon as they are consumed.
-    const int t0 = split * a.TPS, t1 = min(t0 + a.TPS, n);
-    if (t0 < t1) {
-        const int tl = lane % TPI, sub = lane / TPI;
-        float *my_acc = acc + tl * G; // coordinate c of this slot: my_acc[c * TPI * G]
-        const uint8_t *kidx = a.kidx, *vidx = a.vidx;
-        const uint16_t *kval = a.kval, *vval = a.vval;
-        if constexpr (!PAGED) { // per-unit base in scalar registers, 32-bit lane offsets
-            const int64_t ub = ((int64_t)b * a.H + h) * a.geom.n_cap * KS;
-            kidx += ub;
-            vidx += ub;
-            kval += ub;
-            vval += ub;
-        }
-        // entry offset of this lane's slice of row r0 + tl (rows past t1
-        // re-read the last row and are masked); paged rows whose block-table
-        // entry is not a block of the pool read block 0 and are dropped
-        auto slice = [&](int r0, bool &ok) -> uint32_t {
-            const int r = min(r0 + tl, t1 - 1);
-            if constexpr (PAGED) {
-                const int blk = a.geom.bt[(int64_t)b * a.geom.max_blocks + r / a.geom.bs];
-                ok = blk >= 0 && blk < a.geom.num_blocks;
-                const int bb = ok ? blk : 0;
-                return (uint32_t)(((bb * a.H + h) * a.geom.bs + r % a.geom.bs) * KS + sub * E);
-            } else {
-                ok = true;
-                return (uint32_t)(r * KS + sub * E);
-            }
-        };
-        KSlot<E> rk[D];
-        VSlot<E> rv[D];
-        // Contiguous rows: a buffer resource per plane covers rows r0 .. t1-1
-        // (scalar arithmetic); each lane reads its slice at a fixed offset and
-        // rows past t1 read zeros (masked by valid).  Paged rows go through the
-        // block table one row at a time.
-        const uint32_t lane_off = (uint32_t)(tl * KS + sub * E);
-        auto load_k = [&](int r0, KSlot<E> &st) {
-            if constexpr (PAGED) {
-                const uint32_t o = slice(r0, st.ok);
-                load_words<E>(kidx + o, st.ki);
-                load_words<2 * E>(kval + o, st.kv);
-            } else {
-                const uint32_t rows = (uint32_t)max(t1 - r0, 0);
-                st.ok = true;
-                buffer_words<E>(buffer_rsrc(kidx + (int64_t)r0 * KS, rows * KS), lane_off, st.ki);
-                buffer_words<2 * E>(buffer_rsrc(kval + (int64_t)r0 * KS, rows * KS * 2), 2 * lane_off, st.kv);
-            }
-        };
-        auto load_v = [&](int r0, VSlot<E> &st) {
-            if constexpr (PAGED) {
-                bool ok;
-                const uint32_t o = slice(r0, ok);
-                load_words<E>(vidx + o, st.vi);
-                load_words<2 * E>(vval + o, st.vv);
-            } else {
-                const uint32_t rows = (uint32_t)max(t1 - r0, 0);
-                buffer_words<E>(buffer_rsrc(vidx + (int64_t)r0 * KS, rows * KS), lane_off, st.vi);
-                buffer_words<2 * E>(buffer_rsrc(vval + (int64_t)r0 * KS, rows * KS * 2), 2 * lane_off, st.vv);
-            }
-        };
-        // entries at row positions >= k are padding (index 0, value +0): they
-        // add nothing to a score, but their write-back could overwrite the
-        // update of a kept entry at index 0, so they are not written
-        const int kept = a.k - sub * E;
-
-        // Software pipeline over passes of D * TPI rows: while the values of
-        // pass i are scattered, the scores of pass i + 1 are gathered, so the
-        // LDS and memory waits of one overlap the arithmetic of the other.
-        // Ring loads are issued in the order they are consumed (K slot d for
-        // two passes ahead, then V slot d for one pass ahead).
-        constexpr int P = D * TPI;
-        // g = 4 with 16 slots keeps scores transposed (one head per lane):
-        // m_me / ls_me are the running max and weight sum of head hme of
-        // this lane's row slot
-        const int hme = transposed_head(lane);
-        float m_me = kNoScore, ls_me = 0.f;
-        if constexpr (kT) {
-            m_me = m[0];
-#pragma unroll
-            for (int hh = 1; hh < G; ++hh) m_me = hme == hh ? m[hh] : m_me;
-        }
-        auto reduce_scores = [&](float (&sk)[G], bool valid, float (&out)[G]) {
-            if constexpr (kT) {
-                const float t = transposed_sum4(sk[0], sk[1], sk[2], sk[3]);
-                out[0] = valid ? t : -INFINITY;
-            } else {
-#pragma unroll
-                for (int hh = 0; hh < G; ++hh) {
-                    const float gs = slot_sum<TPI>(sk[hh]); // all lanes take part in the permutes
-                    out[hh] = valid ? gs : -INFINITY;
-                }
-            }
-        };
-        // scores of one ring slot (gather q_hat at the stored key indices);
-        // rows past t1 get -inf
-        auto score = [&](int r0, const KSlot<E> &st, float (&sc)[G]) {
-            const bool valid = (r0 + tl < t1) && st.ok;
-            float q[E][G], s[G]; // all gathers in flight before the first product
-#pragma unroll
-            for (int e = 0; e < E; ++e) lds_get<G>(qs + byte_at(st.ki, e) * G, q[e]);
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) s[hh] = 0.f;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const float v = half_at(st.kv, e);
-#pragma unroll
-                for (int hh = 0; hh < G; ++hh) s[hh] = fmaf(q[e][hh], v, s[hh]);
-            }
-            reduce_scores(s, valid, sc);
-        };
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            load_k(t0 + d * TPI, rk[d]);
-            __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-        }
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            load_v(t0 + d * TPI, rv[d]);
-            __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-        }
-        float sc[D][G];
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            score(t0 + d * TPI, rk[d], sc[d]);
-            __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-            load_k(t0 + P + d * TPI, rk[d]);
-            __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-        }
-
-        for (int rb = t0; rb < t1; rb += P) {
-            // rescale test for pass rb (wave-uniform, rare)
-            float dm = -INFINITY;
-#pragma unroll
-            for (int d = 0; d < D; ++d) {
-                if constexpr (kT) {
-                    dm = fmaxf(dm, sc[d][0] - m_me);
-                } else {
-#pragma unroll
-                    for (int hh = 0; hh < G; ++hh) dm = fmaxf(dm, sc[d][hh] - m[hh]);
-                }
-            }
-            if constexpr (kT) {
-                if (__any(dm > kRescaleSlack)) {
-                    float mx = sc[0][0];
-#pragma unroll
-                    for (int d = 1; d < D; ++d) mx = fmaxf(mx, sc[d][0]);
-                    const float mn = fmaxf(m_me, row_max16(mx)); // a row holds one head
-                    const float f_me = fast_exp2(m_me - mn);
-                    m_me = mn;
-                    ls_me *= f_me;
-                    float f[4];
-                    transposed_broadcast4(f_me, f);
-#pragma unroll
-                    for (int hh = 0; hh < G; ++hh) ld[hh] *= f[hh];
-                    const f32x4 fv = {f[0], f[1], f[2], f[3]};
-                    for (int i = lane * 4; i < NACC; i += kWave * 4) *(f32x4 *)(acc + i) *= fv;
-                }
-            } else if (__any(dm > kRescaleSlack)) {
-                float f[G];
-#pragma unroll
-                for (int hh = 0; hh < G; ++hh) {
-                    float mx = sc[0][hh];
-#pragma unroll
-                    for (int d = 1; d < D; ++d) mx = fmaxf(mx, sc[d][hh]);
-                    const float mn = fmaxf(m[hh], wave_max(mx));
-                    f[hh] = fast_exp2(m[hh] - mn);
-                    m[hh] = mn;
-                    ls[hh] *= f[hh];
-                    ld[hh] *= f[hh];
-                }
-                // a 4-float group at index i covers heads (i + j) % G; i % 8 is (lane & 1) * 4
-                f32x4 fv;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float x = f[j % G];
-                    if constexpr (G == 8) x = (lane & 1) ? f[4 + j] : f[j];
-                    fv[j] = x;
-                }
-                for (int i = lane * 4; i < NACC; i += kWave * 4) *(f32x4 *)(acc + i) *= fv;
-            }
-            float sn[D][G];
-#pragma unroll
-            for (int d = 0; d < D; ++d) {
-                // both LDS batches in flight before any arithmetic: the value
-                // reads of pass rb and the key gathers of pass rb + P
-                const KSlot<E> &ks = rk[d];
-                const VSlot<E> &vs = rv[d];
-                float o[E][G], q[E][G];
-                float *vaddr[E];
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    if constexpr (TPI * G * 4 == 256) // 16 slots x 4 heads: one v_perm per address
-                        vaddr[e] = (float *)((char *)acc + acc_offset_256(vs.vi, e, (uint32_t)(tl * G * 4)));
-                    else
-                        vaddr[e] = my_acc + byte_at(vs.vi, e) * (TPI * G);
-                }
-#pragma unroll
-                for (int e = 0; e < E; ++e) lds_get<G>(vaddr[e], o[e]);
-#pragma unroll
-                for (int e = 0; e < E; ++e) lds_get<G>(qs + byte_at(ks.ki, e) * G, q[e]);
-                // values of pass rb
-                float w[G];
-                if constexpr (kT) {
-                    const float w_me = fast_exp2(sc[d][0] - m_me);
-                    ls_me += w_me;
-                    transposed_broadcast4(w_me, w);
-                } else {
+                for (int i = 0; i < 8; ++i)
 #pragma unroll
                     for (int hh = 0; hh < G; ++hh) {
-                        w[hh] = fast_exp2(sc[d][hh] - m[hh]);
-                        ls[hh] += w[hh];
+                        ar[i][hh] += __shfl_xor(ar[i][hh], 16);
+                        ar[i][hh] += __shfl_xor(ar[i][hh], 32);
+                    }
+                if (tl == 0) { // lanes 0..15 own coordinates c0..c0+7 of slot 0 (still zero)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) lds_put<G>(acc + (c0 + i) * TPI * G, ar[i]);
+                }
+                __syncthreads();
+            }
+
+            // ---- sparse rows [t0, t1)
+            // Rows go in passes of D ring slots x TPI rows.  Key and value planes
+            // sit in separate ring slots: a pass's scores come from the K slots, one
+            // rescale test covers the whole pass, then its values are scattered from
+            // the V slots.  Slots are reloaded as soon as they are consumed.
+            if (t0 < t1) {
+                const int tl = lane % TPI, sub = lane / TPI;
+                float *my_acc = acc + tl * G; // coordinate c of this slot: my_acc[c * TPI * G]
+                const uint8_t *kidx = a.kidx, *vidx = a.vidx;
+                const uint16_t *kval = a.kval, *vval = a.vval;
+                if constexpr (!PAGED) { // per-unit base in scalar registers, 32-bit lane offsets
+                    const int64_t ub = ((int64_t)b * a.H + h) * a.geom.n_cap * KS;
+                    kidx += ub;
+                    vidx += ub;
+                    kval += ub;
+                    vval += ub;
+                }
+                // entry offset of this lane's slice of row r0 + tl (rows past t1
+                // re-read the last row and are masked); paged rows whose block-table
+                // entry is not a block of the pool read block 0 and are dropped
+                auto slice = [&](int r0, bool &ok) -> uint32_t {
+                    const int r = min(r0 + tl, t1 - 1);
+                    if constexpr (PAGED) {
+                        const int blk = a.geom.bt[(int64_t)b * a.geom.max_blocks + r / a.geom.bs];
+                        ok = blk >= 0 && blk < a.geom.num_blocks;
+                        const int bb = ok ? blk : 0;
+                        return (uint32_t)(((bb * a.H + h) * a.geom.bs + r % a.geom.bs) * KS + sub * E);
+                    } else {
+                        ok = true;
+                        return (uint32_t)(r * KS + sub * E);
+                    }
+                };
+                KSlot<E> rk[D];
+                VSlot<E> rv[D];
+                // Contiguous rows: a buffer resource per plane covers rows r0 .. t1-1
+                // (scalar arithmetic); each lane reads its slice at a fixed offset and
+                // rows past t1 read zeros (masked by valid).  Paged rows go through the
+                // block table one row at a time.
+                const uint32_t lane_off = (uint32_t)(tl * KS + sub * E);
+                // Paged pools whose blocks hold a multiple of TPI rows: the TPI rows
+                // of a ring slot start at a multiple of TPI (t0 and TPS are multiples
+                // of 64), so they lie in one block, whose id is wave-uniform and
+                // comes through the scalar cache.  The slot then reads through a
+                // buffer resource on that block like the contiguous layout.  Other
+                // block sizes look the block up per row.
+                const bool slot_blocks = PAGED && a.geom.bs % TPI == 0;
+                // first entry of the slot at r0 and the number of its rows to read;
+                // rows past t1 read nothing (zeros) and are masked by row, rows of a
+                // block outside the pool read nothing and clear ok.  The contiguous
+                // layout reads up to t1 from the slot on.
+                auto slot_base = [&](int r0, uint32_t &rows, bool &ok) -> int64_t {
+                    ok = true;
+                    if constexpr (PAGED) {
+                        rows = 0;
+                        if (r0 >= t1) return 0; // past the split: the table may end here
+                        const int blk = a.geom.bt[(int64_t)b * a.geom.max_blocks + r0 / a.geom.bs];
+                        if (blk < 0 || blk >= a.geom.num_blocks) {
+                            ok = false;
+                            return 0;
+                        }
+                        rows = (uint32_t)min(t1 - r0, TPI);
+                        return (((int64_t)blk * a.H + h) * a.geom.bs + r0 % a.geom.bs) * KS;
+                    } else {
+                        rows = (uint32_t)max(t1 - r0, 0);
+                        return (int64_t)r0 * KS;
+                    }
+                };
+                auto load_k = [&](int r0, KSlot<E> &st) {
+                    if (PAGED && !slot_blocks) {
+                        const uint32_t o = slice(r0, st.ok);
+                        load_words<E>(kidx + o, st.ki);
+                        load_words<2 * E>(kval + o, st.kv);
+                    } else {
+                        uint32_t rows;
+                        const int64_t base = slot_base(r0, rows, st.ok);
+                        buffer_words<E>(buffer_rsrc(kidx + base, rows * KS), lane_off, st.ki);
+                        buffer_words<2 * E>(buffer_rsrc(kval + base, rows * KS * 2), 2 * lane_off, st.kv);
+                    }
+                };
+                auto load_v = [&](int r0, VSlot<E> &st) {
+                    if (PAGED && !slot_blocks) {
+                        bool ok;
+                        const uint32_t o = slice(r0, ok);
+                        load_words<E>(vidx + o, st.vi);
+                        load_words<2 * E>(vval + o, st.vv);
+                    } else {
+                        uint32_t rows;
+                        bool ok;
+                        const int64_t base = slot_base(r0, rows, ok);
+                        buffer_words<E>(buffer_rsrc(vidx + base, rows * KS), lane_off, st.vi);
+                        buffer_words<2 * E>(buffer_rsrc(vval + base, rows * KS * 2), 2 * lane_off, st.vv);
+                    }
+                };
+                // entries at row positions >= k are padding (index 0, value +0): they
+                // add nothing to a score, but their write-back could overwrite the
+                // update of a kept entry at index 0, so they are not written
+                const int kept = a.k - sub * E;
+
+                // Software pipeline over passes of D * TPI rows: while the values of
+                // pass i are scattered, the scores of pass i + 1 are gathered, so the
+                // LDS and memory waits of one overlap the arithmetic of the other.
+                // Ring loads are issued in the order they are consumed (K slot d for
+                // two passes ahead, then V slot d for one pass ahead).
+                constexpr int P = D * TPI;
+                // g = 4 with 16 slots keeps scores transposed (one head per lane):
+                // m_me / ls_me are the running max and weight sum of head hme of
+                // this lane's row slot
+                const int hme = transposed_head(lane);
+                float m_me = kNoScore, ls_me = 0.f;
+                if constexpr (kT) {
+                    m_me = m[0];
+#pragma unroll
+                    for (int hh = 1; hh < G; ++hh) m_me = hme == hh ? m[hh] : m_me;
+                }
+                auto reduce_scores = [&](float (&sk)[G], bool valid, float (&out)[G]) {
+                    if constexpr (kT) {
+                        const float t = transposed_sum4(sk[0], sk[1], sk[2], sk[3]);
+                        out[0] = valid ? t : -INFINITY;
+                    } else {
+#pragma unroll
+                        for (int hh = 0; hh < G; ++hh) {
+                            const float gs = slot_sum<TPI>(sk[hh]); // all lanes take part in the permutes
+                            out[hh] = valid ? gs : -INFINITY;
+                        }
+                    }
+                };
+                // scores of one ring slot (gather q_hat at the stored key indices);
+                // rows past t1 get -inf
+                auto score = [&](int r0, const KSlot<E> &st, float (&sc)[G]) {
+                    const bool valid = (r0 + tl < t1) && st.ok;
+                    float q[E][G], s[G]; // all gathers in flight before the first product
+#pragma unroll
+                    for (int e = 0; e < E; ++e) lds_get<G>(qs + byte_at(st.ki, e) * G, q[e]);
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) s[hh] = 0.f;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float v = half_at(st.kv, e);
+#pragma unroll
+                        for (int hh = 0; hh < G; ++hh) s[hh] = fmaf(q[e][hh], v, s[hh]);
+                    }
+                    reduce_scores(s, valid, sc);
+                };
+#pragma unroll
+                for (int d = 0; d < D; ++d) {
+                    load_k(t0 + d * TPI, rk[d]);
+                    __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+                }
+#pragma unroll
+                for (int d = 0; d < D; ++d) {
+                    load_v(t0 + d * TPI, rv[d]);
+                    __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+                }
+                float sc[D][G];
+#pragma unroll
+                for (int d = 0; d < D; ++d) {
+                    score(t0 + d * TPI, rk[d], sc[d]);
+                    __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+                    load_k(t0 + P + d * TPI, rk[d]);
+                    __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+                }
+
+                for (int rb = t0; rb < t1; rb += P) {
+                    // rescale test for pass rb (wave-uniform, rare)
+                    float dm = -INFINITY;
+#pragma unroll
+                    for (int d = 0; d < D; ++d) {
+                        if constexpr (kT) {
+                            dm = fmaxf(dm, sc[d][0] - m_me);
+                        } else {
+#pragma unroll
+                            for (int hh = 0; hh < G; ++hh) dm = fmaxf(dm, sc[d][hh] - m[hh]);
+                        }
+                    }
+                    if constexpr (kT) {
+                        if (__any(dm > kRescaleSlack)) {
+                            float mx = sc[0][0];
+#pragma unroll
+                            for (int d = 1; d < D; ++d) mx = fmaxf(mx, sc[d][0]);
+                            const float mn = fmaxf(m_me, row_max16(mx)); // a row holds one head
+                            const float f_me = fast_exp2(m_me - mn);
+                            m_me = mn;
+                            ls_me *= f_me;
+                            float f[4];
+                            transposed_broadcast4(f_me, f);
+#pragma unroll
+                            for (int hh = 0; hh < G; ++hh) ld[hh] *= f[hh];
+                            const f32x4 fv = {f[0], f[1], f[2], f[3]};
+                            for (int i = lane * 4; i < NACC; i += kWave * 4) *(f32x4 *)(acc + i) *= fv;
+                        }
+                    } else if (__any(dm > kRescaleSlack)) {
+                        float f[G];
+#pragma unroll
+                        for (int hh = 0; hh < G; ++hh) {
+                            float mx = sc[0][hh];
+#pragma unroll
+                            for (int d = 1; d < D; ++d) mx = fmaxf(mx, sc[d][hh]);
+                            const float mn = fmaxf(m[hh], wave_max(mx));
+                            f[hh] = fast_exp2(m[hh] - mn);
+                            m[hh] = mn;
+                            ls[hh] *= f[hh];
+                            ld[hh] *= f[hh];
+                        }
+                        // a 4-float group at index i covers heads (i + j) % G; i % 8 is (lane & 1) * 4
+                        f32x4 fv;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            float x = f[j % G];
+                            if constexpr (G == 8) x = (lane & 1) ? f[4 + j] : f[j];
+                            fv[j] = x;
+                        }
+                        for (int i = lane * 4; i < NACC; i += kWave * 4) *(f32x4 *)(acc + i) *= fv;
+                    }
+                    float sn[D][G];
+#pragma unroll
+                    for (int d = 0; d < D; ++d) {
+                        // both LDS batches in flight before any arithmetic: the value
+                        // reads of pass rb and the key gathers of pass rb + P
+                        const KSlot<E> &ks = rk[d];
+                        const VSlot<E> &vs = rv[d];
+                        float o[E][G], q[E][G];
+                        float *vaddr[E];
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            if constexpr (TPI * G * 4 == 256) // 16 slots x 4 heads: one v_perm per address
+                                vaddr[e] = (float *)((char *)acc + acc_offset_256(vs.vi, e, (uint32_t)(tl * G * 4)));
+                            else
+                                vaddr[e] = my_acc + byte_at(vs.vi, e) * (TPI * G);
+                        }
+#pragma unroll
+                        for (int e = 0; e < E; ++e) lds_get<G>(vaddr[e], o[e]);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) lds_get<G>(qs + byte_at(ks.ki, e) * G, q[e]);
+                        // values of pass rb
+                        float w[G];
+                        if constexpr (kT) {
+                            const float w_me = fast_exp2(sc[d][0] - m_me);
+                            ls_me += w_me;
+                            transposed_broadcast4(w_me, w);
+                        } else {
+#pragma unroll
+                            for (int hh = 0; hh < G; ++hh) {
+                                w[hh] = fast_exp2(sc[d][hh] - m[hh]);
+                                ls[hh] += w[hh];
+                            }
+                        }
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            const float v = half_at(vs.vv, e);
+#pragma unroll
+                            for (int hh = 0; hh < G; ++hh) o[e][hh] = fmaf(w[hh], v, o[e][hh]);
+                        }
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            if (!PAD || e < kept) lds_put<G>(vaddr[e], o[e]);
+                        // scores of pass rb + P
+                        const int r1 = rb + P + d * TPI;
+                        const bool valid = (r1 + tl < t1) && ks.ok;
+                        float sk[G];
+#pragma unroll
+                        for (int hh = 0; hh < G; ++hh) sk[hh] = 0.f;
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            const float v = half_at(ks.kv, e);
+#pragma unroll
+                            for (int hh = 0; hh < G; ++hh) sk[hh] = fmaf(q[e][hh], v, sk[hh]);
+                        }
+                        reduce_scores(sk, valid, sn[d]);
+                        __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+                        load_k(rb + 2 * P + d * TPI, rk[d]);
+                        __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+                        load_v(rb + P + d * TPI, rv[d]);
+                        __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
+                    }
+#pragma unroll
+                    for (int d = 0; d < D; ++d)
+#pragma unroll
+                        for (int hh = 0; hh < G; ++hh) sc[d][hh] = sn[d][hh];
+                }
+                if constexpr (kT) {
+                    // back to per-head registers: a row holds one head; its 16 lanes
+                    // hold the weight sums of the 16 row slots (once each)
+                    float mh[4], lh[4];
+                    transposed_broadcast4(m_me, mh);
+                    transposed_broadcast4(group_sum<16>(ls_me), lh);
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) {
+                        m[hh] = mh[hh];
+                        ls[hh] = lh[hh]; // the head's whole sum, in every lane
                     }
                 }
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float v = half_at(vs.vv, e);
-#pragma unroll
-                    for (int hh = 0; hh < G; ++hh) o[e][hh] = fmaf(w[hh], v, o[e][hh]);
-                }
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    if (!PAD || e < kept) lds_put<G>(vaddr[e], o[e]);
-                // scores of pass rb + P
-                const int r1 = rb + P + d * TPI;
-                const bool valid = (r1 + tl < t1) && ks.ok;
-                float sk[G];
-#pragma unroll
-                for (int hh = 0; hh < G; ++hh) sk[hh] = 0.f;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float v = half_at(ks.kv, e);
-#pragma unroll
-                    for (int hh = 0; hh < G; ++hh) sk[hh] = fmaf(q[e][hh], v, sk[hh]);
-                }
-                reduce_scores(sk, valid, sn[d]);
-                __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-                load_k(rb + 2 * P + d * TPI, rk[d]);
-                __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-                load_v(rb + P + d * TPI, rv[d]);
-                __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
             }
-#pragma unroll
-            for (int d = 0; d < D; ++d)
-#pragma unroll
-                for (int hh = 0; hh < G; ++hh) sc[d][hh] = sn[d][hh];
-        }
-        if constexpr (kT) {
-            // back to per-head registers: a row holds one head; its 16 lanes
-            // hold the weight sums of the 16 row slots (once each)
-            float mh[4], lh[4];
-            transposed_broadcast4(m_me, mh);
-            transposed_broadcast4(group_sum<16>(ls_me), lh);
+            __syncthreads();
+
+            // ---- partials of the piece: (m, l) and the sum of the accumulator copies
+            const int64_t pbase = piece * G; // + hh per head
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) {
-                m[hh] = mh[hh];
-                ls[hh] = lh[hh]; // the head's whole sum, in every lane
+                // generic path: every lane of a row slot added the slot's weights, so
+                // the wave sum counts each LPT times (exactly: LPT is a power of two)
+                const float lsum = kT ? ls[hh] : wave_sum(ls[hh]) * (1.0f / LPT);
+                const float lt = lsum + wave_sum(ld[hh]);
+                if (lane == 0) {
+                    a.part_ml[(pbase + hh) * 2] = m[hh];
+                    a.part_ml[(pbase + hh) * 2 + 1] = lt;
+                }
             }
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                // lane walks the slots of its coordinate starting at slot lane % TPI,
+                // so the 16 lanes of an LDS phase read 16 different bank quads
+                const int c = lane + half * kWave;
+                float o[G], t[G];
+                lds_get<G>(acc + (c * TPI + lane % TPI) * G, o);
+#pragma unroll
+                for (int cp = 1; cp < TPI; ++cp) {
+                    lds_get<G>(acc + (c * TPI + (lane + cp) % TPI) * G, t);
+#pragma unroll
+                    for (int hh = 0; hh < G; ++hh) o[hh] += t[hh];
+                }
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) a.part_o[(pbase + hh) * kD + c] = o[hh];
+            }
+            __syncthreads(); // the next piece rewrites the queries and accumulators
         }
-    }
-    __syncthreads();
-
-    // ---- partials: (m, l) and the sum of the accumulator copies
-    const int64_t pbase = ((int64_t)b * a.N_h + h * G) * a.S + split; // + hh * S per head
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        // generic path: every lane of a row slot added the slot's weights, so
-        // the wave sum counts each LPT times (exactly: LPT is a power of two)
-        const float lsum = kT ? ls[hh] : wave_sum(ls[hh]) * (1.0f / LPT);
-        const float lt = lsum + wave_sum(ld[hh]);
-        if (lane == 0) {
-            a.part_ml[(pbase + hh * a.S) * 2] = m[hh];
-            a.part_ml[(pbase + hh * a.S) * 2 + 1] = lt;
-        }
-    }
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        // lane walks the slots of its coordinate starting at slot lane % TPI,
-        // so the 16 lanes of an LDS phase read 16 different bank quads
-        const int c = lane + half * kWave;
-        float o[G], t[G];
-        lds_get<G>(acc + (c * TPI + lane % TPI) * G, o);
-#pragma unroll
-        for (int cp = 1; cp < TPI; ++cp) {
-            lds_get<G>(acc + (c * TPI + (lane + cp) % TPI) * G, t);
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) o[hh] += t[hh];
-        }
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) a.part_o[(pbase + hh * a.S) * kD + c] = o[hh];
+        P += uw.len * a.H;
     }
 }
 
 // ---------------------------------------------------------------------------
-// pass 2: merge the S partials of one (query head, sequence).  Thread c owns
-// output coordinate c.  An all-empty head (inactive sequence) yields zeros.
+// pass 2: merge the partials of one (query head, sequence): the pieces of its
+// unit, found from the same work plan as the split pass.  Thread c owns
+// output coordinate c.  A unit with no tokens (inactive sequence) yields zeros.
 // ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int64_t block_sum128(int64_t v, int64_t *red)
+{
+    const int t = threadIdx.x;
+    v = lane_value(wave_scan(v), kWave - 1);
+    if ((t & (kWave - 1)) == 0) red[t / kWave] = v;
+    __syncthreads();
+    v = red[0] + red[1];
+    __syncthreads();
+    return v;
+}
 
 __global__ __launch_bounds__(128) void k_reduce(ReduceArgs a)
 {
-    __shared__ float wsh[kMaxSplits];
-    __shared__ float red[4];
+    __shared__ float wsh[128];
+    __shared__ float redf[2];
+    __shared__ int64_t red[2];
     const int hq = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-    const int64_t base = ((int64_t)b * a.N_h + hq) * a.S;
+    const int G = a.N_h / a.H, h = hq / G, hh = hq % G;
+    float *out = a.o_hat + ((int64_t)b * a.N_h + hq) * kD + t;
+
+    int64_t tot = 0, before = 0;
+    for (int bb = t; bb < a.B; bb += 128) {
+        const int64_t len = seq_work(a.pos, bb, a.R, a.row_cap, a.ks);
+        tot += len;
+        if (bb < b) before += len;
+    }
+    tot = block_sum128(tot, red);
+    before = block_sum128(before, red);
+    const int64_t len = unit_work(a.pos[b], a.R, a.row_cap, a.ks).len;
+    if (len == 0) {
+        *out = 0.f;
+        return;
+    }
+    // waves whose ranges [w T / V, (w + 1) T / V) meet [us, us + len)
+    const int64_t T = tot * a.H, V = active_waves(T, a.W, a.split_tokens);
+    const int64_t us = before * a.H + h * len, u = (int64_t)b * a.H + h;
+    const int64_t w0 = max(((us + 1) * V + T - 1) / T - 1, (int64_t)0);
+    const int64_t w1 = min(((us + len) * V + T - 1) / T - 1, V - 1);
+    // partial of wave w: index w + u, head hh
+    const float *ml = a.part_ml + (u * G + hh) * 2;
+    const float *po = a.part_o + (u * G + hh) * kD + t;
+    const int64_t ml_step = (int64_t)G * 2, po_step = (int64_t)G * kD;
 
     float mx = -INFINITY;
-    for (int s = t; s < a.S; s += 128) mx = fmaxf(mx, a.part_ml[(base + s) * 2]);
+    for (int64_t w = w0 + t; w <= w1; w += 128) mx = fmaxf(mx, ml[w * ml_step]);
     mx = wave_max(mx);
-    if ((t & 63) == 0) red[t >> 6] = mx;
+    if ((t & (kWave - 1)) == 0) redf[t / kWave] = mx;
     __syncthreads();
-    mx = fmaxf(red[0], red[1]);
+    mx = fmaxf(redf[0], redf[1]);
+    __syncthreads();
 
-    float L = 0.f;
-    for (int s = t; s < a.S; s += 128) {
-        const float ms = a.part_ml[(base + s) * 2];
-        const float w = exp2f(ms - mx);
-        wsh[s] = w;
-        L = fmaf(w, a.part_ml[(base + s) * 2 + 1], L);
+    float L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    for (int64_t c0 = w0; c0 <= w1; c0 += 128) {
+        const int64_t w = c0 + t;
+        float wt = 0.f;
+        if (w <= w1) {
+            wt = exp2f(ml[w * ml_step] - mx);
+            L = fmaf(wt, ml[w * ml_step + 1], L);
+        }
+        wsh[t] = wt;
+        __syncthreads();
+        const int cnt = (int)min((int64_t)128, w1 - c0 + 1);
+        const float *pc = po + c0 * po_step;
+        int j = 0;
+        for (; j + 4 <= cnt; j += 4) {
+            o0 = fmaf(wsh[j], pc[j * po_step], o0);
+            o1 = fmaf(wsh[j + 1], pc[(j + 1) * po_step], o1);
+            o2 = fmaf(wsh[j + 2], pc[(j + 2) * po_step], o2);
+            o3 = fmaf(wsh[j + 3], pc[(j + 3) * po_step], o3);
+        }
+        for (; j < cnt; ++j) o0 = fmaf(wsh[j], pc[j * po_step], o0);
+        __syncthreads();
     }
     L = wave_sum(L);
-    if ((t & 63) == 0) red[2 + (t >> 6)] = L;
+    if ((t & (kWave - 1)) == 0) redf[t / kWave] = L;
     __syncthreads();
-    L = red[2] + red[3];
-
-    const float *po = a.part_o + base * kD + t;
-    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-    int s = 0;
-    for (; s + 4 <= a.S; s += 4) {
-        o0 = fmaf(wsh[s], po[(int64_t)s * kD], o0);
-        o1 = fmaf(wsh[s + 1], po[(int64_t)(s + 1) * kD], o1);
-        o2 = fmaf(wsh[s + 2], po[(int64_t)(s + 2) * kD], o2);
-        o3 = fmaf(wsh[s + 3], po[(int64_t)(s + 3) * kD], o3);
-    }
-    for (; s < a.S; ++s) o0 = fmaf(wsh[s], po[(int64_t)s * kD], o0);
+    L = redf[0] + redf[1];
     const float o = (o0 + o1) + (o2 + o3);
-    a.o_hat[((int64_t)b * a.N_h + hq) * kD + t] = L > 0.f ? o / L : 0.f;
+    *out = L > 0.f ? o / L : 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -825,7 +974,7 @@ __global__ __launch_bounds__(128) void k_reduce(ReduceArgs a)
 template <int G, int KS, bool PAGED>
 static void launch_split_k(const SplitArgs &a, hipStream_t s)
 {
-    const dim3 grid(a.S, a.H, a.B), block(kWave);
+    const dim3 grid(a.W), block(kWave);
     if (a.k < KS)
         hipLaunchKernelGGL((k_split<G, KS, PAGED, true>), grid, block, 0, s, a);
     else
@@ -860,7 +1009,6 @@ hipError_t launch_split(const SplitArgs &a, int g, hipStream_t s)
 
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s)
 {
-    if (a.S > kMaxSplits) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_reduce, dim3(a.N_h, a.B), dim3(kD), 0, s, a);
     return hipGetLastError();
 }

@@ -13,8 +13,7 @@ constexpr int kD = 128;          // head dimension (indices fit in 8 bits)
 constexpr int kWave = 64;        // CDNA wavefront
 constexpr int kCUs = 256;          // MI355X compute units (launch sizing only)
 constexpr int kLdsPerCU = 160 * 1024;
-constexpr int kMaxSplits = 1024;   // splits per (sequence, kv head) in one decode
-constexpr int kDenseMinSplit = 64; // buffered tokens per split when there are few sparse rows
+constexpr int kMaxWaves = 1 << 20; // waves of one split pass (bounds the workspace)
 
 // log2(e) / sqrt(128): scores are kept in base-2 units so softmax uses exp2
 constexpr float kScoreScaleLog2 = 0.12751743074573063f;
@@ -145,23 +144,80 @@ __host__ __device__ constexpr int split_lds_bytes(int G, int KS)
     return 4 * kD * G * (1 + split_token_slots(G, KS));
 }
 
+// ---- work plan of the decode split pass
+// Each unit (sequence b, kv head h) is a run of work rows in one virtual
+// sequence over all units, b-major then h: one per sparse row plus, per
+// buffered token, its bytes relative to a sparse row (a buffered token
+// streams 2 x 256 bytes, a sparse row 2 x 3 KS).  The T work rows of the
+// batch are cut into V nearly equal ranges, wave w taking [w T / V,
+// (w + 1) T / V) (rounded down), so every wave streams about the same bytes
+// whatever the mix of lengths; when V is a multiple of the unit count and
+// the units are equally long, every range lies inside one unit.  A piece
+// [lo, hi) of a unit's work rows covers the same fraction of its sparse rows
+// (in whole ring slots of kSparseQuantum rows) and of its buffered tokens.
+// A wave may cover the end of one unit and the start of the next, one
+// partial per piece: the piece of unit u in wave w writes partial w + u
+// (pieces in work-row order step w, u or both by one, so the index is unique
+// and below V + B H).
+constexpr int kSparseQuantum = 16; // a multiple of the rows per ring slot
+constexpr int kMinWaveRows = 64;
+
+// work rows of buffered tokens [0, f) for stored rows of ks entries
+__host__ __device__ inline int64_t dense_work(int64_t f, int ks) { return (f * 256 + 3 * ks - 1) / (3 * ks); }
+
+struct UnitWork {
+    int64_t n, f, len; // sparse rows, buffered tokens, work rows
+};
+__host__ __device__ inline UnitWork unit_work(int32_t pos, int R, int64_t row_cap, int ks)
+{
+    const int64_t ctx = (int64_t)pos + 1; // <= 0: inactive sequence
+    UnitWork u;
+    u.n = ctx > R ? ctx - R : 0;
+    if (u.n > row_cap) u.n = row_cap;
+    u.f = ctx <= 0 ? 0 : (ctx < R ? ctx : R);
+    u.len = u.n + dense_work(u.f, ks);
+    return u;
+}
+// first sparse row of the piece starting at work row x of the unit (0 <= x
+// <= len): a multiple of kSparseQuantum, or n at the end
+__host__ __device__ inline int64_t sparse_split(int64_t x, const UnitWork &u)
+{
+    if (x >= u.len) return u.n;
+    const int64_t r = x * ((u.n + kSparseQuantum - 1) / kSparseQuantum) / u.len * kSparseQuantum;
+    return r < u.n ? r : u.n;
+}
+// first buffered token of the piece starting at work row x
+__host__ __device__ inline int64_t dense_split(int64_t x, const UnitWork &u)
+{
+    return x >= u.len ? u.f : (x * u.f + u.len - 1) / u.len;
+}
+// waves V that take part for a batch of T work rows and a grid of W waves
+__host__ __device__ inline int64_t active_waves(int64_t T, int W, int split_tokens)
+{
+    int64_t v = split_tokens > 0 ? (T + split_tokens - 1) / split_tokens : T / kMinWaveRows;
+    if (v > W) v = W;
+    return v < 1 ? 1 : v;
+}
+
 struct SplitArgs {
     int B, N_h, H, R;
-    int S, TPS, DPS; // splits; sparse rows and buffered tokens per split
-    int k;           // kept entries per row; entries k..ks-1 are padding
-    int row_cap;     // sparse rows addressable per unit
+    int W;            // waves of the split pass (the grid)
+    int split_tokens; // about this many work rows per wave; 0: spread the batch over W waves
+    int k;            // kept entries per row; entries k..ks-1 are padding
+    int row_cap;      // sparse rows addressable per unit
     SparseGeom geom;
     const int32_t *pos;
     const float *q_hat;
     const uint8_t *kidx, *vidx;
     const uint16_t *kval, *vval, *kbuf, *vbuf;
-    float *part_o;  // [B][N_h][S][128]
-    float *part_ml; // [B][N_h][S][2]
+    float *part_o;  // [W + B H][g][128]
+    float *part_ml; // [W + B H][g][2]
 };
 hipError_t launch_split(const SplitArgs &a, int g, hipStream_t s);
 
 struct ReduceArgs {
-    int B, N_h, S;
+    int B, N_h, H, R, W, split_tokens, ks, row_cap;
+    const int32_t *pos;
     const float *part_o, *part_ml;
     float *o_hat;
 };

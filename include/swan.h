@@ -93,7 +93,7 @@ typedef struct swan_dims {
     int32_t block_size;   /* 0 = contiguous sparse rows, >0 = rows per paged block */
     int32_t max_blocks;   /* paged: block-table entries per sequence               */
     int32_t num_blocks;   /* paged: blocks in the pool                             */
-    int32_t split_tokens; /* decode: sparse rows per split (multiple of 64), 0=auto*/
+    int32_t split_tokens; /* decode: work rows per wave (multiple of 64), 0 = auto */
 } swan_dims;
 
 /* Caller-owned cache planes (host struct holding device pointers). */
@@ -162,8 +162,15 @@ swan_status swan_append_evict(const swan_dims *dims, const swan_cache *cache, co
  * dims are invalid. */
 size_t swan_decode_workspace_bytes(const swan_dims *dims, int32_t max_pos);
 
-/* Number of splits (workgroups per (sequence, kv head)) swan_decode_attn
- * launches for max_pos (host); -1 if dims are invalid. */
+/* Number of waves of the split pass swan_decode_attn launches for max_pos
+ * (host); -1 if dims are invalid.  The batch's work rows are spread evenly
+ * over them: a unit (sequence, kv head) counts its sparse rows plus its
+ * buffered tokens weighted 256 / (3 swan_row_stride(k)) rows each (their
+ * bytes relative to a sparse row), each part rounded up to 16; a wave takes
+ * split_tokens consecutive work rows, or with split_tokens = 0 an equal share
+ * (a multiple of 16, at least 64) of the batch's total.  A piece of a unit
+ * takes the same fraction of its sparse rows and of its buffered tokens; a
+ * wave that covers pieces of several units writes one partial per piece. */
 int32_t swan_decode_num_splits(const swan_dims *dims, int32_t max_pos);
 
 /*
@@ -176,17 +183,20 @@ int32_t swan_decode_num_splits(const swan_dims *dims, int32_t max_pos);
  *   q_hat  float32 [B][N_h][128]
  *   o_hat  float32 [B][N_h][128]   out, in the rotated value basis
  *   workspace  device scratch of at least swan_decode_workspace_bytes()
- * Two kernels: a split kernel (one wavefront per (sequence, kv head, split)
- * serving the g query heads of the group, online softmax) and a reduce
- * kernel that merges the splits.
+ * Two kernels: a split kernel (wavefronts over equal shares of the batch's
+ * work, each piece of a (sequence, kv head) serving the g query heads of the
+ * group with an online softmax) and a reduce kernel that merges the pieces.
+ * Every pos[b] must be <= max_pos: rows of a longer sequence can fall beyond
+ * the last wave and are then left out (no access outside the buffers).
  */
 swan_status swan_decode_attn(const swan_dims *dims, const swan_cache *cache, const int32_t *pos, int32_t max_pos,
                              const float *q_hat, float *o_hat, void *workspace, size_t workspace_bytes,
                              void *stream);
 
 /* The two halves of swan_decode_attn, for callers that time or schedule them
- * separately: the split pass writes per-split partials to the workspace, the
- * reduce pass merges them into o_hat.  Same arguments and checks. */
+ * separately: the split pass writes per-piece partials to the workspace, the
+ * reduce pass merges them into o_hat.  Same arguments and checks; the two
+ * calls must see the same pos and max_pos. */
 swan_status swan_decode_split(const swan_dims *dims, const swan_cache *cache, const int32_t *pos, int32_t max_pos,
                               const float *q_hat, void *workspace, size_t workspace_bytes, void *stream);
 swan_status swan_decode_reduce(const swan_dims *dims, const int32_t *pos, int32_t max_pos, const void *workspace,

@@ -47,23 +47,109 @@ def test_row_stride_and_sizes():
 
 def test_split_plan():
     d = S.make_dims(16, 32, 8, 256, 32, n_cap=40000)
-    # 32512 sparse rows + 256 buffered at the first step of the batch-16 32K
-    # workload: one wave per resident slot (the split kernel's 34 KB of LDS
-    # fits 4 per CU; 256 CUs) -> 1024 waves over 128 (sequence, kv head)
-    # units -> 8 splits of 4096 rows
-    S_ = S.swan_decode_num_splits(d, 32767)
-    assert S_ == 8
-    assert S.swan_decode_workspace_bytes(d, 32767) == 16 * 32 * S_ * 130 * 4
+    # first step of the batch-16 32K workload: per (sequence, kv head) 32512
+    # sparse rows + 256 buffered tokens of 256 / 96 work rows each (683 in
+    # all) = 33195 work rows; 128 units.  One wave per resident slot (the
+    # split kernel's 34 KB of LDS fits 4 per CU; 256 CUs) -> 1024 waves.
+    W = S.swan_decode_num_splits(d, 32767)
+    assert W == 1024
+    # partials: at most W + B H_kv pieces, g = 4 heads each, 128 + 2 floats
+    assert S.swan_decode_workspace_bytes(d, 32767) == (1024 + 128) * 4 * 130 * 4
     d.split_tokens = 1024
-    assert S.swan_decode_num_splits(d, 32767) == 32  # 32512 / 1024; buffered tokens ride along (8 per split)
+    assert S.swan_decode_num_splits(d, 32767) == _ceil(128 * 33195, 1024)  # 4150
     d.R = 0
-    assert S.swan_decode_num_splits(d, 32767) == 32
+    assert S.swan_decode_num_splits(d, 32767) == 128 * 32768 // 1024
     assert S.swan_decode_num_splits(S.make_dims(1, 1, 1, 128, 32, n_cap=0), -1) == 1
-    # only buffered tokens (context <= R): 64 per split
-    assert S.swan_decode_num_splits(S.make_dims(2, 8, 2, 256, 32, n_cap=10), 199) == 4
-    # a split count above the supported maximum is refused
+    # only buffered tokens (context 200 <= R): ceil(200 * 256 / 96) = 534
+    # work rows per unit, 4 units, at least 64 rows per wave -> 33 waves
+    assert S.swan_decode_num_splits(S.make_dims(2, 8, 2, 256, 32, n_cap=10), 199) == 33
     d2 = S.make_dims(1, 1, 1, 0, 32, n_cap=1 << 20, split_tokens=64)
     assert S.swan_decode_num_splits(d2, (1 << 20) - 1) == (1 << 20) // 64
+
+
+def _ceil(a, b):
+    return -(-a // b)
+
+
+def _unit(p, R, ks, row_cap):
+    ctx = p + 1
+    n = min(max(ctx - R, 0), row_cap)
+    f = 0 if ctx <= 0 else min(ctx, R)
+    return n, f, n + _ceil(f * 256, 3 * ks)
+
+
+def _active_waves(T, W, st):
+    v = _ceil(T, st) if st > 0 else T // 64
+    return max(1, min(v, W))
+
+
+def _plan_pieces(pos, H, W, split_tokens, R, ks, row_cap):
+    """The split pass's work plan written out on the host: for every wave,
+    its pieces (b, h, sparse rows [t0, t1), buffered tokens [d0, d1), partial
+    index).  It follows the kernel's integer arithmetic so that the plan's
+    invariants can be checked here; the GPU parity tests check the kernel."""
+    def sparse_split(x, n, L):
+        return n if x >= L else min(x * _ceil(n, 16) // L * 16, n)
+
+    def dense_split(x, f, L):
+        return f if x >= L else _ceil(x * f, L)
+
+    units = [_unit(p, R, ks, row_cap) for p in pos]
+    T = H * sum(u[2] for u in units)
+    V = _active_waves(T, W, split_tokens)
+    pieces = []
+    for w in range(V):
+        x0, x1 = w * T // V, (w + 1) * T // V
+        P = 0
+        for b, (n, f, L) in enumerate(units):
+            for h in range(H):
+                us = P + h * L
+                lo, hi = max(x0, us) - us, min(x1, us + L) - us
+                if L == 0 or lo >= hi:
+                    continue
+                pieces.append((w, b, h, sparse_split(lo, n, L), sparse_split(hi, n, L),
+                               dense_split(lo, f, L), dense_split(hi, f, L), w + b * H + h))
+            P += H * L
+    return units, pieces, T, V
+
+
+@pytest.mark.parametrize("pos,H,W,st,R,ks", [
+    ([1023, 16383, 5000, 64, -1, 300], 8, 1024, 0, 64, 64),
+    ([32767] * 4, 8, 1024, 0, 256, 32),
+    ([32767] * 16, 8, 1024, 0, 256, 32),
+    ([130, 17, 2000, 99999], 2, 37, 0, 128, 16),
+    ([4000, 1, 0, 70000], 3, 1 << 20, 128, 128, 128),
+])
+def test_work_plan_partitions_every_unit(pos, H, W, st, R, ks):
+    units, pieces, T, V = _plan_pieces(pos, H, W, st, R, ks, 1 << 20)
+    # every sparse row and buffered token of every unit lies in exactly one piece
+    for b, (n, f, L) in enumerate(units):
+        for h in range(H):
+            mine = [p for p in pieces if p[1] == b and p[2] == h]
+            rows = sorted(r for p in mine for r in range(p[3], max(p[3], p[4])))
+            toks = sorted(t for p in mine for t in range(p[5], max(p[5], p[6])))
+            assert rows == list(range(n)) and toks == list(range(f))
+            # a ring slot never straddles a 16-row block
+            assert all(p[3] % 16 == 0 or p[3] == p[4] for p in mine)
+            # equal pieces carry the unit's mix of sparse rows and buffered tokens
+            if len(mine) > 2 and f > 0:
+                inner = mine[1:-1]
+                assert max(p[6] - p[5] for p in inner) - min(p[6] - p[5] for p in inner) <= 1
+    idx = [p[7] for p in pieces]
+    assert len(set(idx)) == len(idx) and max(idx, default=0) < V + len(pos) * H
+    # equal units and a wave count that is a multiple of the unit count: one piece per wave
+    if len(set(pos)) == 1 and V % (len(pos) * H) == 0:
+        assert len(pieces) == V
+    # the reduce finds a unit's pieces as the waves ceil((us + 1) V / T) - 1 ..
+    # ceil((us + L) V / T) - 1
+    P = 0
+    for b, (n, f, L) in enumerate(units):
+        for h in range(H):
+            us = P + h * L
+            waves = sorted(p[0] for p in pieces if p[1] == b and p[2] == h)
+            w0, w1 = max(_ceil((us + 1) * V, T) - 1, 0), min(_ceil((us + L) * V, T) - 1, V - 1)
+            assert waves == (list(range(w0, w1 + 1)) if L else [])
+        P += H * L
 
 
 ERROR_CASES = r'''
@@ -119,7 +205,7 @@ cases = [
     ("decode null workspace", dec(dims(), ws=N), E),
     ("decode null q_hat", dec(dims(), qh=N), E),
     ("decode null pos", dec(dims(), pos=N), E),
-    ("decode too many splits", dec(dims(split_tokens=64, n_cap=1 << 20), max_pos=(1 << 20) - 1), E),
+    ("decode too many waves", dec(dims(split_tokens=64, n_cap=1 << 25), max_pos=(1 << 25) - 1), E),
     ("prefill capacity", pre(dims(), max_len=100 + 17, T=200), CAP),
     ("prefill T_stride < max_len", pre(dims(), max_len=70, T=64), E),
     ("prefill null raw keys", pre(dims(), kr=N), E),

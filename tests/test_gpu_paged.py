@@ -10,7 +10,7 @@ import torch
 import oracle
 from decode_attention_compressed_02_amd import swan as S
 from decode_attention_compressed_02_amd import workloads as wl
-from decode_attention_compressed_02_amd.cache import PagedPool, PagedSwanDecoder
+from decode_attention_compressed_02_amd.cache import PagedSwanDecoder, shared_prefix_pool
 
 from gpu_helpers import download_rows, rel_l2_max, upload
 
@@ -60,23 +60,9 @@ def test_copy_blocks_moves_whole_blocks():
 
 
 def build_pool(w, prefix_blocks, slack=8):
-    """Sequence 0 owns the prefix blocks, every other sequence shares them;
-    all other logical blocks of the prefilled rows come from a permuted pool."""
-    bs = w.block_size
     rows = [max(0, w.history_len(b) - w.R) for b in range(w.B)]
-    need = [-(-(r + w.steps) // bs) for r in rows]
-    max_blocks = max(need)
-    num_blocks = prefix_blocks + sum(max(0, n - prefix_blocks) for n in need) + w.B + slack
-    pool = PagedPool(num_blocks, w.B, max_blocks, bs, order=wl.pool_order(w, num_blocks))
-    have = [-(-r // bs) for r in rows]
-    for lb in range(max(have[0], prefix_blocks)):
-        pool.map_new(0, lb)
-    for b in range(1, w.B):
-        pool.share(0, b, min(prefix_blocks, have[b]))
-        for lb in range(prefix_blocks, have[b]):
-            pool.map_new(b, lb)
-    return pool
-
+    return shared_prefix_pool(w.B, rows, w.steps, w.block_size, prefix_blocks * w.block_size,
+                              lambda n: wl.pool_order(w, n), slack)
 
 
 @pytest.mark.parametrize("k", [64, 40])
