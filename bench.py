@@ -15,7 +15,6 @@ Prints one JSON line (rank 0).
 from __future__ import annotations
 
 import argparse
-import concurrent.futures as cf
 import json
 import os
 import sys
@@ -32,47 +31,6 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_traffic.json")
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
-
-
-def build_state(w, split_tokens: int):
-    """Generate the seeded history on the host (threads over sequences), move
-    it to the GPU and convert it to the hybrid cache there."""
-    import torch
-    from decode_attention_compressed_02_amd import swan as S
-    from decode_attention_compressed_02_amd import workloads as wl
-    from decode_attention_compressed_02_amd.cache import PagedSwanDecoder, SwanDecoder, shared_prefix_pool
-
-    B, H = w.B, w.H_kv
-    T = [w.history_len(b) for b in range(B)]
-    Tm = max(T)
-    P = torch.from_numpy(wl.projection_qk(w)).cuda()
-    if w.block_size > 0:
-        # paged pool: the shared prefix's blocks are mapped by every sequence
-        rows = [max(0, t - w.R) for t in T]
-        pool = shared_prefix_pool(B, rows, w.steps, w.block_size, w.shared_prefix, lambda n: wl.pool_order(w, n),
-                                  w.pool_slack)
-        dims = S.make_dims(w.B, w.N_h, w.H_kv, w.R, w.k, block_size=w.block_size, max_blocks=pool.max_blocks,
-                           num_blocks=pool.num_blocks, split_tokens=split_tokens)
-        dec = PagedSwanDecoder(dims, P, pool, w.rope_base)
-        log(f"paged pool: {pool.num_blocks} blocks of {w.block_size} rows, "
-            f"{int((pool.ref > 1).sum())} shared (reference count {int(pool.ref.max())})")
-    else:
-        dims = S.make_dims(w.B, w.N_h, w.H_kv, w.R, w.k, n_cap=w.n_cap() + 64, split_tokens=split_tokens)
-        dec = SwanDecoder(dims, P, w.rope_base)
-    K = torch.empty((B, H, Tm, 128), dtype=torch.float32, device="cuda")
-    V = torch.empty_like(K)
-    t0 = time.time()
-    with cf.ThreadPoolExecutor(max_workers=min(16, B)) as ex:
-        for b, (kb, vb) in enumerate(ex.map(lambda b: wl.history(w, b), range(B))):
-            K[b, :, :T[b]].copy_(torch.from_numpy(kb))
-            V[b, :, :T[b]].copy_(torch.from_numpy(vb))
-    log(f"generated + uploaded history {B}x{H}x{Tm} in {time.time() - t0:.1f}s")
-    lens = torch.tensor(T, dtype=torch.int32, device="cuda")
-    dec.prefill(lens, Tm, K, V)
-    torch.cuda.synchronize()
-    del K, V
-    torch.cuda.empty_cache()
-    return dec
 
 
 def cpu_baseline(w, steps: int, seqs: list[int]):
@@ -133,6 +91,7 @@ def main():
     from decode_attention_compressed_02_amd import accounting as acc
     from decode_attention_compressed_02_amd import swan as S
     from decode_attention_compressed_02_amd import workloads as wl
+    from decode_attention_compressed_02_amd.state import build_decoder
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -141,7 +100,7 @@ def main():
     w = wl.config(args.config)
     if args.steps > w.steps:
         w = w.scaled(steps=args.steps)
-    dec = build_state(w, args.split_tokens)
+    dec = build_decoder(w, args.split_tokens)
     log(f"device {torch.cuda.get_device_name(0)}; dims {dec.dims}")
 
     # step inputs for every step, resident in HBM before timing

@@ -3,14 +3,17 @@
 // and every older one as its pruned sparse row).
 //
 // One workgroup of 256 threads per (32-token tile, kv head, sequence):
-//   1. RoPE of the tile's raw keys at their own positions (angles in double)
-//      into LDS, transposed as xs[c][token];
+//   1. RoPE of the tile's raw keys at their own positions into LDS,
+//      transposed as xs[c][token];
 //   2. the tile times P_QK (thread = output column j and a 16-token half),
-//      rounded to fp16; values rounded to fp16;
+//      rounded once to fp16; values rounded to fp16;
 //   3. each wave places 8 tokens: tokens older than len - R are pruned into
 //      their sparse rows (the same wave-level top-k as the append kernel),
 //      the newest R go to buffer slots t mod R.
-// The result is identical to appending the tokens one at a time.
+// The result is identical to appending the tokens one at a time.  Keys are
+// rotated and projected in double, as in the decode-step projection, so that
+// their fp16 rounding (and with it the pruning) does not depend on float
+// rounding of intermediate products.
 #include "swan_internal.h"
 
 namespace swan {
@@ -25,7 +28,7 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a)
     const int t0 = tile * kTile;
     if (t0 >= T) return;
 
-    __shared__ __attribute__((aligned(16))) float xs[kD][kTile + 4];
+    __shared__ __attribute__((aligned(16))) double xs[kD][kTile + 2];
     __shared__ uint16_t kh[kTile][kD], vh[kTile][kD];
 
     const int64_t u = (int64_t)b * a.H + h;
@@ -33,14 +36,14 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a)
     const float *vr = a.v_hat + u * a.T_stride * kD;
     for (int e = tid; e < kTile * (kD / 2); e += 256) {
         const int tt = e / (kD / 2), i = e % (kD / 2), t = t0 + tt;
-        float y0 = 0.f, y1 = 0.f;
+        double y0 = 0.0, y1 = 0.0;
         if (t < T) {
             const double theta = pow((double)a.base, -(double)i / (double)(kD / 2));
             double sn, cs;
             sincos((double)t * theta, &sn, &cs);
             const double x0 = kr[(int64_t)t * kD + i], x1 = kr[(int64_t)t * kD + i + kD / 2];
-            y0 = (float)(x0 * cs - x1 * sn);
-            y1 = (float)(x1 * cs + x0 * sn);
+            y0 = x0 * cs - x1 * sn;
+            y1 = x1 * cs + x0 * sn;
         }
         xs[i][tt] = y0;
         xs[i + kD / 2][tt] = y1;
@@ -53,18 +56,18 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a)
 
     {
         const int j = tid % kD, half = tid / kD; // tokens half*16 .. half*16+15
-        float acc[16];
+        double acc[16];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+        for (int q = 0; q < 16; ++q) acc[q] = 0.0;
         const float *P = a.P + (int64_t)h * kD * kD + j;
         for (int c = 0; c < kD; ++c) {
-            const float pc = P[c * kD];
-            const float *xr = &xs[c][half * 16];
+            const double pc = P[c * kD];
+            const double *xr = &xs[c][half * 16];
 #pragma unroll
-            for (int q = 0; q < 16; ++q) acc[q] = fmaf(xr[q], pc, acc[q]);
+            for (int q = 0; q < 16; ++q) acc[q] = fma(xr[q], pc, acc[q]);
         }
 #pragma unroll
-        for (int q = 0; q < 16; ++q) kh[half * 16 + q][j] = f2h(acc[q]);
+        for (int q = 0; q < 16; ++q) kh[half * 16 + q][j] = d2h(acc[q]);
     }
     __syncthreads();
 

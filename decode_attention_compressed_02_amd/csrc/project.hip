@@ -11,6 +11,12 @@
 // FLOPs per head of SWAN appendix A.2 are tiny next to the decode stream: the
 // kernel is latency-bound, so the row walk is cut four ways and its loads are
 // issued eight at a time.
+//
+// The arithmetic is in double: the new key is rounded once to fp16 and its
+// top-k coordinates are chosen on those fp16 magnitudes, so a key computed
+// in float could round one ulp away from the exact product and change which
+// coordinates survive pruning.  In double the result is the correctly
+// rounded fp16 of the exact value except within ~1e-16 of a midpoint.
 #include "swan_internal.h"
 
 namespace swan {
@@ -23,9 +29,9 @@ __global__ __launch_bounds__(kProjThreads) void k_project(ProjectArgs a)
 {
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int j = tid % kD, quarter = tid / kD;
-    __shared__ float xs[G + 1][kD];
-    __shared__ float part[kProjThreads / kD - 1][G + 1][kD];
-    __shared__ float cs[kD / 2], sn[kD / 2];
+    __shared__ double xs[G + 1][kD];
+    __shared__ double part[kProjThreads / kD - 1][G + 1][kD];
+    __shared__ double cs[kD / 2], sn[kD / 2];
 
     const int p = max(a.pos[b], 0);
     if (tid < kD / 2) {
@@ -33,23 +39,23 @@ __global__ __launch_bounds__(kProjThreads) void k_project(ProjectArgs a)
         const double theta = pow((double)a.base, -(double)tid / (double)(kD / 2));
         double s, c;
         sincos((double)p * theta, &s, &c);
-        cs[tid] = (float)c;
-        sn[tid] = (float)s;
+        cs[tid] = c;
+        sn[tid] = s;
     }
     __syncthreads();
     // RoPE: pair (i, i + 64) rotated by angle_i; 512 threads cover 8 vectors per pass
     for (int v = tid / (kD / 2); v < G + 1; v += kProjThreads / (kD / 2)) {
         const int i = tid % (kD / 2);
         const float *x = (v < G) ? a.q + ((int64_t)b * a.N_h + h * G + v) * kD : a.k + ((int64_t)b * a.H + h) * kD;
-        const float x0 = x[i], x1 = x[i + kD / 2];
+        const double x0 = x[i], x1 = x[i + kD / 2];
         xs[v][i] = x0 * cs[i] - x1 * sn[i];
         xs[v][i + kD / 2] = x1 * cs[i] + x0 * sn[i];
     }
     __syncthreads();
 
-    float acc[G + 1];
+    double acc[G + 1];
 #pragma unroll
-    for (int v = 0; v < G + 1; ++v) acc[v] = 0.f;
+    for (int v = 0; v < G + 1; ++v) acc[v] = 0.0;
     const int c0 = quarter * kProjRows;
     const float *P = a.P + (int64_t)h * kD * kD + (int64_t)c0 * kD + j;
 #pragma unroll
@@ -60,7 +66,7 @@ __global__ __launch_bounds__(kProjThreads) void k_project(ProjectArgs a)
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
-            for (int v = 0; v < G + 1; ++v) acc[v] = fmaf(xs[v][c0 + cb + u], pr[u], acc[v]);
+            for (int v = 0; v < G + 1; ++v) acc[v] = fma(xs[v][c0 + cb + u], (double)pr[u], acc[v]);
     }
     if (quarter > 0) {
 #pragma unroll
@@ -73,8 +79,8 @@ __global__ __launch_bounds__(kProjThreads) void k_project(ProjectArgs a)
 #pragma unroll
             for (int r = 0; r < kProjThreads / kD - 1; ++r) acc[v] += part[r][v][j];
 #pragma unroll
-        for (int v = 0; v < G; ++v) a.q_hat[((int64_t)b * a.N_h + h * G + v) * kD + j] = acc[v];
-        a.k_hat[((int64_t)b * a.H + h) * kD + j] = f2h(acc[G]);
+        for (int v = 0; v < G; ++v) a.q_hat[((int64_t)b * a.N_h + h * G + v) * kD + j] = (float)acc[v];
+        a.k_hat[((int64_t)b * a.H + h) * kD + j] = d2h(acc[G]);
     }
 }
 

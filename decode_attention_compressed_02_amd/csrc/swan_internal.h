@@ -24,6 +24,38 @@ __device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_c
 // round to nearest even (the default mode of v_cvt_f16_f32)
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
+// fp16 bits of a double, rounded once to nearest even (IEEE 754 binary16:
+// 10 stored significand bits, exponent bias 15, subnormal spacing 2^-24).
+// Going through float first would round twice and can land one ulp off
+// when the float lies on an fp16 midpoint.
+__host__ __device__ inline uint16_t d2h(double x)
+{
+    const uint64_t bits = __builtin_bit_cast(uint64_t, x);
+    const uint16_t sign = (uint16_t)((bits >> 48) & 0x8000u);
+    const int ex = (int)((bits >> 52) & 0x7FF);
+    const uint64_t man = bits & ((1ull << 52) - 1);
+    if (ex == 0x7FF) return sign | (man ? 0x7E00u : 0x7C00u); // NaN, infinity
+    const int e = ex - 1023;                                   // x = 1.man * 2^e (normal doubles)
+    if (e > 15) return sign | 0x7C00u;                         // >= 65536: overflow
+    int shift;          // significand bits below the kept ones
+    uint64_t sig;       // significand with its leading one
+    uint32_t base;      // exponent field of the result before rounding
+    if (e >= -14) {     // normal fp16
+        sig = man;
+        shift = 42;
+        base = (uint32_t)(e + 15) << 10;
+    } else {            // subnormal fp16 (or zero): units of 2^-24
+        if (ex == 0 || e < -25) return sign; // below half the smallest subnormal
+        sig = man | (1ull << 52);
+        shift = 28 - e; // 43 .. 53
+        base = 0;
+    }
+    const uint64_t kept = sig >> shift, rest = sig & ((1ull << shift) - 1), half = 1ull << (shift - 1);
+    const uint32_t up = (rest > half || (rest == half && (kept & 1))) ? 1u : 0u;
+    // a carry out of the significand steps the exponent (up to infinity)
+    return sign | (uint16_t)(base + (uint32_t)kept + up);
+}
+
 // Where the sparse rows of one (sequence, kv head) live.
 struct SparseGeom {
     int H;          // kv heads
