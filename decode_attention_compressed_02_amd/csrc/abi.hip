@@ -91,20 +91,17 @@ struct Plan {
 // rows (unit_work: sparse rows plus buffered tokens weighted by their bytes);
 // max_pos bounds every unit, and the kernels use active_waves() <= W of them
 // for the batch at hand.  The automatic plan launches one wave per
-// resident-wave slot of the chip (the split kernel's LDS footprint decides
-// how many fit on a CU), fewer when the longest batch max_pos allows has
-// under kMinWaveRows work rows per wave; split_tokens sets the rows per wave
-// instead.
+// resident-wave slot of the chip (the split kernel's LDS footprint and
+// register budget decide how many fit on a CU), fewer when the longest batch
+// max_pos allows has under kMinWaveRows work rows per wave; split_tokens sets
+// the rows per wave instead.
 Plan plan(const swan_dims *d, int32_t max_pos)
 {
     const int g = d->N_h / d->H_kv, ks = row_stride(d->k);
     const int64_t total_max = (int64_t)d->B * d->H_kv * swan::unit_work(max_pos, d->R, row_cap(d), ks).len;
     int slots = INT32_MAX;
     if (d->split_tokens == 0) {
-        int per_cu = swan::kLdsPerCU / swan::split_lds_bytes(g, ks);
-        if (per_cu > 8) per_cu = 8;
-        if (per_cu < 1) per_cu = 1;
-        slots = swan::kCUs * per_cu;
+        slots = swan::kCUs * swan::split_waves_per_cu(g, ks);
     }
     Plan p;
     p.W = (int)swan::active_waves(total_max, slots, d->split_tokens);

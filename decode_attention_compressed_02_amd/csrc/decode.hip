@@ -375,7 +375,7 @@ __host__ __device__ constexpr int split_depth(int E)
 }
 
 template <int G, int KS, bool PAGED, bool PAD>
-__global__ __launch_bounds__(64) void k_split(SplitArgs a)
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS)))) void k_split(SplitArgs a)
 {
     constexpr int E = split_entries(G, KS);
     constexpr int LPT = KS / E;     // lanes per row
@@ -597,51 +597,60 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
                 // buffer resource on that block like the contiguous layout.  Other
                 // block sizes look the block up per row.
                 const bool slot_blocks = PAGED && a.geom.bs % TPI == 0;
-                // first entry of the slot at r0 and the number of its rows to read;
-                // rows past t1 read nothing (zeros) and are masked by row, rows of a
-                // block outside the pool read nothing and clear ok.  The contiguous
-                // layout reads up to t1 from the slot on.
+                // Paged: first entry of the slot at r0 and the number of its rows to
+                // read; rows past t1 read nothing (zeros) and are masked by row, rows
+                // of a block outside the pool read nothing and clear ok.
                 auto slot_base = [&](int r0, uint32_t &rows, bool &ok) -> int64_t {
                     ok = true;
-                    if constexpr (PAGED) {
-                        rows = 0;
-                        if (r0 >= t1) return 0; // past the split: the table may end here
-                        const int blk = a.geom.bt[(int64_t)b * a.geom.max_blocks + r0 / a.geom.bs];
-                        if (blk < 0 || blk >= a.geom.num_blocks) {
-                            ok = false;
-                            return 0;
-                        }
-                        rows = (uint32_t)min(t1 - r0, TPI);
-                        return (((int64_t)blk * a.H + h) * a.geom.bs + r0 % a.geom.bs) * KS;
-                    } else {
-                        rows = (uint32_t)max(t1 - r0, 0);
-                        return (int64_t)r0 * KS;
+                    rows = 0;
+                    if (r0 >= t1) return 0; // past the piece: the table may end here
+                    const int blk = a.geom.bt[(int64_t)b * a.geom.max_blocks + r0 / a.geom.bs];
+                    if (blk < 0 || blk >= a.geom.num_blocks) {
+                        ok = false;
+                        return 0;
                     }
+                    rows = (uint32_t)min(t1 - r0, TPI);
+                    return (((int64_t)blk * a.H + h) * a.geom.bs + r0 % a.geom.bs) * KS;
                 };
-                auto load_k = [&](int r0, KSlot<E> &st) {
+                // Ring slot d of the pass starting at row rp.  Contiguous rows: one
+                // buffer resource per plane and pass, covering rows rp .. t1-1 (the
+                // rest read as zeros), and slot d at a constant offset from it, so
+                // the per-slot address work is an immediate offset.
+                auto load_k = [&](int rp, int d, KSlot<E> &st) {
+                    const int r0 = rp + d * TPI;
                     if (PAGED && !slot_blocks) {
                         const uint32_t o = slice(r0, st.ok);
                         load_words<E>(kidx + o, st.ki);
                         load_words<2 * E>(kval + o, st.kv);
-                    } else {
+                    } else if constexpr (PAGED) {
                         uint32_t rows;
                         const int64_t base = slot_base(r0, rows, st.ok);
                         buffer_words<E>(buffer_rsrc(kidx + base, rows * KS), lane_off, st.ki);
                         buffer_words<2 * E>(buffer_rsrc(kval + base, rows * KS * 2), 2 * lane_off, st.kv);
+                    } else {
+                        const uint32_t rows = (uint32_t)max(t1 - rp, 0), off = lane_off + d * TPI * KS;
+                        st.ok = true;
+                        buffer_words<E>(buffer_rsrc(kidx + (int64_t)rp * KS, rows * KS), off, st.ki);
+                        buffer_words<2 * E>(buffer_rsrc(kval + (int64_t)rp * KS, rows * KS * 2), 2 * off, st.kv);
                     }
                 };
-                auto load_v = [&](int r0, VSlot<E> &st) {
+                auto load_v = [&](int rp, int d, VSlot<E> &st) {
+                    const int r0 = rp + d * TPI;
                     if (PAGED && !slot_blocks) {
                         bool ok;
                         const uint32_t o = slice(r0, ok);
                         load_words<E>(vidx + o, st.vi);
                         load_words<2 * E>(vval + o, st.vv);
-                    } else {
+                    } else if constexpr (PAGED) {
                         uint32_t rows;
                         bool ok;
                         const int64_t base = slot_base(r0, rows, ok);
                         buffer_words<E>(buffer_rsrc(vidx + base, rows * KS), lane_off, st.vi);
                         buffer_words<2 * E>(buffer_rsrc(vval + base, rows * KS * 2), 2 * lane_off, st.vv);
+                    } else {
+                        const uint32_t rows = (uint32_t)max(t1 - rp, 0), off = lane_off + d * TPI * KS;
+                        buffer_words<E>(buffer_rsrc(vidx + (int64_t)rp * KS, rows * KS), off, st.vi);
+                        buffer_words<2 * E>(buffer_rsrc(vval + (int64_t)rp * KS, rows * KS * 2), 2 * off, st.vv);
                     }
                 };
                 // entries at row positions >= k are padding (index 0, value +0): they
@@ -696,12 +705,12 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
                 };
 #pragma unroll
                 for (int d = 0; d < D; ++d) {
-                    load_k(t0 + d * TPI, rk[d]);
+                    load_k(t0, d, rk[d]);
                     __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
                 }
 #pragma unroll
                 for (int d = 0; d < D; ++d) {
-                    load_v(t0 + d * TPI, rv[d]);
+                    load_v(t0, d, rv[d]);
                     __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
                 }
                 float sc[D][G];
@@ -709,7 +718,7 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
                 for (int d = 0; d < D; ++d) {
                     score(t0 + d * TPI, rk[d], sc[d]);
                     __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-                    load_k(t0 + P + d * TPI, rk[d]);
+                    load_k(t0 + P, d, rk[d]);
                     __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
                 }
 
@@ -820,9 +829,9 @@ __global__ __launch_bounds__(64) void k_split(SplitArgs a)
                         }
                         reduce_scores(sk, valid, sn[d]);
                         __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-                        load_k(rb + 2 * P + d * TPI, rk[d]);
+                        load_k(rb + 2 * P, d, rk[d]);
                         __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-                        load_v(rb + P + d * TPI, rv[d]);
+                        load_v(rb + P, d, rv[d]);
                         __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
                     }
 #pragma unroll

@@ -163,9 +163,16 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 // acc[c][slot][g], so with 16 slots the 16 lanes of a phase always hit 16
 // different quads: the value scatter runs without bank conflicts whatever
 // the indices are.  G = 8 keeps 8 slots (LDS size), and very wide rows cap E.
+// Rows of 64 or more entries also use 8 slots: half the accumulator LDS lets
+// two waves share a SIMD, and with 8 or more entries per lane the row sums
+// stay cheap; measured faster than 16 slots at one wave per SIMD.
+__host__ __device__ constexpr int split_slots(int G, int KS) { return (G <= 4 && KS <= 32) ? 16 : 8; }
+// resident waves per SIMD the split kernel is compiled for (register budget:
+// 256 registers a lane at two waves; wider rows and g = 8 need more)
+__host__ __device__ constexpr int split_waves_per_simd(int G, int KS) { return (G <= 4 && KS == 64) ? 2 : 1; }
 __host__ __device__ constexpr int split_entries(int G, int KS)
 {
-    const int slots = G <= 4 ? 16 : 8;
+    const int slots = split_slots(G, KS);
     const int e = KS * slots / 64;
     return e < 1 ? 1 : (e > 16 ? 16 : e);
 }
@@ -174,6 +181,14 @@ __host__ __device__ constexpr int split_token_slots(int G, int KS) { return 64 *
 __host__ __device__ constexpr int split_lds_bytes(int G, int KS)
 {
     return 4 * kD * G * (1 + split_token_slots(G, KS));
+}
+// split waves resident on one CU: the LDS footprint and, for g >= 4, the
+// register budget above (g <= 2 fits at least two waves per SIMD)
+__host__ __device__ constexpr int split_waves_per_cu(int G, int KS)
+{
+    const int by_lds = kLdsPerCU / split_lds_bytes(G, KS), by_regs = G >= 4 ? 4 * split_waves_per_simd(G, KS) : 8;
+    const int w = by_lds < by_regs ? by_lds : by_regs;
+    return w < 1 ? 1 : w;
 }
 
 // ---- work plan of the decode split pass
