@@ -33,34 +33,37 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, steps: int, seqs: list[int]):
+def cpu_baseline(w, seqs: list[int], seconds: float, max_steps: int = 4096):
     """The float64 oracle on a sample of the workload: the chosen sequences,
-    all kv heads, the first `steps` decode steps.  Returns (KV tokens/s,
-    threads, seconds, sample description)."""
+    all kv heads, consecutive decode steps from the workload's first step
+    until about `seconds` of stepping (prefill excluded).  Returns (KV
+    tokens/s, threads, seconds, sample description)."""
     import oracle
     from decode_attention_compressed_02_amd import workloads as wl
 
     sub = w.scaled(B=len(seqs), ctx=tuple(w.ctx[b] for b in seqs))
-    oc = oracle.OracleCache.for_workload(sub, sub.n_cap() + steps)
+    oc = oracle.OracleCache.for_workload(sub, sub.n_cap() + max_steps)
     Tm = max(sub.history_len(b) for b in range(sub.B))
     K = np.zeros((sub.B, sub.H_kv, Tm, 128), np.float32)
     V = np.zeros_like(K)
     for i, b in enumerate(seqs):
-        K[i], V[i] = wl.history(w, b)
+        kb, vb = wl.history(w, b)
+        K[i, :, :kb.shape[1]], V[i, :, :vb.shape[1]] = kb, vb
     P = wl.projection_qk(w).astype(np.float64)
     threads = oracle.default_threads()
     t0 = time.time()
     oc.prefill(K, V, np.array([sub.history_len(b) for b in range(sub.B)], np.int64), P, w.rope_base, threads)
     log(f"oracle prefill of the sample in {time.time() - t0:.1f}s")
     del K, V
-    tokens, secs = 0, 0.0
-    for s in range(steps):
-        q, kr, vn, pos = wl.step_inputs(w, s)
+    tokens, secs, steps = 0, 0.0, 0
+    while secs < seconds and steps < max_steps:
+        q, kr, vn, pos = wl.step_inputs(w, steps)
         q, kr, vn, pos = q[seqs], kr[seqs], vn[seqs], pos[seqs].astype(np.int64)
         t = time.perf_counter()
         oc.step(q, kr, vn, pos, P, w.rope_base, threads)
         secs += time.perf_counter() - t
         tokens += int(np.sum(pos + 1))
+        steps += 1
     used = min(threads, sub.B * sub.H_kv)
     desc = (f"sequences {seqs} of {w.B} (all {w.H_kv} kv heads), steps 0..{steps - 1}: "
             f"project + append/evict + decode in float64")
@@ -78,6 +81,7 @@ def main():
     ap.add_argument("--split-tokens", type=int, default=0, help="sparse rows per split (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle stepping time of the sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run plain device copies of this size (for calibrating HBM byte counters)")
     args = ap.parse_args()
@@ -244,7 +248,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         seqs = list(range(min(args.cpu_seqs, w.B)))
-        v, cores, secs, desc = cpu_baseline(w, min(args.steps, 16), seqs)
+        v, cores, secs, desc = cpu_baseline(w, seqs, args.cpu_seconds)
         result["cpu_baseline"] = {"value": v, "unit": "KV tokens/s", "cores": cores, "kind": "oracle",
                                   "sample": desc, "seconds": secs}
     print(json.dumps(result), flush=True)
