@@ -227,6 +227,7 @@ static void so_append_unit(int d, int R, int k, long ncap, long pos,
                            uint8_t *kidx, double *kval, uint8_t *vidx, double *vval,
                            double *ringk, double *ringv, int *err)
 {
+    if (pos < 0) return; /* inactive sequence (a library convention, not the pages'): nothing appended */
     if (R == 0) {
         if (pos >= ncap) { *err = 1; return; }
         so_prune(d, k, khat, kidx + (size_t)pos * k, kval + (size_t)pos * k);
@@ -327,9 +328,9 @@ void so_decode_batch(int B, int N, int H, int d, int R, int k, long ncap, const 
 #pragma omp parallel for collapse(2) schedule(dynamic) num_threads(nthreads)
     for (int b = 0; b < B; ++b)
         for (int h = 0; h < H; ++h) {
-            long ctx = pos[b] + 1;
+            long ctx = pos[b] + 1; /* <= 0: inactive sequence, nothing attended, output zero */
             long n = ctx > R ? ctx - R : 0;
-            long nd = ctx < R ? ctx : R;
+            long nd = ctx <= 0 ? 0 : (ctx < R ? ctx : R);
             if (n > ncap) n = ncap;
             double *scratch = (double *)malloc(sizeof(double) * (size_t)(n + nd + 1));
             so_attend(d, g, qhat + ((size_t)b * N + (size_t)h * g) * d,

@@ -25,7 +25,7 @@ MUTANTS = {
     "ring_slot": ("long slot = pos % R;", "long slot = (pos + 1) % R;"),
     "round_ties_away": ("double r = nearbyint(ax / ulp) * ulp;", "double r = round(ax / ulp) * ulp;"),
     "subnormal_spacing": ("ex = -14;", "ex = -15;"),
-    "drop_newest": ("long nd = ctx < R ? ctx : R;", "long nd = ctx < R ? ctx : R - 1;"),
+    "drop_newest": ("long nd = ctx <= 0 ? 0 : (ctx < R ? ctx : R);", "long nd = ctx <= 0 ? 0 : (ctx < R ? ctx : R - 1);"),
     "softmax_bias": ("scratch[t] = exp(scratch[t] - m);",
                      "scratch[t] = exp(scratch[t] - m) * (t == 0 ? 1.0000001 : 1.0);"),
 }

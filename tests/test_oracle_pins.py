@@ -327,3 +327,23 @@ def test_zero_buffer_prunes_new_token_first():
                    for t in range(T + 1)])
     Vs = np.stack([densify(*[a[None] for a in brute_topk(oracle.round_f16(Vall[t]), k)])[0] for t in range(T + 1)])
     np.testing.assert_allclose(out[0], textbook_attention(qhat[0], Ks, Vs), atol=1e-13)
+
+
+def test_inactive_sequence_appends_nothing_and_attends_nothing():
+    """Reading R14 (a library convention): pos < 0 marks an inactive sequence;
+    its state is left as it is and its outputs are zero, whatever the others do."""
+    r = np.random.default_rng(77)
+    B, N, H, R, k, ncap = 3, 4, 2, 4, 8, 16
+    oc = oracle.OracleCache(B, N, H, D, R, k, ncap)
+    K = r.standard_normal((B, H, 9, D))
+    V = r.standard_normal((B, H, 9, D))
+    oc.prefill(K, V, np.array([9, 9, 9], np.int64), np.stack([np.eye(D)] * H))
+    before = [x.copy() for x in (oc.kidx, oc.kval, oc.vidx, oc.vval, oc.ringk, oc.ringv)]
+    pos = np.array([9, -1, -7], np.int64)
+    oc.append(r.standard_normal((B, H, D)), r.standard_normal((B, H, D)), pos)
+    after = (oc.kidx, oc.kval, oc.vidx, oc.vval, oc.ringk, oc.ringv)
+    for x0, x1 in zip(before, after):
+        np.testing.assert_array_equal(x0[1:], x1[1:])
+    assert any(not np.array_equal(x0[0], x1[0]) for x0, x1 in zip(before, after))
+    out = oc.decode(r.standard_normal((B, N, D)), pos)
+    assert not out[1:].any() and np.abs(out[0]).sum() > 0
