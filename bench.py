@@ -8,8 +8,9 @@ tensors of that shape (raw keys and queries N(0,1), values N(0,1) in the
 stored basis, random orthogonal P_QK); the initial hybrid cache is built on
 the GPU from a 32767-token history with swan_prefill_convert.
 
-A timed step is the whole hot path: swan_project_qk -> swan_append_evict ->
-swan_decode_split -> swan_decode_reduce, all inputs already resident in HBM.
+A timed step is the whole hot path: swan_project_append (projection and
+append/evict in one launch) -> swan_decode_split -> swan_decode_reduce, all
+inputs already resident in HBM.
 Prints one JSON line (rank 0).
 """
 from __future__ import annotations
@@ -128,8 +129,7 @@ def main():
         q, kr, vn, pos, mp = x
         if paged:  # host bookkeeping + copy-on-write copies + table refresh
             dec.prepare_step(ph)
-        dec.project(q, kr, pos)
-        dec.append(pos, mp, vn)
+        dec.project_append(q, kr, vn, pos, mp)
         if ev is not None:
             ev[0].record(stream)
         S.swan_decode_split(dec.dims, dec.cache.struct(), pos, mp, dec.q_hat, dec.workspace)

@@ -95,6 +95,10 @@ class SwanDecoder:
     def append(self, pos, max_pos, v_hat, stream=None):
         S.swan_append_evict(self.dims, self.cache.struct(), pos, max_pos, self.k_hat, v_hat, stream)
 
+    def project_append(self, q, k, v_hat, pos, max_pos, stream=None):
+        S.swan_project_append(self.dims, self.cache.struct(), q, k, v_hat, pos, max_pos, self.P_qk, self.rope_base,
+                              self.q_hat, self.k_hat, stream)
+
     def decode(self, pos, max_pos, stream=None):
         self.ensure_workspace(max_pos)
         S.swan_decode_attn(self.dims, self.cache.struct(), pos, max_pos, self.q_hat, self.o_hat, self.workspace,
@@ -102,8 +106,7 @@ class SwanDecoder:
         return self.o_hat
 
     def step(self, q, k, v_hat, pos, max_pos, stream=None):
-        self.project(q, k, pos, stream)
-        self.append(pos, max_pos, v_hat, stream)
+        self.project_append(q, k, v_hat, pos, max_pos, stream)
         return self.decode(pos, max_pos, stream)
 
 

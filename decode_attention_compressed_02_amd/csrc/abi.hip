@@ -215,6 +215,38 @@ swan_status swan_append_evict(const swan_dims *d, const swan_cache *c, const int
     return hip_status(swan::launch_append(a, (hipStream_t)stream), "swan_append_evict launch");
 }
 
+swan_status swan_project_append(const swan_dims *d, const swan_cache *c, const float *q, const float *k,
+                                const float *v_hat, const int32_t *pos, int32_t max_pos, const float *P_qk,
+                                float rope_base, float *q_hat, uint16_t *k_hat, void *stream)
+{
+    swan_status st = check_dims(d);
+    if (st) return st;
+    if ((st = check_cache(d, c, true))) return st;
+    if (!q || !k || !v_hat || !pos || !P_qk || !q_hat || !k_hat) return fail(SWAN_ERR_INVALID_ARG, "NULL array argument");
+    if (!(rope_base > 1.0f)) return fail(SWAN_ERR_INVALID_ARG, "rope_base must be > 1");
+    const int64_t row = d->R > 0 ? (int64_t)max_pos - d->R : (int64_t)max_pos;
+    if (row >= row_cap(d))
+        return fail(SWAN_ERR_CAPACITY, "max_pos = %d writes sparse row %lld, capacity is %lld", max_pos,
+                    (long long)row, (long long)row_cap(d));
+    swan::ProjectArgs p{d->B, d->N_h, d->H_kv, q, k, pos, P_qk, rope_base, q_hat, k_hat};
+    swan::AppendArgs a;
+    a.B = d->B;
+    a.H = d->H_kv;
+    a.R = d->R;
+    a.k = d->k;
+    a.geom = geom(d, c);
+    a.kidx = c->k_idx;
+    a.vidx = c->v_idx;
+    a.kval = c->k_val;
+    a.vval = c->v_val;
+    a.kbuf = c->k_buf;
+    a.vbuf = c->v_buf;
+    a.pos = pos;
+    a.k_hat = k_hat;
+    a.v_hat = v_hat;
+    return hip_status(swan::launch_project_append(p, a, (hipStream_t)stream), "swan_project_append launch");
+}
+
 size_t swan_decode_workspace_bytes(const swan_dims *d, int32_t max_pos)
 {
     if (check_dims(d)) return 0;

@@ -24,14 +24,17 @@ namespace swan {
 constexpr int kProjThreads = 512;
 constexpr int kProjRows = kD / (kProjThreads / kD); // rows of P per thread group
 
-template <int G>
-__global__ __launch_bounds__(kProjThreads) void k_project(ProjectArgs a)
+// With APPEND the first two waves then append the unit's new key (from LDS)
+// and value to the cache, as k_append does.
+template <int G, bool APPEND>
+__global__ __launch_bounds__(kProjThreads) void k_project(ProjectArgs a, AppendArgs ap)
 {
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int j = tid % kD, quarter = tid / kD;
     __shared__ double xs[G + 1][kD];
     __shared__ double part[kProjThreads / kD - 1][G + 1][kD];
     __shared__ double cs[kD / 2], sn[kD / 2];
+    __shared__ uint16_t khs[APPEND ? kD : 1];
 
     const int p = max(a.pos[b], 0);
     if (tid < kD / 2) {
@@ -80,21 +83,41 @@ __global__ __launch_bounds__(kProjThreads) void k_project(ProjectArgs a)
             for (int r = 0; r < kProjThreads / kD - 1; ++r) acc[v] += part[r][v][j];
 #pragma unroll
         for (int v = 0; v < G; ++v) a.q_hat[((int64_t)b * a.N_h + h * G + v) * kD + j] = (float)acc[v];
-        a.k_hat[((int64_t)b * a.H + h) * kD + j] = d2h(acc[G]);
+        const uint16_t kh = d2h(acc[G]);
+        a.k_hat[((int64_t)b * a.H + h) * kD + j] = kh;
+        if constexpr (APPEND) khs[j] = kh;
+    }
+    if constexpr (APPEND) {
+        __syncthreads();
+        const int wave = tid / kWave, lane = tid % kWave;
+        if (wave < 2) {
+            const int64_t u = (int64_t)b * a.H + h;
+            const uint16_t lo = wave == 0 ? khs[lane] : f2h(ap.v_hat[u * kD + lane]);
+            const uint16_t hi = wave == 0 ? khs[lane + 64] : f2h(ap.v_hat[u * kD + lane + 64]);
+            append_token(ap, b, h, wave, lane, lo, hi);
+        }
     }
 }
 
-hipError_t launch_project(const ProjectArgs &a, hipStream_t s)
+template <bool APPEND>
+static hipError_t launch_g(const ProjectArgs &a, const AppendArgs &ap, hipStream_t s)
 {
     const dim3 grid(a.H, a.B), block(kProjThreads);
     switch (a.N_h / a.H) {
-    case 1: hipLaunchKernelGGL(k_project<1>, grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL(k_project<2>, grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL(k_project<4>, grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL(k_project<8>, grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_project<1, APPEND>), grid, block, 0, s, a, ap); break;
+    case 2: hipLaunchKernelGGL((k_project<2, APPEND>), grid, block, 0, s, a, ap); break;
+    case 4: hipLaunchKernelGGL((k_project<4, APPEND>), grid, block, 0, s, a, ap); break;
+    case 8: hipLaunchKernelGGL((k_project<8, APPEND>), grid, block, 0, s, a, ap); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_project(const ProjectArgs &a, hipStream_t s) { return launch_g<false>(a, AppendArgs{}, s); }
+
+hipError_t launch_project_append(const ProjectArgs &p, const AppendArgs &a, hipStream_t s)
+{
+    return launch_g<true>(p, a, s);
 }
 
 } // namespace swan

@@ -155,6 +155,39 @@ struct AppendArgs {
 };
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 
+// Append of one token to unit (b, h) by one wave: `wave` 0 handles the key,
+// 1 the value; (lo, hi) are the token's fp16 coordinates lane and lane + 64.
+// The token leaving the circular buffer (slot = position mod R) is pruned into
+// its sparse row first; with R = 0 the new token is pruned straight into row
+// pos.  Inactive sequences (pos < 0) append nothing.
+__device__ inline void append_token(const AppendArgs &a, int b, int h, int wave, int lane, uint16_t lo, uint16_t hi)
+{
+    const int p = a.pos[b];
+    if (p < 0) return;
+    const int64_t u = (int64_t)b * a.H + h;
+    uint8_t *idx = wave == 0 ? a.kidx : a.vidx;
+    uint16_t *val = wave == 0 ? a.kval : a.vval;
+    const int row_cap = a.geom.bs > 0 ? a.geom.max_blocks * a.geom.bs : a.geom.n_cap;
+    if (a.R == 0) {
+        const int64_t off = p < row_cap ? row_offset_rt(a.geom, b, h, p) : -1;
+        if (off >= 0) wave_prune_row(lane, lo, hi, a.k, a.geom.ks, idx + off, val + off);
+        return;
+    }
+    uint16_t *buf = (wave == 0 ? a.kbuf : a.vbuf) + (u * a.R + p % a.R) * kD;
+    if (p >= a.R) { // the slot holds token p - R, the oldest one
+        const uint16_t olo = buf[lane], ohi = buf[lane + 64];
+        const int r = p - a.R;
+        const int64_t off = r < row_cap ? row_offset_rt(a.geom, b, h, r) : -1;
+        if (off >= 0) wave_prune_row(lane, olo, ohi, a.k, a.geom.ks, idx + off, val + off);
+    }
+    buf[lane] = lo;
+    buf[lane + 64] = hi;
+}
+
+// projection and append of a step in one launch (the append waits for the
+// unit's new key inside the workgroup, not for the whole grid)
+hipError_t launch_project_append(const ProjectArgs &p, const AppendArgs &a, hipStream_t s);
+
 // Shape of the sparse stream in the split kernel for GQA group G and stored
 // row width KS.  TPI rows (tokens) are in flight per wave iteration, one per
 // accumulator slot, and lane l works on row slot l % TPI; KS / E lanes share

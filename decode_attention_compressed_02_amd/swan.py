@@ -18,7 +18,8 @@ SWAN_OK, SWAN_ERR_INVALID_ARG, SWAN_ERR_UNSUPPORTED, SWAN_ERR_CAPACITY, SWAN_ERR
 
 EXPORTS = ("swan_status_str", "swan_last_error", "swan_row_stride", "swan_cache_bytes", "swan_project_qk",
            "swan_append_evict", "swan_decode_workspace_bytes", "swan_decode_num_splits", "swan_decode_attn",
-           "swan_decode_split", "swan_decode_reduce", "swan_prefill_convert", "swan_copy_blocks")
+           "swan_decode_split", "swan_decode_reduce", "swan_prefill_convert", "swan_copy_blocks",
+           "swan_project_append")
 
 
 class SwanError(RuntimeError):
@@ -59,6 +60,7 @@ def lib():
             "swan_cache_bytes": ([D, P(SZ)], C.c_int),
             "swan_project_qk": ([D, V, V, V, V, F, V, V, V], C.c_int),
             "swan_append_evict": ([D, Cc, V, I32, V, V, V], C.c_int),
+            "swan_project_append": ([D, Cc, V, V, V, V, I32, V, F, V, V, V], C.c_int),
             "swan_decode_workspace_bytes": ([D, I32], SZ),
             "swan_decode_num_splits": ([D, I32], I32),
             "swan_decode_attn": ([D, Cc, V, I32, V, V, V, SZ, V], C.c_int),
@@ -126,6 +128,16 @@ def swan_project_qk(dims, q, k, pos, P_qk, rope_base, q_hat, k_hat, stream=None)
                                  _ptr(pos, torch.int32, "pos"), _ptr(P_qk, torch.float32, "P_qk"), float(rope_base),
                                  _ptr(q_hat, torch.float32, "q_hat"), _ptr(k_hat, torch.float16, "k_hat"),
                                  _stream(stream)))
+
+
+def swan_project_append(dims, cache: "swan_cache", q, k, v_hat, pos, max_pos, P_qk, rope_base, q_hat, k_hat,
+                        stream=None):
+    import torch
+    _check(lib().swan_project_append(C.byref(dims), C.byref(cache), _ptr(q, torch.float32, "q"),
+                                     _ptr(k, torch.float32, "k"), _ptr(v_hat, torch.float32, "v_hat"),
+                                     _ptr(pos, torch.int32, "pos"), int(max_pos), _ptr(P_qk, torch.float32, "P_qk"),
+                                     float(rope_base), _ptr(q_hat, torch.float32, "q_hat"),
+                                     _ptr(k_hat, torch.float16, "k_hat"), _stream(stream)))
 
 
 def swan_append_evict(dims, cache: "swan_cache", pos, max_pos, k_hat, v_hat, stream=None):

@@ -158,6 +158,17 @@ swan_status swan_project_qk(const swan_dims *dims, const float *q, const float *
 swan_status swan_append_evict(const swan_dims *dims, const swan_cache *cache, const int32_t *pos, int32_t max_pos,
                               const uint16_t *k_hat, const float *v_hat, void *stream);
 
+/*
+ * Steps 1 and 2 in one launch: swan_project_qk followed by
+ * swan_append_evict, with the same arguments, layouts, results and checks
+ * as the two calls (q_hat and k_hat are written as well).  Within the launch
+ * each (sequence, kv head) appends as soon as its own new key is projected,
+ * so the step needs one launch and no grid-wide wait between the two.
+ */
+swan_status swan_project_append(const swan_dims *dims, const swan_cache *cache, const float *q, const float *k,
+                                const float *v_hat, const int32_t *pos, int32_t max_pos, const float *P_qk,
+                                float rope_base, float *q_hat, uint16_t *k_hat, void *stream);
+
 /* Bytes of scratch memory swan_decode_attn needs for max_pos (host); 0 if
  * dims are invalid. */
 size_t swan_decode_workspace_bytes(const swan_dims *dims, int32_t max_pos);

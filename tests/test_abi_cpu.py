@@ -175,6 +175,10 @@ def app(d, c=cache, max_pos=50, **kw):
 def dec(d, c=cache, max_pos=50, ws_bytes=1 << 30, **kw):
     a = dict(pos=F, qh=F, oh=F, ws=F); a.update(kw)
     return L.swan_decode_attn(C.byref(d), C.byref(c), a['pos'], max_pos, a['qh'], a['oh'], a['ws'], ws_bytes, st)
+def pa(d, c=cache, max_pos=50, **kw):
+    a = dict(q=F, k=F, vh=F, pos=F, P=F, base=10000.0, qh=F, kh=F); a.update(kw)
+    return L.swan_project_append(C.byref(d), C.byref(c), a['q'], a['k'], a['vh'], a['pos'], max_pos, a['P'],
+                                 a['base'], a['qh'], a['kh'], st)
 def pre(d, c=cache, max_len=40, T=64, **kw):
     a = dict(len=F, kr=F, vh=F, P=F); a.update(kw)
     return L.swan_prefill_convert(C.byref(d), C.byref(c), a['len'], max_len, T, a['kr'], a['vh'], a['P'], 10000.0, st)
@@ -206,6 +210,11 @@ cases = [
     ("decode null q_hat", dec(dims(), qh=N), E),
     ("decode null pos", dec(dims(), pos=N), E),
     ("decode too many waves", dec(dims(split_tokens=64, n_cap=1 << 25), max_pos=(1 << 25) - 1), E),
+    ("project+append null v_hat", pa(dims(), vh=N), E),
+    ("project+append null plane", pa(dims(), c=nocache), E),
+    ("project+append capacity", pa(dims(), max_pos=100 + 16), CAP),
+    ("project+append rope base", pa(dims(), base=0.5), E),
+    ("project+append g = 3", pa(dims(N_h=6, H_kv=2)), U),
     ("prefill capacity", pre(dims(), max_len=100 + 17, T=200), CAP),
     ("prefill T_stride < max_len", pre(dims(), max_len=70, T=64), E),
     ("prefill null raw keys", pre(dims(), kr=N), E),

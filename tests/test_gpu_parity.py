@@ -171,6 +171,54 @@ def test_append_evict_bit_exact(k, R, paged):
         np.testing.assert_array_equal(vb.view(np.uint16), rv.view(np.uint16))
 
 
+@pytest.mark.parametrize("k,R", [(32, 16), (64, 0), (5, 1)])
+@pytest.mark.parametrize("paged", [False, True])
+def test_project_append_one_launch(k, R, paged):
+    """swan_project_append (projection and append in one launch) against the
+    oracle's projection followed by its append: q_hat to the float bar,
+    k_hat, sparse rows and ring bit-exact; an inactive sequence appends
+    nothing."""
+    r = rng(2000 + k + R * 5 + paged)
+    B, N, H = 4, 8, 2
+    T = [40, 9, 0, 25]
+    ncap = 48
+    w = wl.Workload("pa", B, N, H, R, k, tuple(t + 1 for t in T), seed=31 + k + R)
+    oc = oracle.OracleCache(B, N, H, D, R, k, ncap)
+    K = r.standard_normal((B, H, max(T), D)).astype(np.float32)
+    V = r.standard_normal((B, H, max(T), D)).astype(np.float32)
+    P = wl.projection_qk(w)
+    oc.prefill(K, V, np.array(T, np.int64), P.astype(np.float64))
+    bt, kw = None, {}
+    if paged:
+        bs, mb = 16, 3
+        nb = B * mb + 2
+        bt = (rng(6).permutation(nb)[:B * mb]).reshape(B, mb).astype(np.int32)
+        kw = dict(block_size=bs, max_blocks=mb, num_blocks=nb, block_table=bt)
+    dec = make_decoder(oc, P, **kw)
+    upload(dec.cache, oc, bt)
+    q = r.standard_normal((B, N, D)).astype(np.float32)
+    kr = r.standard_normal((B, H, D)).astype(np.float32)
+    vhat = tie_values(r, (B, H, D)).astype(np.float32)
+    pos = np.array(T, np.int64)
+    pos[3] = -1  # inactive: projected at position 0, nothing appended
+    dec.project_append(cuda(q), cuda(kr), cuda(vhat), cuda(pos.astype(np.int32)), int(pos.max()))
+    torch.cuda.synchronize()
+    qh, kh = oc.project(q, kr, np.maximum(pos, 0), P.astype(np.float64))
+    oc.append(kh, vhat.astype(np.float64), pos)
+    assert rel_l2_max(dec.q_hat.cpu().numpy(), qh) < 1e-6
+    np.testing.assert_array_equal(dec.k_hat.cpu().numpy().astype(np.float64), oracle.round_f16(kh))
+    rows = download_rows(dec.cache, B, H, ncap, bt)
+    for b in range(B):
+        n = max(0, int(pos[b]) + 1 - R) if pos[b] >= 0 else max(0, T[b] - R)
+        for got, want in zip(rows, (oc.kidx, oc.kval, oc.vidx, oc.vval)):
+            np.testing.assert_array_equal(got[b, :, :n, :k].astype(want.dtype), want[b, :, :n])
+    if R > 0:
+        kb, vb = (x.cpu().numpy() for x in dec.cache.buffer_views())
+        rk, rv = oc.ring_f16()
+        np.testing.assert_array_equal(kb.view(np.uint16), rk.view(np.uint16))
+        np.testing.assert_array_equal(vb.view(np.uint16), rv.view(np.uint16))
+
+
 # ---------------------------------------------------------------------------
 # a3-a5: decode attention on identical cache states
 # ---------------------------------------------------------------------------
