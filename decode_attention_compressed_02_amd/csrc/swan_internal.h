@@ -294,6 +294,10 @@ struct SplitArgs {
     float *part_ml; // [W + B H][g][2]
 };
 hipError_t launch_split(const SplitArgs &a, int g, hipStream_t s);
+hipError_t launch_split_g1(const SplitArgs &a, hipStream_t s);
+hipError_t launch_split_g2(const SplitArgs &a, hipStream_t s);
+hipError_t launch_split_g4(const SplitArgs &a, hipStream_t s);
+hipError_t launch_split_g8(const SplitArgs &a, hipStream_t s);
 
 struct ReduceArgs {
     int B, N_h, H, R, W, split_tokens, ks, row_cap;

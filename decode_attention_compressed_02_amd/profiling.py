@@ -26,7 +26,8 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # sources that define the split kernel; a traffic figure is valid only for them
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_compressed_02_amd", "csrc", f)
-                  for f in ("decode.hip", "swan_internal.h")]
+                  for f in ("split_kernel.h", "split_g1.hip", "split_g2.hip", "split_g4.hip", "split_g8.hip",
+                            "decode.hip", "swan_internal.h")]
 COPY_KERNEL_HINT = "copy"  # torch's device-to-device copy kernel names contain this
 
 

@@ -52,19 +52,22 @@ def _declare(L):
     L.so_round_f16.argtypes = [_d]
     L.so_round_f16.restype = _d
     L.so_round_f16_array.argtypes = [_l, _pd, _pd]
+    L.so_round_e4m3.argtypes = [_d]
+    L.so_round_e4m3.restype = _d
+    L.so_round_e4m3_array.argtypes = [_l, _pd, _pd]
     L.so_rope.argtypes = [_i, _pd, _d, _d, _pd]
     L.so_project.argtypes = [_i, _pd, _d, _d, _pd, _pd]
     L.so_prune.argtypes = [_i, _i, _pd, _pu8, _pd]
     L.so_attend.argtypes = [_i, _i, _pd, _l, _i, _pu8, _pd, _pu8, _pd, _l, _pd, _pd, _pd, _pd]
     L.so_prefill.argtypes = [_i, _i, _i, _i, _i, _l, _l, _pl, _pd, _pd, _pd, _d,
-                             _pu8, _pd, _pu8, _pd, _pd, _pd, _i]
+                             _pu8, _pd, _pu8, _pd, _pd, _pd, _i, _i]
     L.so_prefill.restype = _i
     L.so_project_batch.argtypes = [_i, _i, _i, _i, _pd, _pd, _pl, _pd, _d, _pd, _pd]
-    L.so_append_batch.argtypes = [_i, _i, _i, _i, _i, _l, _pl, _pd, _pd, _pu8, _pd, _pu8, _pd, _pd, _pd]
+    L.so_append_batch.argtypes = [_i, _i, _i, _i, _i, _l, _pl, _pd, _pd, _pu8, _pd, _pu8, _pd, _pd, _pd, _i]
     L.so_append_batch.restype = _i
     L.so_decode_batch.argtypes = [_i, _i, _i, _i, _i, _i, _l, _pl, _pd, _pu8, _pd, _pu8, _pd, _pd, _pd, _pd, _i]
     L.so_step.argtypes = [_i, _i, _i, _i, _i, _i, _l, _pl, _pd, _pd, _pd, _pd, _d,
-                          _pu8, _pd, _pu8, _pd, _pd, _pd, _pd, _pd, _pd, _i]
+                          _pu8, _pd, _pu8, _pd, _pd, _pd, _pd, _pd, _pd, _i, _i]
     L.so_step.restype = _i
     return L
 
@@ -85,6 +88,14 @@ def round_f16(x) -> np.ndarray:
     x = _f64(x)
     y = np.empty_like(x)
     lib().so_round_f16_array(x.size, x.reshape(-1), y.reshape(-1))
+    return y
+
+
+def round_e4m3(x) -> np.ndarray:
+    """Round to the nearest E4M3 value (ties to even, saturating at +-448)."""
+    x = _f64(x)
+    y = np.empty_like(x)
+    lib().so_round_e4m3_array(x.size, x.reshape(-1), y.reshape(-1))
     return y
 
 
@@ -139,10 +150,12 @@ def attend(qhat, kidx, kval, vidx, vval, kd, vd) -> np.ndarray:
 
 class OracleCache:
     """The hybrid cache of a batch in logical layout (float64, binary16-exact
-    values): sparse rows [B][H][ncap][k] and dense buffer [B][H][R][d]."""
+    values; with value_format 1 the sparse values are E4M3-exact): sparse rows
+    [B][H][ncap][k] and dense buffer [B][H][R][d]."""
 
-    def __init__(self, B: int, N_h: int, H_kv: int, d: int, R: int, k: int, ncap: int):
+    def __init__(self, B: int, N_h: int, H_kv: int, d: int, R: int, k: int, ncap: int, value_format: int = 0):
         self.B, self.N_h, self.H_kv, self.d, self.R, self.k, self.ncap = B, N_h, H_kv, d, R, k, ncap
+        self.value_format = int(value_format)
         self.kidx = np.zeros((B, H_kv, ncap, k), np.uint8)
         self.vidx = np.zeros_like(self.kidx)
         self.kval = np.zeros((B, H_kv, ncap, k))
@@ -152,7 +165,8 @@ class OracleCache:
 
     @classmethod
     def for_workload(cls, w, ncap: int | None = None):
-        return cls(w.B, w.N_h, w.H_kv, w.d_h, w.R, w.k, w.n_cap() if ncap is None else ncap)
+        return cls(w.B, w.N_h, w.H_kv, w.d_h, w.R, w.k, w.n_cap() if ncap is None else ncap,
+                   getattr(w, "value_format", 0))
 
     def _state(self):
         return (self.kidx, self.kval, self.vidx, self.vval, self.ringk, self.ringv)
@@ -163,7 +177,7 @@ class OracleCache:
         T = np.ascontiguousarray(T, np.int64)
         err = lib().so_prefill(self.B, self.H_kv, self.d, self.R, self.k, self.ncap, Kraw.shape[2], T,
                                Kraw, Vraw, _f64(P), float(base), *self._state(),
-                               nthreads or default_threads())
+                               nthreads or default_threads(), self.value_format)
         if err:
             raise ValueError("sparse capacity exceeded in prefill")
 
@@ -176,7 +190,8 @@ class OracleCache:
 
     def append(self, khat, vhat, pos):
         err = lib().so_append_batch(self.B, self.H_kv, self.d, self.R, self.k, self.ncap,
-                                    np.ascontiguousarray(pos, np.int64), _f64(khat), _f64(vhat), *self._state())
+                                    np.ascontiguousarray(pos, np.int64), _f64(khat), _f64(vhat), *self._state(),
+                                    self.value_format)
         if err:
             raise ValueError("sparse capacity exceeded in append")
 
@@ -194,7 +209,8 @@ class OracleCache:
         out = np.zeros((self.B, self.N_h, self.d))
         err = lib().so_step(self.B, self.N_h, self.H_kv, self.d, self.R, self.k, self.ncap,
                             np.ascontiguousarray(pos, np.int64), _f64(q), _f64(kraw), _f64(vnew), _f64(P),
-                            float(base), *self._state(), qhat, khat, out, nthreads or default_threads())
+                            float(base), *self._state(), qhat, khat, out, nthreads or default_threads(),
+                            self.value_format)
         if err:
             raise ValueError("sparse capacity exceeded in step")
         return qhat, khat, out

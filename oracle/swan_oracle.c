@@ -16,7 +16,9 @@
  * to binary16 are where the method stores it in the cache: the rotated key and
  * the value when they enter the dense buffer ([SWAN] section 4.2: values are
  * stored as float16, section 5.1).  Stored values are kept as doubles that are
- * exactly representable in binary16, so widening them back is exact.
+ * exactly representable in binary16, so widening them back is exact.  With
+ * 8-bit sparse values (section 5.1) the values a pruned row keeps are rounded
+ * once more, to E4M3, when they enter the sparse cache.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - RoPE pairs coordinate i with i + d/2 ("rotate half"), angle pos*theta_i,
@@ -72,6 +74,42 @@ void so_round_f16_array(long n, const double *x, double *y)
 {
     for (long i = 0; i < n; ++i)
         y[i] = so_round_f16(x[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* 8-bit float sparse values ([SWAN] section 5.1: the values kept in a      */
+/* sparse vector may be stored as 8-bit floats, 2k + 2 bytes a vector)      */
+/* ------------------------------------------------------------------------ */
+
+/* Round a double to the nearest E4M3 value, ties to even.  The pages name
+ * no 8-bit format and no scale; the reading here is the OCP E4M3 encoding
+ * (4 exponent bits with bias 7, 3 fraction bits, normal exponents -6..8,
+ * subnormal spacing 2^-9, largest finite value 448, no infinities) applied
+ * with no scale, saturating: magnitudes that round past 448 become 448.
+ * NaN stays NaN. */
+double so_round_e4m3(double x)
+{
+    if (isnan(x) || x == 0.0)
+        return x;
+    if (isinf(x))
+        return copysign(448.0, x);
+    double ax = fabs(x);
+    int e;
+    frexp(ax, &e);            /* ax = m * 2^e with m in [0.5, 1) */
+    int ex = e - 1;           /* floor(log2(ax)) */
+    if (ex < -6)
+        ex = -6;              /* subnormal range: fixed spacing 2^-9 */
+    double ulp = ldexp(1.0, ex - 3);
+    double r = nearbyint(ax / ulp) * ulp;
+    if (r > 448.0)
+        r = 448.0;
+    return copysign(r, x);
+}
+
+void so_round_e4m3_array(long n, const double *x, double *y)
+{
+    for (long i = 0; i < n; ++i)
+        y[i] = so_round_e4m3(x[i]);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -222,24 +260,34 @@ static size_t unit_off(int b, int h, int H, size_t per) { return ((size_t)b * H 
  * pos, evicting and pruning the token that leaves the buffer ([SWAN]
  * section 4.2: the oldest buffered vectors are evicted, pruned and appended
  * to the sparse cache). */
+/* Prune x into a sparse row and store its kept values in the sparse value
+ * format: binary16 as they are (vfmt 0) or rounded to E4M3 (vfmt 1). */
+static void so_prune_store(int d, int k, int vfmt, const double *x, uint8_t *idx, double *val)
+{
+    so_prune(d, k, x, idx, val);
+    if (vfmt == 1)
+        for (int i = 0; i < k; ++i)
+            val[i] = so_round_e4m3(val[i]);
+}
+
 static void so_append_unit(int d, int R, int k, long ncap, long pos,
                            const double *khat, const double *vhat,
                            uint8_t *kidx, double *kval, uint8_t *vidx, double *vval,
-                           double *ringk, double *ringv, int *err)
+                           double *ringk, double *ringv, int vfmt, int *err)
 {
     if (pos < 0) return; /* inactive sequence (a library convention, not the pages'): nothing appended */
     if (R == 0) {
         if (pos >= ncap) { *err = 1; return; }
-        so_prune(d, k, khat, kidx + (size_t)pos * k, kval + (size_t)pos * k);
-        so_prune(d, k, vhat, vidx + (size_t)pos * k, vval + (size_t)pos * k);
+        so_prune_store(d, k, vfmt, khat, kidx + (size_t)pos * k, kval + (size_t)pos * k);
+        so_prune_store(d, k, vfmt, vhat, vidx + (size_t)pos * k, vval + (size_t)pos * k);
         return;
     }
     long slot = pos % R;
     if (pos >= R) {
         long row = pos - R;  /* the evicted token's position = its sparse row */
         if (row >= ncap) { *err = 1; return; }
-        so_prune(d, k, ringk + (size_t)slot * d, kidx + (size_t)row * k, kval + (size_t)row * k);
-        so_prune(d, k, ringv + (size_t)slot * d, vidx + (size_t)row * k, vval + (size_t)row * k);
+        so_prune_store(d, k, vfmt, ringk + (size_t)slot * d, kidx + (size_t)row * k, kval + (size_t)row * k);
+        so_prune_store(d, k, vfmt, ringv + (size_t)slot * d, vidx + (size_t)row * k, vval + (size_t)row * k);
     }
     memcpy(ringk + (size_t)slot * d, khat, sizeof(double) * d);
     memcpy(ringv + (size_t)slot * d, vhat, sizeof(double) * d);
@@ -253,7 +301,7 @@ static void so_append_unit(int d, int R, int k, long ncap, long pos,
 int so_prefill(int B, int H, int d, int R, int k, long ncap, long Tmax, const long *T,
                const double *Kraw, const double *Vraw, const double *P, double base,
                uint8_t *kidx, double *kval, uint8_t *vidx, double *vval,
-               double *ringk, double *ringv, int nthreads)
+               double *ringk, double *ringv, int nthreads, int vfmt)
 {
     int err = 0;
 #pragma omp parallel for collapse(2) schedule(dynamic) num_threads(nthreads) reduction(| : err)
@@ -273,7 +321,7 @@ int so_prefill(int B, int H, int d, int R, int k, long ncap, long Tmax, const lo
                                kidx + unit_off(b, h, H, (size_t)ncap * k), kval + unit_off(b, h, H, (size_t)ncap * k),
                                vidx + unit_off(b, h, H, (size_t)ncap * k), vval + unit_off(b, h, H, (size_t)ncap * k),
                                ringk + unit_off(b, h, H, (size_t)R * d), ringv + unit_off(b, h, H, (size_t)R * d),
-                               &err);
+                               vfmt, &err);
             }
         }
     return err;
@@ -298,7 +346,7 @@ void so_project_batch(int B, int N, int H, int d, const double *q, const double 
 int so_append_batch(int B, int H, int d, int R, int k, long ncap, const long *pos,
                     const double *khat, const double *vhat,
                     uint8_t *kidx, double *kval, uint8_t *vidx, double *vval,
-                    double *ringk, double *ringv)
+                    double *ringk, double *ringv, int vfmt)
 {
     int err = 0;
     for (int b = 0; b < B; ++b)
@@ -311,7 +359,8 @@ int so_append_batch(int B, int H, int d, int R, int k, long ncap, const long *po
             so_append_unit(d, R, k, ncap, pos[b], kh, vh,
                            kidx + unit_off(b, h, H, (size_t)ncap * k), kval + unit_off(b, h, H, (size_t)ncap * k),
                            vidx + unit_off(b, h, H, (size_t)ncap * k), vval + unit_off(b, h, H, (size_t)ncap * k),
-                           ringk + unit_off(b, h, H, (size_t)R * d), ringv + unit_off(b, h, H, (size_t)R * d), &err);
+                           ringk + unit_off(b, h, H, (size_t)R * d), ringv + unit_off(b, h, H, (size_t)R * d), vfmt,
+                           &err);
         }
     return err;
 }
@@ -350,10 +399,10 @@ void so_decode_batch(int B, int N, int H, int d, int R, int k, long ncap, const 
 int so_step(int B, int N, int H, int d, int R, int k, long ncap, const long *pos,
             const double *q, const double *kraw, const double *vnew, const double *P, double base,
             uint8_t *kidx, double *kval, uint8_t *vidx, double *vval, double *ringk, double *ringv,
-            double *qhat, double *khat, double *out, int nthreads)
+            double *qhat, double *khat, double *out, int nthreads, int vfmt)
 {
     so_project_batch(B, N, H, d, q, kraw, pos, P, base, qhat, khat);
-    int err = so_append_batch(B, H, d, R, k, ncap, pos, khat, vnew, kidx, kval, vidx, vval, ringk, ringv);
+    int err = so_append_batch(B, H, d, R, k, ncap, pos, khat, vnew, kidx, kval, vidx, vval, ringk, ringv, vfmt);
     for (size_t i = 0; i < (size_t)B * H * d; ++i)
         khat[i] = so_round_f16(khat[i]);
     so_decode_batch(B, N, H, d, R, k, ncap, pos, qhat, kidx, kval, vidx, vval, ringk, ringv, out, nthreads);

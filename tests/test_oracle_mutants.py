@@ -25,6 +25,10 @@ MUTANTS = {
     "ring_slot": ("long slot = pos % R;", "long slot = (pos + 1) % R;"),
     "round_ties_away": ("double r = nearbyint(ax / ulp) * ulp;", "double r = round(ax / ulp) * ulp;"),
     "subnormal_spacing": ("ex = -14;", "ex = -15;"),
+    "e4m3_subnormal": ("ex = -6;", "ex = -7;"),
+    "e4m3_fraction_bits": ("double ulp = ldexp(1.0, ex - 3);", "double ulp = ldexp(1.0, ex - 4);"),
+    "e4m3_saturation": ("if (r > 448.0)\n        r = 448.0;", "if (r > 480.0)\n        r = 480.0;"),
+    "fp8_values_unrounded": ("if (vfmt == 1)", "if (vfmt == 2)"),
     "drop_newest": ("long nd = ctx <= 0 ? 0 : (ctx < R ? ctx : R);", "long nd = ctx <= 0 ? 0 : (ctx < R ? ctx : R - 1);"),
     "softmax_bias": ("scratch[t] = exp(scratch[t] - m);",
                      "scratch[t] = exp(scratch[t] - m) * (t == 0 ? 1.0000001 : 1.0);"),

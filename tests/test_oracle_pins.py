@@ -347,3 +347,90 @@ def test_inactive_sequence_appends_nothing_and_attends_nothing():
     assert any(not np.array_equal(x0[0], x1[0]) for x0, x1 in zip(before, after))
     out = oc.decode(r.standard_normal((B, N, D)), pos)
     assert not out[1:].any() and np.abs(out[0]).sum() > 0
+
+
+# ---------------------------------------------------------------------------
+# 8-bit sparse values (reading: OCP E4M3, no scale, round to nearest even,
+# saturating at 448)
+# ---------------------------------------------------------------------------
+
+def _e4m3_codes():
+    """Every finite E4M3 value, decoded from its bit fields by definition:
+    exponent bias 7, 3 fraction bits, exponent field 0 subnormal (m/8 * 2^-6),
+    code S.1111.111 NaN (no infinities)."""
+    vals = []
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            continue
+        v = (1 + m / 8) * 2.0 ** (e - 7) if e else (m / 8) * 2.0 ** -6
+        vals.append(-v if s else v)
+    return np.array(vals)
+
+
+def test_e4m3_codes_are_fixed_points():
+    codes = _e4m3_codes()
+    assert len(codes) == 254 and codes.max() == 448 and np.min(np.abs(codes[codes != 0])) == 2.0 ** -9
+    np.testing.assert_array_equal(oracle.round_e4m3(codes), codes)
+
+
+def test_e4m3_rounding_is_nearest_with_ties_to_even():
+    """Brute force over the code table: the nearest finite value, and on an
+    exact tie the one whose fraction field is even."""
+    codes = np.unique(_e4m3_codes())
+    r = np.random.default_rng(5)
+    pos = codes[codes >= 0]
+    mids = (pos[:-1] + pos[1:]) / 2
+    x = np.concatenate([r.uniform(-448, 448, 2000), r.uniform(-0.02, 0.02, 500), mids, -mids,
+                        np.nextafter(mids, 0), np.nextafter(mids, 1e9)])
+    got = oracle.round_e4m3(x)
+    for xi, gi in zip(x, got):
+        d = np.abs(codes - xi)
+        best = codes[d == d.min()]
+        if len(best) == 1:
+            assert gi == best[0], (xi, gi, best)
+        else:  # a tie: the even fraction field (the code whose value/ulp is even)
+            frac_even = []
+            for b in best:
+                ab = abs(b)
+                ex = max(int(np.floor(np.log2(ab))) if ab else -6, -6)
+                frac_even.append(int(round(ab / 2.0 ** (ex - 3))) % 2 == 0)
+            assert gi == best[frac_even.index(True)], (xi, gi, best)
+
+
+def test_e4m3_matches_torch_in_range_and_saturates_beyond():
+    """Against torch's float8_e4m3fn conversion (a separate implementation)
+    for float32 inputs within +-448; beyond it the reading saturates where
+    torch gives NaN."""
+    import torch
+    r = np.random.default_rng(9)
+    x = np.concatenate([r.standard_normal(4000) * 4, r.standard_normal(1000) * 1e-2, r.uniform(-448, 448, 1000),
+                        [0.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -10, 1.5 * 2.0 ** -10, 240.0, 232.0]])
+    x = x.astype(np.float32)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.round_e4m3(x.astype(np.float64)), want)
+    big = np.array([448.5, 463.9, 464.0, 500.0, 65504.0, np.inf])
+    np.testing.assert_array_equal(oracle.round_e4m3(big), np.full(6, 448.0))
+    np.testing.assert_array_equal(oracle.round_e4m3(-big), np.full(6, -448.0))
+    assert np.isnan(oracle.round_e4m3(np.array([np.nan])))[0]
+
+
+def test_fp8_rows_keep_the_fp16_selection():
+    """With 8-bit values the pruned row keeps the same indices as with fp16
+    values (the top-k is taken on the stored fp16 entry) and each kept value
+    is the E4M3 rounding of the fp16 one."""
+    r = np.random.default_rng(21)
+    B, N, H, R, k, ncap = 2, 4, 2, 4, 16, 20
+    K = r.standard_normal((B, H, 15, D)) * 3
+    V = r.standard_normal((B, H, 15, D)) * 300  # reaches the saturation range
+    P = np.stack([np.eye(D)] * H)
+    a = oracle.OracleCache(B, N, H, D, R, k, ncap)
+    b8 = oracle.OracleCache(B, N, H, D, R, k, ncap, value_format=1)
+    a.prefill(K, V, np.array([15, 12], np.int64), P)
+    b8.prefill(K, V, np.array([15, 12], np.int64), P)
+    np.testing.assert_array_equal(a.kidx, b8.kidx)
+    np.testing.assert_array_equal(a.vidx, b8.vidx)
+    np.testing.assert_array_equal(oracle.round_e4m3(a.kval), b8.kval)
+    np.testing.assert_array_equal(oracle.round_e4m3(a.vval), b8.vval)
+    np.testing.assert_array_equal(a.ringk, b8.ringk)  # the dense buffer stays fp16
+    assert np.abs(b8.vval).max() == 448.0
