@@ -79,7 +79,9 @@ def main():
                     help="untimed steps first (replaying the step sequence); the GPU's power "
                          "management needs ~20 ms of sustained load to settle")
     ap.add_argument("--config", type=int, default=3, help="workload number (1-5); 3 is the headline")
-    ap.add_argument("--split-tokens", type=int, default=0, help="sparse rows per split (0 = automatic)")
+    ap.add_argument("--split-tokens", type=int, default=0, help="work rows per wave (0 = automatic)")
+    ap.add_argument("--values", choices=("fp16", "fp8"), default="fp16",
+                    help="storage of the sparse values (fp8: E4M3, one byte each)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle stepping time of the sample")
@@ -103,6 +105,9 @@ def main():
         sys.exit(1)
     S.lib()
     w = wl.config(args.config)
+    if args.values == "fp8":
+        w = w.scaled(value_format=1)
+    vbytes = 1 if w.value_format else 2
     if args.steps > w.steps:
         w = w.scaled(steps=args.steps)
     dec = build_decoder(w, args.split_tokens)
@@ -195,8 +200,8 @@ def main():
         pos = inputs[s][3].cpu().numpy()
         n = [max(0, int(p) + 1 - w.R) for p in pos]
         f = [min(int(p) + 1, w.R) for p in pos]
-        split_bytes.append(acc.split_kernel_bytes(n, w.H_kv, w.N_h, f, w.k))
-        dec_bytes.append(acc.decode_bytes(n, w.H_kv, w.N_h, f, w.k))
+        split_bytes.append(acc.split_kernel_bytes(n, w.H_kv, w.N_h, f, w.k, value_bytes=vbytes))
+        dec_bytes.append(acc.decode_bytes(n, w.H_kv, w.N_h, f, w.k, value_bytes=vbytes))
         flops.append(acc.decode_flops(n, w.H_kv, w.N_h, f, w.k))
     split_avg_ms = float(np.mean(split_ms))
     # bytes of the last step's launch over the back-to-back duration
@@ -207,7 +212,8 @@ def main():
         from decode_attention_compressed_02_amd.profiling import kernel_source_hash
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("kernel_source_sha") == kernel_source_hash() and tr.get("workload") == w.name:
+        if (tr.get("kernel_source_sha") == kernel_source_hash() and tr.get("workload") == w.name
+                and tr.get("value_format", 0) == w.value_format):
             traffic = tr.get("hbm_bytes_per_launch")
 
     if args.copy_calibration_mib > 0:
@@ -232,9 +238,11 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded N(0,1) raw keys/queries, stored-basis values, random orthogonal P_QK)",
-        "config": {"workload": f"config {args.config}: {w.name}", "B": w.B, "N_h": w.N_h, "H_kv": w.H_kv,
+        "config": {"workload": f"config {args.config}: {w.name}" + (", fp8 values" if w.value_format else ""),
+                   "B": w.B, "N_h": w.N_h, "H_kv": w.H_kv,
                    "d_h": w.d_h, "ctx_first_step": int(w.ctx[0]), "R": w.R, "k": w.k,
-                   "storage": "fp16 values, uint8 indices, fp16 dense buffer", "split_waves": nsplit,
+                   "storage": f"{'fp8 E4M3' if w.value_format else 'fp16'} values, uint8 indices, fp16 dense buffer",
+                   "split_waves": nsplit,
                    "split_tokens": dec.dims.split_tokens or "auto"},
         "step_hbm_GBps": float(np.mean(dec_bytes)) / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": float(np.mean(dec_bytes)) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,

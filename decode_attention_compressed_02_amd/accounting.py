@@ -65,23 +65,26 @@ def break_even_length(b: int, k: int, d_h: int = 128) -> float:
 # per-step traffic and work of this library's decode kernels
 # ---------------------------------------------------------------------------
 
-def split_kernel_bytes(n_per_seq, H_kv: int, N_h: int, R_fill_per_seq, k: int, d_h: int = 128) -> int:
+def split_kernel_bytes(n_per_seq, H_kv: int, N_h: int, R_fill_per_seq, k: int, d_h: int = 128,
+                       value_bytes: int = 2) -> int:
     """Algorithmic HBM bytes of one launch of the split (streaming) kernel:
-    every sparse row read once (K and V: k one-byte indices and k fp16
-    values each, 6k bytes per token per kv-head), every buffered token read
-    once (K and V fp16, 4 d_h bytes), and the fp32 rotated queries read once.
-    Split-K partials (a few percent) are not counted."""
-    sparse = sum(int(n) for n in n_per_seq) * H_kv * 6 * k
+    every sparse row read once (K and V: k one-byte indices and k values of
+    value_bytes each -- 6k bytes per token per kv-head with fp16 values, 4k
+    with fp8), every buffered token read once (K and V fp16, 4 d_h bytes),
+    and the fp32 rotated queries read once.  Partials (a few percent) are
+    not counted."""
+    sparse = sum(int(n) for n in n_per_seq) * H_kv * 2 * k * (1 + value_bytes)
     dense = sum(int(r) for r in R_fill_per_seq) * H_kv * 4 * d_h
     q_in = len(list(n_per_seq)) * N_h * d_h * 4
     return sparse + dense + q_in
 
 
-def decode_bytes(n_per_seq, H_kv: int, N_h: int, R_fill_per_seq, k: int, d_h: int = 128) -> int:
+def decode_bytes(n_per_seq, H_kv: int, N_h: int, R_fill_per_seq, k: int, d_h: int = 128,
+                 value_bytes: int = 2) -> int:
     """Algorithmic bytes of the whole decode (split + reduce): the split
     kernel's bytes plus the fp32 outputs written once."""
     B = len(list(n_per_seq))
-    return split_kernel_bytes(n_per_seq, H_kv, N_h, R_fill_per_seq, k, d_h) + B * N_h * d_h * 4
+    return split_kernel_bytes(n_per_seq, H_kv, N_h, R_fill_per_seq, k, d_h, value_bytes) + B * N_h * d_h * 4
 
 
 def decode_flops(n_per_seq, H_kv: int, N_h: int, R_fill_per_seq, k: int, d_h: int = 128) -> float:

@@ -19,7 +19,9 @@ class HybridCache:
         n_idx, n_val, n_buf = S.swan_cache_bytes(dims)
         z = lambda n, dt: torch.zeros(max(n, 1), dtype=dt, device=device)
         self.k_idx, self.v_idx = z(n_idx, torch.uint8), z(n_idx, torch.uint8)
-        self.k_val, self.v_val = z(n_val // 2, torch.float16), z(n_val // 2, torch.float16)
+        # sparse values: fp16, or E4M3 bytes (held as uint8: torch has no arithmetic on them here)
+        vdt, vb = (torch.uint8, 1) if dims.value_format == S.SWAN_VALUES_FP8_E4M3 else (torch.float16, 2)
+        self.k_val, self.v_val = z(n_val // vb, vdt), z(n_val // vb, vdt)
         self.k_buf, self.v_buf = z(n_buf // 2, torch.float16), z(n_buf // 2, torch.float16)
         self.block_table = None
         if dims.block_size > 0:

@@ -53,8 +53,12 @@ swan_status check_dims(const swan_dims *d)
     }
     if (d->split_tokens < 0 || d->split_tokens % 64)
         return fail(SWAN_ERR_INVALID_ARG, "split_tokens = %d must be 0 or a positive multiple of 64", d->split_tokens);
+    if (d->value_format != SWAN_VALUES_FP16 && d->value_format != SWAN_VALUES_FP8_E4M3)
+        return fail(SWAN_ERR_UNSUPPORTED, "value_format = %d, supported: 0 (fp16), 1 (fp8 E4M3)", d->value_format);
     return SWAN_OK;
 }
+
+int value_bytes(const swan_dims *d) { return d->value_format == SWAN_VALUES_FP8_E4M3 ? 1 : 2; }
 
 int64_t row_cap(const swan_dims *d)
 {
@@ -79,6 +83,7 @@ swan::SparseGeom geom(const swan_dims *d, const swan_cache *c)
     g.bs = d->block_size;
     g.max_blocks = d->max_blocks;
     g.num_blocks = d->num_blocks;
+    g.vbytes = value_bytes(d);
     g.bt = d->block_size > 0 ? c->block_table : nullptr;
     return g;
 }
@@ -170,7 +175,7 @@ swan_status swan_cache_bytes(const swan_dims *d, size_t out[3])
     const size_t rows = d->block_size > 0 ? (size_t)d->num_blocks * d->H_kv * d->block_size
                                           : (size_t)d->B * d->H_kv * d->n_cap;
     out[0] = rows * ks;
-    out[1] = rows * ks * 2;
+    out[1] = rows * ks * (size_t)value_bytes(d);
     out[2] = (size_t)d->B * d->H_kv * d->R * swan::kD * 2;
     return SWAN_OK;
 }
@@ -205,8 +210,8 @@ swan_status swan_append_evict(const swan_dims *d, const swan_cache *c, const int
     a.geom = geom(d, c);
     a.kidx = c->k_idx;
     a.vidx = c->v_idx;
-    a.kval = c->k_val;
-    a.vval = c->v_val;
+    a.kval = (uint8_t *)c->k_val;
+    a.vval = (uint8_t *)c->v_val;
     a.kbuf = c->k_buf;
     a.vbuf = c->v_buf;
     a.pos = pos;
@@ -237,8 +242,8 @@ swan_status swan_project_append(const swan_dims *d, const swan_cache *c, const f
     a.geom = geom(d, c);
     a.kidx = c->k_idx;
     a.vidx = c->v_idx;
-    a.kval = c->k_val;
-    a.vval = c->v_val;
+    a.kval = (uint8_t *)c->k_val;
+    a.vval = (uint8_t *)c->v_val;
     a.kbuf = c->k_buf;
     a.vbuf = c->v_buf;
     a.pos = pos;
@@ -276,8 +281,8 @@ static swan::SplitArgs split_args(const swan_dims *d, const swan_cache *c, const
     a.q_hat = q_hat;
     a.kidx = c->k_idx;
     a.vidx = c->v_idx;
-    a.kval = c->k_val;
-    a.vval = c->v_val;
+    a.kval = (uint8_t *)c->k_val;
+    a.vval = (uint8_t *)c->v_val;
     a.kbuf = c->k_buf;
     a.vbuf = c->v_buf;
     a.part_o = (float *)ws;
@@ -357,8 +362,8 @@ swan_status swan_prefill_convert(const swan_dims *d, const swan_cache *c, const 
     a.geom = geom(d, c);
     a.kidx = c->k_idx;
     a.vidx = c->v_idx;
-    a.kval = c->k_val;
-    a.vval = c->v_val;
+    a.kval = (uint8_t *)c->k_val;
+    a.vval = (uint8_t *)c->v_val;
     a.kbuf = c->k_buf;
     a.vbuf = c->v_buf;
     a.len = len;
@@ -387,10 +392,11 @@ swan_status swan_copy_blocks(const swan_dims *d, const swan_cache *c, const int3
     a.count = count;
     a.num_blocks = d->num_blocks;
     a.block_bytes_idx = (int64_t)d->H_kv * d->block_size * row_stride(d->k);
+    a.vbytes = value_bytes(d);
     a.kidx = c->k_idx;
     a.vidx = c->v_idx;
-    a.kval = c->k_val;
-    a.vval = c->v_val;
+    a.kval = (uint8_t *)c->k_val;
+    a.vval = (uint8_t *)c->v_val;
     a.src = src;
     a.dst = dst;
     return hip_status(swan::launch_copy_blocks(a, (hipStream_t)stream), "swan_copy_blocks launch");

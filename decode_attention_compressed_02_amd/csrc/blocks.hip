@@ -5,8 +5,8 @@
 //
 // One workgroup of 256 threads per (copy, plane) streams the block's bytes
 // with 16-byte accesses; a block of a plane is H_kv x block_size x k_stride
-// entries (k_stride bytes per row for the index planes, 2 k_stride for the
-// value planes), always a multiple of 16 bytes.
+// entries (k_stride bytes per row for the index planes, k_stride times the
+// value width for the value planes), always a multiple of 16 bytes.
 #include "swan_internal.h"
 
 namespace swan {
@@ -19,8 +19,8 @@ __global__ __launch_bounds__(256) void k_copy_blocks(CopyBlocksArgs a)
     const int src = a.src[i], dst = a.dst[i];
     // ids outside the pool are a caller error: the pair is skipped
     if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks || src == dst) return;
-    uint8_t *base = plane == 0 ? a.kidx : plane == 1 ? a.vidx : plane == 2 ? (uint8_t *)a.kval : (uint8_t *)a.vval;
-    const int64_t bytes = plane < 2 ? a.block_bytes_idx : 2 * a.block_bytes_idx;
+    uint8_t *base = plane == 0 ? a.kidx : plane == 1 ? a.vidx : plane == 2 ? a.kval : a.vval;
+    const int64_t bytes = plane < 2 ? a.block_bytes_idx : a.vbytes * a.block_bytes_idx;
     const cpy_u32x4 *s = (const cpy_u32x4 *)(base + (int64_t)src * bytes);
     cpy_u32x4 *d = (cpy_u32x4 *)(base + (int64_t)dst * bytes);
     for (int64_t j = threadIdx.x; j < bytes / 16; j += 256) d[j] = s[j];

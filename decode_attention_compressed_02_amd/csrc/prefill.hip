@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a)
                 const int64_t off = t < row_cap ? row_offset_rt(a.geom, b, h, t) : -1;
                 if (off >= 0)
                     wave_prune_row(lane, lo, hi, a.k, a.geom.ks, (which ? a.vidx : a.kidx) + off,
-                                   (which ? a.vval : a.kval) + off);
+                                   (which ? a.vval : a.kval) + off * a.geom.vbytes, a.geom.vbytes);
             } else {
                 uint16_t *buf = (which ? a.vbuf : a.kbuf) + (u * a.R + t % a.R) * kD;
                 buf[lane] = lo;

@@ -11,7 +11,7 @@
 // (running max m, running sum l) over the piece's sparse rows and buffered
 // tokens and writes (m, l, unnormalised output) per query head.
 //
-// Sparse stream: a stored row is KS entries (uint8 index, fp16 value).  A
+// Sparse stream: a stored row is KS entries (uint8 index, fp16 or fp8 value).  A
 // lane loads E consecutive entries of one row from each of the four planes
 // (K index, K value, V index, V value), KS / E lanes share a row and TPI =
 // 64 E / KS rows are in flight per wave iteration, so each wave load
@@ -329,24 +329,37 @@ __device__ __forceinline__ uint32_t acc_offset_256(const Words<NB> &o, int e, ui
     return __builtin_amdgcn_perm(o.w[e >> 2], slot_off, sel);
 }
 
-template <int NB>
-__device__ __forceinline__ float half_at(const Words<NB> &o, int e)
+// Value e of a row slice: fp16 (VB = 2 bytes) or fp8 E4M3 (VB = 1; the
+// gfx950 conversion decodes the OCP E4M3 encoding exactly).  e is a
+// compile-time constant after unrolling, so the byte select folds.
+template <int VB, int NB>
+__device__ __forceinline__ float value_at(const Words<NB> &o, int e)
 {
-    return h2f((uint16_t)(o.w[e >> 1] >> ((e & 1) * 16)));
+    if constexpr (VB == 2) {
+        return h2f((uint16_t)(o.w[e >> 1] >> ((e & 1) * 16)));
+    } else {
+        const uint32_t w = o.w[e >> 2];
+        switch (e & 3) {
+        case 0: return __builtin_amdgcn_cvt_f32_fp8(w, 0);
+        case 1: return __builtin_amdgcn_cvt_f32_fp8(w, 1);
+        case 2: return __builtin_amdgcn_cvt_f32_fp8(w, 2);
+        default: return __builtin_amdgcn_cvt_f32_fp8(w, 3);
+        }
+    }
 }
 
 // E entries of one sparse row: the key planes and the value planes are
-// separate ring slots (consumed in different phases)
-template <int E>
+// separate ring slots (consumed in different phases); VB bytes per value
+template <int E, int VB>
 struct KSlot {
     Words<E> ki;
-    Words<2 * E> kv;
+    Words<VB * E> kv;
     bool ok; // the row's block-table entry is a block of the pool
 };
-template <int E>
+template <int E, int VB>
 struct VSlot {
     Words<E> vi;
-    Words<2 * E> vv;
+    Words<VB * E> vv;
 };
 
 // 2^x with the hardware instruction: arguments are <= kRescaleSlack, and
@@ -366,24 +379,28 @@ constexpr int kKeepLoadOrder = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0x200 | 0x
 // pass 1
 // ---------------------------------------------------------------------------
 
-// Ring depth of the sparse stream: about kInflightBytes per lane in flight
-// (6 E bytes per row slice), between 2 and 8 slots.
+// Ring depth of the sparse stream: about SWAN_INFLIGHT_BYTES per lane in
+// flight (2 (1 + VB) E bytes per row slice of the four planes), between 2
+// and 8 slots.
 #ifndef SWAN_INFLIGHT_BYTES
 #define SWAN_INFLIGHT_BYTES 192
 #endif
-__host__ __device__ constexpr int split_depth(int E)
+__host__ __device__ constexpr int split_depth(int E, int VB)
 {
-    const int d = (SWAN_INFLIGHT_BYTES + 6 * E - 1) / (6 * E);
+    const int slice = 2 * (1 + VB) * E;
+    const int d = (SWAN_INFLIGHT_BYTES + slice - 1) / slice;
     return d < 2 ? 2 : (d > 8 ? 8 : d);
 }
 
-template <int G, int KS, bool PAGED, bool PAD>
+template <int G, int KS, bool PAGED, bool PAD, int VB>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS)))) void k_split(SplitArgs a)
 {
     constexpr int E = split_entries(G, KS);
     constexpr int LPT = KS / E;     // lanes per row
     constexpr int TPI = kWave / LPT; // rows per iteration = accumulator copies
-    constexpr int D = split_depth(E);
+    // fp8 values: the same bytes in flight in more slots, except where the
+    // register budget of two waves per SIMD has no room for them
+    constexpr int D = split_depth(E, split_waves_per_simd(G, KS) == 2 ? 2 : VB);
     constexpr int NACC = TPI * kD * G;
     static_assert(LPT * E == KS && TPI * LPT == kWave, "bad split shape");
     static_assert(split_lds_bytes(G, KS) == 4 * (kD * G + NACC), "host and device disagree on LDS size");
@@ -563,13 +580,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
                 const int tl = lane % TPI, sub = lane / TPI;
                 float *my_acc = acc + tl * G; // coordinate c of this slot: my_acc[c * TPI * G]
                 const uint8_t *kidx = a.kidx, *vidx = a.vidx;
-                const uint16_t *kval = a.kval, *vval = a.vval;
+                const uint8_t *kval = a.kval, *vval = a.vval; // VB bytes per entry
                 if constexpr (!PAGED) { // per-unit base in scalar registers, 32-bit lane offsets
                     const int64_t ub = ((int64_t)b * a.H + h) * a.geom.n_cap * KS;
                     kidx += ub;
                     vidx += ub;
-                    kval += ub;
-                    vval += ub;
+                    kval += ub * VB;
+                    vval += ub * VB;
                 }
                 // entry offset of this lane's slice of row r0 + tl (rows past t1
                 // re-read the last row and are masked); paged rows whose block-table
@@ -586,8 +603,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
                         return (uint32_t)(r * KS + sub * E);
                     }
                 };
-                KSlot<E> rk[D];
-                VSlot<E> rv[D];
+                KSlot<E, VB> rk[D];
+                VSlot<E, VB> rv[D];
                 // Contiguous rows: a buffer resource per plane covers rows r0 .. t1-1
                 // (scalar arithmetic); each lane reads its slice at a fixed offset and
                 // rows past t1 read zeros (masked by valid).  Paged rows go through the
@@ -619,41 +636,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
                 // buffer resource per plane and pass, covering rows rp .. t1-1 (the
                 // rest read as zeros), and slot d at a constant offset from it, so
                 // the per-slot address work is an immediate offset.
-                auto load_k = [&](int rp, int d, KSlot<E> &st) {
+                auto load_k = [&](int rp, int d, KSlot<E, VB> &st) {
                     const int r0 = rp + d * TPI;
                     if (PAGED && !slot_blocks) {
                         const uint32_t o = slice(r0, st.ok);
                         load_words<E>(kidx + o, st.ki);
-                        load_words<2 * E>(kval + o, st.kv);
+                        load_words<VB * E>(kval + (int64_t)o * VB, st.kv);
                     } else if constexpr (PAGED) {
                         uint32_t rows;
                         const int64_t base = slot_base(r0, rows, st.ok);
                         buffer_words<E>(buffer_rsrc(kidx + base, rows * KS), lane_off, st.ki);
-                        buffer_words<2 * E>(buffer_rsrc(kval + base, rows * KS * 2), 2 * lane_off, st.kv);
+                        buffer_words<VB * E>(buffer_rsrc(kval + base * VB, rows * KS * VB), VB * lane_off, st.kv);
                     } else {
                         const uint32_t rows = (uint32_t)max(t1 - rp, 0), off = lane_off + d * TPI * KS;
                         st.ok = true;
                         buffer_words<E>(buffer_rsrc(kidx + (int64_t)rp * KS, rows * KS), off, st.ki);
-                        buffer_words<2 * E>(buffer_rsrc(kval + (int64_t)rp * KS, rows * KS * 2), 2 * off, st.kv);
+                        buffer_words<VB * E>(buffer_rsrc(kval + (int64_t)rp * KS * VB, rows * KS * VB), VB * off, st.kv);
                     }
                 };
-                auto load_v = [&](int rp, int d, VSlot<E> &st) {
+                auto load_v = [&](int rp, int d, VSlot<E, VB> &st) {
                     const int r0 = rp + d * TPI;
                     if (PAGED && !slot_blocks) {
                         bool ok;
                         const uint32_t o = slice(r0, ok);
                         load_words<E>(vidx + o, st.vi);
-                        load_words<2 * E>(vval + o, st.vv);
+                        load_words<VB * E>(vval + (int64_t)o * VB, st.vv);
                     } else if constexpr (PAGED) {
                         uint32_t rows;
                         bool ok;
                         const int64_t base = slot_base(r0, rows, ok);
                         buffer_words<E>(buffer_rsrc(vidx + base, rows * KS), lane_off, st.vi);
-                        buffer_words<2 * E>(buffer_rsrc(vval + base, rows * KS * 2), 2 * lane_off, st.vv);
+                        buffer_words<VB * E>(buffer_rsrc(vval + base * VB, rows * KS * VB), VB * lane_off, st.vv);
                     } else {
                         const uint32_t rows = (uint32_t)max(t1 - rp, 0), off = lane_off + d * TPI * KS;
                         buffer_words<E>(buffer_rsrc(vidx + (int64_t)rp * KS, rows * KS), off, st.vi);
-                        buffer_words<2 * E>(buffer_rsrc(vval + (int64_t)rp * KS, rows * KS * 2), 2 * off, st.vv);
+                        buffer_words<VB * E>(buffer_rsrc(vval + (int64_t)rp * KS * VB, rows * KS * VB), VB * off, st.vv);
                     }
                 };
                 // entries at row positions >= k are padding (index 0, value +0): they
@@ -691,7 +708,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
                 };
                 // scores of one ring slot (gather q_hat at the stored key indices);
                 // rows past t1 get -inf
-                auto score = [&](int r0, const KSlot<E> &st, float (&sc)[G]) {
+                auto score = [&](int r0, const KSlot<E, VB> &st, float (&sc)[G]) {
                     const bool valid = (r0 + tl < t1) && st.ok;
                     float q[E][G], s[G]; // all gathers in flight before the first product
 #pragma unroll
@@ -700,7 +717,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
                     for (int hh = 0; hh < G; ++hh) s[hh] = 0.f;
 #pragma unroll
                     for (int e = 0; e < E; ++e) {
-                        const float v = half_at(st.kv, e);
+                        const float v = value_at<VB>(st.kv, e);
 #pragma unroll
                         for (int hh = 0; hh < G; ++hh) s[hh] = fmaf(q[e][hh], v, s[hh]);
                     }
@@ -781,8 +798,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
                     for (int d = 0; d < D; ++d) {
                         // both LDS batches in flight before any arithmetic: the value
                         // reads of pass rb and the key gathers of pass rb + P
-                        const KSlot<E> &ks = rk[d];
-                        const VSlot<E> &vs = rv[d];
+                        const KSlot<E, VB> &ks = rk[d];
+                        const VSlot<E, VB> &vs = rv[d];
                         float o[E][G], q[E][G];
                         float *vaddr[E];
 #pragma unroll
@@ -811,7 +828,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
                         }
 #pragma unroll
                         for (int e = 0; e < E; ++e) {
-                            const float v = half_at(vs.vv, e);
+                            const float v = value_at<VB>(vs.vv, e);
 #pragma unroll
                             for (int hh = 0; hh < G; ++hh) o[e][hh] = fmaf(w[hh], v, o[e][hh]);
                         }
@@ -826,7 +843,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
                         for (int hh = 0; hh < G; ++hh) sk[hh] = 0.f;
 #pragma unroll
                         for (int e = 0; e < E; ++e) {
-                            const float v = half_at(ks.kv, e);
+                            const float v = value_at<VB>(ks.kv, e);
 #pragma unroll
                             for (int hh = 0; hh < G; ++hh) sk[hh] = fmaf(q[e][hh], v, sk[hh]);
                         }
@@ -896,14 +913,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
 // launchers
 // ---------------------------------------------------------------------------
 
-template <int G, int KS, bool PAGED>
-inline void launch_split_k(const SplitArgs &a, hipStream_t s)
+template <int G, int KS, bool PAGED, int VB>
+inline void launch_split_v(const SplitArgs &a, hipStream_t s)
 {
     const dim3 grid(a.W), block(kWave);
     if (a.k < KS)
-        hipLaunchKernelGGL((k_split<G, KS, PAGED, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_split<G, KS, PAGED, true, VB>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((k_split<G, KS, PAGED, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_split<G, KS, PAGED, false, VB>), grid, block, 0, s, a);
+}
+
+template <int G, int KS, bool PAGED>
+inline void launch_split_k(const SplitArgs &a, hipStream_t s)
+{
+    if (a.geom.vbytes == 1)
+        launch_split_v<G, KS, PAGED, 1>(a, s);
+    else
+        launch_split_v<G, KS, PAGED, 2>(a, s);
 }
 
 template <int G, bool PAGED>

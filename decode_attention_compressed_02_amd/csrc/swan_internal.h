@@ -56,6 +56,34 @@ __host__ __device__ inline uint16_t d2h(double x)
     return sign | (uint16_t)(base + (uint32_t)kept + up);
 }
 
+// E4M3 bits of an fp16 value, rounded once to nearest even and saturating
+// at +-448 (OCP E4M3: exponent bias 7, 3 fraction bits, subnormal spacing
+// 2^-9, largest finite 448, code S.1111.111 NaN, no infinities).  Integer
+// only: the fp16 significand is shifted to the E4M3 grid of its exponent.
+__host__ __device__ inline uint8_t h2e4m3(uint16_t h)
+{
+    const uint32_t sign = (h >> 8) & 0x80u, mag = h & 0x7fffu;
+    if (mag > 0x7c00u) return (uint8_t)(sign | 0x7fu); // NaN
+    const uint32_t E = mag >> 10, M = mag & 0x3ffu;
+    if (E >= 9) { // at least 2^-6: normal E4M3 (or beyond its range)
+        uint32_t e = E - 8, sig = 1024u + M;            // 1.M with 10 fraction bits
+        uint32_t kept = sig >> 7, rest = sig & 127u;    // keep 1 + 3 bits
+        kept += (rest > 64u || (rest == 64u && (kept & 1u))) ? 1u : 0u;
+        if (kept == 16u) { // carried into the next binade
+            kept = 8u;
+            ++e;
+        }
+        if (e > 15u || (e == 15u && kept == 15u)) return (uint8_t)(sign | 0x7eu); // past 448: saturate
+        return (uint8_t)(sign | (e << 3) | (kept - 8u));
+    }
+    // below 2^-6: multiples of 2^-9, i.e. of 2^15 units of 2^-24
+    const uint32_t v24 = E ? ((1024u + M) << (E - 1)) : M;
+    uint32_t kept = v24 >> 15;
+    const uint32_t rest = v24 & 0x7fffu;
+    kept += (rest > 0x4000u || (rest == 0x4000u && (kept & 1u))) ? 1u : 0u; // 8 -> 2^-6, the smallest normal
+    return (uint8_t)(sign | kept);
+}
+
 // Where the sparse rows of one (sequence, kv head) live.
 struct SparseGeom {
     int H;          // kv heads
@@ -64,6 +92,7 @@ struct SparseGeom {
     int bs;         // paged: rows per block (0 = contiguous)
     int max_blocks; // paged: block-table width
     int num_blocks; // paged: blocks in the pool
+    int vbytes;     // bytes per stored value: 2 (fp16) or 1 (fp8 E4M3)
     const int32_t *bt;
 };
 
@@ -93,12 +122,19 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (lane == 0) ?
 // Magnitude top-k of one 128-vector held by a full wave, two fp16 per lane
 // (coordinate lane in `lo`, coordinate lane + 64 in `hi`).  Coordinates are
 // ranked by (fp16 magnitude bits descending, index ascending); the k first
-// are written to the row with ascending indices, values copied bit for bit,
-// and entries k..ks-1 are zero padding.  Integer-only, so the selection is
-// exact.  Must be called by all 64 lanes.
+// are written to the row with ascending indices, values copied bit for bit
+// (vbytes 2) or rounded to E4M3 (vbytes 1; the selection is still on the
+// fp16 magnitudes), and entries k..ks-1 are zero padding.  Integer-only, so
+// the selection is exact.  Must be called by all 64 lanes.
 __device__ __forceinline__ void wave_prune_row(int lane, uint16_t lo, uint16_t hi, int k, int ks, uint8_t *idx_row,
-                                               uint16_t *val_row)
+                                               uint8_t *val_row, int vbytes)
 {
+    auto put = [&](int o, uint16_t v) {
+        if (vbytes == 1)
+            val_row[o] = h2e4m3(v);
+        else
+            ((uint16_t *)val_row)[o] = v;
+    };
     const uint32_t mlo = lo & 0x7fffu, mhi = hi & 0x7fffu;
     int rank_lo = 0, rank_hi = 0;
 #pragma unroll 8
@@ -118,16 +154,16 @@ __device__ __forceinline__ void wave_prune_row(int lane, uint16_t lo, uint16_t h
     if (keep_lo) {
         const int o = __popcll(blo & lt);
         idx_row[o] = (uint8_t)lane;
-        val_row[o] = lo;
+        put(o, lo);
     }
     if (keep_hi) {
         const int o = __popcll(blo) + __popcll(bhi & lt);
         idx_row[o] = (uint8_t)(lane + 64);
-        val_row[o] = hi;
+        put(o, hi);
     }
     if (lane < ks - k) {
         idx_row[k + lane] = 0;
-        val_row[k + lane] = 0;
+        put(k + lane, 0);
     }
 }
 
@@ -148,7 +184,8 @@ struct AppendArgs {
     int B, H, R, k;
     SparseGeom geom;
     uint8_t *kidx, *vidx;
-    uint16_t *kval, *vval, *kbuf, *vbuf;
+    uint8_t *kval, *vval; // value planes, geom.vbytes bytes per entry
+    uint16_t *kbuf, *vbuf;
     const int32_t *pos;
     const uint16_t *k_hat;
     const float *v_hat;
@@ -166,11 +203,12 @@ __device__ inline void append_token(const AppendArgs &a, int b, int h, int wave,
     if (p < 0) return;
     const int64_t u = (int64_t)b * a.H + h;
     uint8_t *idx = wave == 0 ? a.kidx : a.vidx;
-    uint16_t *val = wave == 0 ? a.kval : a.vval;
+    uint8_t *val = wave == 0 ? a.kval : a.vval;
+    const int vb = a.geom.vbytes;
     const int row_cap = a.geom.bs > 0 ? a.geom.max_blocks * a.geom.bs : a.geom.n_cap;
     if (a.R == 0) {
         const int64_t off = p < row_cap ? row_offset_rt(a.geom, b, h, p) : -1;
-        if (off >= 0) wave_prune_row(lane, lo, hi, a.k, a.geom.ks, idx + off, val + off);
+        if (off >= 0) wave_prune_row(lane, lo, hi, a.k, a.geom.ks, idx + off, val + off * vb, vb);
         return;
     }
     uint16_t *buf = (wave == 0 ? a.kbuf : a.vbuf) + (u * a.R + p % a.R) * kD;
@@ -178,7 +216,7 @@ __device__ inline void append_token(const AppendArgs &a, int b, int h, int wave,
         const uint16_t olo = buf[lane], ohi = buf[lane + 64];
         const int r = p - a.R;
         const int64_t off = r < row_cap ? row_offset_rt(a.geom, b, h, r) : -1;
-        if (off >= 0) wave_prune_row(lane, olo, ohi, a.k, a.geom.ks, idx + off, val + off);
+        if (off >= 0) wave_prune_row(lane, olo, ohi, a.k, a.geom.ks, idx + off, val + off * vb, vb);
     }
     buf[lane] = lo;
     buf[lane + 64] = hi;
@@ -289,7 +327,8 @@ struct SplitArgs {
     const int32_t *pos;
     const float *q_hat;
     const uint8_t *kidx, *vidx;
-    const uint16_t *kval, *vval, *kbuf, *vbuf;
+    const uint8_t *kval, *vval; // value planes, geom.vbytes bytes per entry
+    const uint16_t *kbuf, *vbuf;
     float *part_o;  // [W + B H][g][128]
     float *part_ml; // [W + B H][g][2]
 };
@@ -313,7 +352,8 @@ struct PrefillArgs {
     int max_len;
     SparseGeom geom;
     uint8_t *kidx, *vidx;
-    uint16_t *kval, *vval, *kbuf, *vbuf;
+    uint8_t *kval, *vval; // value planes, geom.vbytes bytes per entry
+    uint16_t *kbuf, *vbuf;
     const int32_t *len;
     const float *k_raw, *v_hat, *P;
     float base;
@@ -322,9 +362,10 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 
 struct CopyBlocksArgs {
     int count, num_blocks;
-    int64_t block_bytes_idx; // bytes of one block of an index plane (value planes: twice)
+    int64_t block_bytes_idx; // bytes of one block of an index plane (value planes: vbytes times)
+    int vbytes;
     uint8_t *kidx, *vidx;
-    uint16_t *kval, *vval;
+    uint8_t *kval, *vval;
     const int32_t *src, *dst;
 };
 hipError_t launch_copy_blocks(const CopyBlocksArgs &a, hipStream_t s);

@@ -62,6 +62,7 @@ class Workload:
     block_size: int = 0  # 0: contiguous sparse rows; >0: paged blocks of this many rows
     shared_prefix: int = 0  # tokens whose K/V are identical across all sequences
     pool_slack: int = 0  # extra free blocks in the paged pool
+    value_format: int = 0  # sparse values: 0 fp16, 1 fp8 E4M3 (storage only; the inputs are the same)
 
     @property
     def g(self) -> int:

@@ -50,10 +50,10 @@
  * contribute nothing to scores or outputs.
  *   contiguous (block_size == 0):
  *     k_idx, v_idx  uint8   [B][H_kv][n_cap][k_stride]
- *     k_val, v_val  fp16    [B][H_kv][n_cap][k_stride]
+ *     k_val, v_val  fp16 or fp8 (value_format) [B][H_kv][n_cap][k_stride]
  *   paged (block_size > 0, "Reuse, Evict, or Limit Earlier Context" 1.2):
  *     k_idx, v_idx  uint8   [num_blocks][H_kv][block_size][k_stride]
- *     k_val, v_val  fp16    [num_blocks][H_kv][block_size][k_stride]
+ *     k_val, v_val  fp16 or fp8 [num_blocks][H_kv][block_size][k_stride]
  *     block_table   int32   [B][max_blocks]: sparse row t of sequence b is
  *                   slot t % block_size of block block_table[b][t / block_size]
  *   dense buffer:
@@ -94,14 +94,25 @@ typedef struct swan_dims {
     int32_t max_blocks;   /* paged: block-table entries per sequence               */
     int32_t num_blocks;   /* paged: blocks in the pool                             */
     int32_t split_tokens; /* decode: work rows per wave (multiple of 64), 0 = auto */
+    int32_t value_format; /* sparse values: SWAN_VALUES_FP16 (0) or SWAN_VALUES_FP8_E4M3 */
 } swan_dims;
+
+/* Storage of the values of sparse rows (the dense buffer is always fp16).
+ * FP8_E4M3 is the 8-bit float storage the SWAN page's memory section allows
+ * (2k + 2 bytes a vector) in the OCP E4M3 encoding (exponent bias 7, 3
+ * fraction bits, largest finite value 448, no infinities), with no scale:
+ * a pruned row keeps the same coordinates as with fp16 values (chosen on the
+ * fp16 magnitudes) and each kept value is rounded from fp16 to nearest even,
+ * saturating at +-448. */
+#define SWAN_VALUES_FP16 0
+#define SWAN_VALUES_FP8_E4M3 1
 
 /* Caller-owned cache planes (host struct holding device pointers). */
 typedef struct swan_cache {
     uint8_t *k_idx;
-    uint16_t *k_val;
+    void *k_val; /* fp16 or fp8 E4M3 entries (dims->value_format) */
     uint8_t *v_idx;
-    uint16_t *v_val;
+    void *v_val;
     uint16_t *k_buf;
     uint16_t *v_buf;
     const int32_t *block_table; /* paged layout only; NULL when contiguous */

@@ -20,7 +20,32 @@ def rel_l2_max(got, want):
 def dims_for(oc, split_tokens=0, block_size=0, max_blocks=0, num_blocks=0):
     return S.make_dims(oc.B, oc.N_h, oc.H_kv, oc.R, oc.k, n_cap=oc.ncap if block_size == 0 else 0,
                        block_size=block_size, max_blocks=max_blocks, num_blocks=num_blocks,
-                       split_tokens=split_tokens)
+                       split_tokens=split_tokens, value_format=oc.value_format)
+
+
+def value_storage(v, value_format):
+    """Stored form of oracle values (float64, exact in the format): fp16, or
+    E4M3 bytes (torch's float8_e4m3fn conversion is exact on E4M3 values)."""
+    if value_format == S.SWAN_VALUES_FP8_E4M3:
+        t = torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.float8_e4m3fn)
+        return t.view(torch.uint8).numpy()
+    return np.asarray(v).astype(np.float16)
+
+
+def assert_values_bits(stored, oracle_vals, value_format):
+    """Stored values equal, bit for bit (sign of zero included), to the
+    oracle's values in the same format."""
+    want = value_storage(oracle_vals, value_format)
+    view = np.uint8 if value_format == S.SWAN_VALUES_FP8_E4M3 else np.uint16
+    np.testing.assert_array_equal(np.ascontiguousarray(stored).view(view), np.ascontiguousarray(want).view(view))
+
+
+def value_f64(stored, value_format):
+    """Stored values (fp16, or E4M3 bytes) as float64."""
+    if value_format == S.SWAN_VALUES_FP8_E4M3:
+        t = torch.from_numpy(np.ascontiguousarray(stored, np.uint8)).view(torch.float8_e4m3fn)
+        return t.to(torch.float64).numpy()
+    return np.asarray(stored).astype(np.float64)
 
 
 def upload(cache: HybridCache, oc, block_table: np.ndarray | None = None, rows=None):
@@ -30,7 +55,7 @@ def upload(cache: HybridCache, oc, block_table: np.ndarray | None = None, rows=N
     overwrite the longer one's rows."""
     d, ks, k = cache.dims, cache.k_stride, oc.k
     planes = cache.sparse_views()
-    src = (oc.kidx, oc.kval.astype(np.float16), oc.vidx, oc.vval.astype(np.float16))
+    src = (oc.kidx, value_storage(oc.kval, d.value_format), oc.vidx, value_storage(oc.vval, d.value_format))
     for dst, s in zip(planes, src):
         host = np.zeros(tuple(dst.shape), dtype=s.dtype)
         if d.block_size == 0:

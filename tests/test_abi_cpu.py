@@ -43,6 +43,9 @@ def test_row_stride_and_sizes():
     assert n_buf == 16 * 8 * 256 * 128 * 2
     dp = S.make_dims(32, 32, 8, 64, 64, block_size=16, max_blocks=1024, num_blocks=20000)
     assert S.swan_cache_bytes(dp)[0] == 20000 * 8 * 16 * 64
+    # 8-bit values: one byte per value entry, the dense buffer stays fp16
+    d8 = S.make_dims(16, 32, 8, 256, 32, n_cap=32528, value_format=S.SWAN_VALUES_FP8_E4M3)
+    assert S.swan_cache_bytes(d8) == (n_idx, n_idx, n_buf)
 
 
 def test_split_plan():
@@ -193,6 +196,8 @@ cases = [
     ("R < 0", proj(dims(R=-1)), E),
     ("B = 0", proj(dims(B=0)), E),
     ("split_tokens not /64", dec(dims(split_tokens=100)), E),
+    ("value format 2", proj(dims(value_format=2)), U),
+    ("value format -1", dec(dims(value_format=-1)), U),
     ("null q", proj(dims(), q=N), E),
     ("null k_hat out", proj(dims(), kh=N), E),
     ("rope base 1", proj(dims(), base=1.0), E),

@@ -12,7 +12,7 @@ from decode_attention_compressed_02_amd import swan as S
 from decode_attention_compressed_02_amd import workloads as wl
 from decode_attention_compressed_02_amd.cache import PagedSwanDecoder, shared_prefix_pool
 
-from gpu_helpers import download_rows, rel_l2_max, upload
+from gpu_helpers import assert_values_bits, download_rows, rel_l2_max, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -31,9 +31,10 @@ def cuda(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def test_copy_blocks_moves_whole_blocks():
+@pytest.mark.parametrize("vf", [0, 1])
+def test_copy_blocks_moves_whole_blocks(vf):
     B, N, H, bs, k, nb = 2, 4, 2, 16, 32, 12
-    dims = S.make_dims(B, N, H, 16, k, block_size=bs, max_blocks=4, num_blocks=nb)
+    dims = S.make_dims(B, N, H, 16, k, block_size=bs, max_blocks=4, num_blocks=nb, value_format=vf)
     from decode_attention_compressed_02_amd.cache import HybridCache
     bt = torch.zeros((B, 4), dtype=torch.int32, device="cuda")
     cache = HybridCache(dims, "cuda", bt)
@@ -65,14 +66,14 @@ def build_pool(w, prefix_blocks, slack=8):
                               lambda n: wl.pool_order(w, n), slack)
 
 
-@pytest.mark.parametrize("k", [64, 40])
-def test_paged_pool_steps_with_copy_on_write(k):
+@pytest.mark.parametrize("k,vf", [(64, 0), (40, 0), (64, 1)])
+def test_paged_pool_steps_with_copy_on_write(k, vf):
     # prefix 96 tokens = 6 blocks of 16 rows; R = 16.  Sequence 1 (83 rows)
     # and 2 (95 rows) append into the shared block 5 (copy-on-write), 3 opens
     # block 6, 5 crosses into block 7 at its second step.
     ctx = (300, 100, 112, 113, 250, 128)
     w = wl.Workload("paged cow", len(ctx), 8, 2, 16, k, ctx, steps=3, seed=55, block_size=16,
-                    shared_prefix=96)
+                    shared_prefix=96, value_format=vf)
     P = wl.projection_qk(w)
     oc = oracle.OracleCache.for_workload(w, ncap=max(w.history_len(b) for b in range(w.B)) + w.steps)
     T = [w.history_len(b) for b in range(w.B)]
@@ -89,7 +90,7 @@ def test_paged_pool_steps_with_copy_on_write(k):
     pool = build_pool(w, prefix_blocks=6)
     assert (pool.ref[pool.table[0, :6]] == w.B).all()
     dims = S.make_dims(w.B, w.N_h, w.H_kv, w.R, w.k, block_size=16, max_blocks=pool.max_blocks,
-                       num_blocks=pool.num_blocks)
+                       num_blocks=pool.num_blocks, value_format=vf)
     dec = PagedSwanDecoder(dims, cuda(P), pool, w.rope_base)
     upload(dec.cache, oc, pool.table, rows=[T[b] - w.R for b in range(w.B)])
     copies = []
@@ -113,7 +114,7 @@ def test_paged_pool_steps_with_copy_on_write(k):
             r = int(pos[b]) - w.R
             np.testing.assert_array_equal(rows[0][b, :, r, :k], oc.kidx[b, :, r])
             np.testing.assert_array_equal(rows[2][b, :, r, :k], oc.vidx[b, :, r])
-            np.testing.assert_array_equal(rows[3][b, :, r, :k].astype(np.float64), oc.vval[b, :, r])
+            assert_values_bits(rows[3][b, :, r, :k], oc.vval[b, :, r], vf)
     # copy-on-write happened exactly for sequences 1 and 2 at their first step
     assert copies == [2, 0, 0]
     assert (pool.ref[pool.table[0, :5]] == w.B).all() and pool.ref[pool.table[0, 5]] == w.B - 2

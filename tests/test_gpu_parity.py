@@ -12,7 +12,7 @@ from decode_attention_compressed_02_amd import swan as S
 from decode_attention_compressed_02_amd import workloads as wl
 from decode_attention_compressed_02_amd.cache import SwanDecoder
 
-from gpu_helpers import download_rows, make_decoder, rel_l2_max, upload
+from gpu_helpers import assert_values_bits, download_rows, make_decoder, rel_l2_max, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -121,16 +121,20 @@ def tie_values(r, shape):
 @pytest.mark.parametrize("k", [1, 5, 32, 64, 100, 128])
 @pytest.mark.parametrize("R", [0, 1, 16])
 @pytest.mark.parametrize("paged", [False, True])
-def test_append_evict_bit_exact(k, R, paged):
-    r = rng(1000 + k * 7 + R * 3 + paged)
+@pytest.mark.parametrize("vf", [0, 1])
+def test_append_evict_bit_exact(k, R, paged, vf):
+    r = rng(1000 + k * 7 + R * 3 + paged + 17 * vf)
     B, N, H = 3, 4, 2
     T = [40, 9, 0]  # tokens already cached per sequence
     ncap = 48
     w = wl.Workload("app", B, N, H, R, k, tuple(t + 1 for t in T), seed=11 + k + R)
-    oc = oracle.OracleCache(B, N, H, D, R, k, ncap)
+    oc = oracle.OracleCache(B, N, H, D, R, k, ncap, value_format=vf)
     K = r.standard_normal((B, H, max(T), D)).astype(np.float32)
     V = r.standard_normal((B, H, max(T), D)).astype(np.float32)
     V[:, :, ::3] = tie_values(r, V[:, :, ::3].shape)
+    if vf:  # E4M3: reach the subnormal range, midpoints and saturation
+        V[:, :, 1::3] *= np.float32(2.0 ** -8)
+        V[:, :, 2::5] *= np.float32(600.0)
     P = wl.projection_qk(w)
     oc.prefill(K, V, np.array(T, np.int64), P.astype(np.float64))
     bt = None
@@ -159,11 +163,11 @@ def test_append_evict_bit_exact(k, R, paged):
         gi, gv, hi, hv = (x[b, :, :n] for x in rows)
         np.testing.assert_array_equal(gi[..., :k], oc.kidx[b, :, :n])
         np.testing.assert_array_equal(hi[..., :k], oc.vidx[b, :, :n])
-        np.testing.assert_array_equal(gv[..., :k].view(np.uint16), oc.kval[b, :, :n].astype(np.float16).view(np.uint16))
-        np.testing.assert_array_equal(hv[..., :k].view(np.uint16), oc.vval[b, :, :n].astype(np.float16).view(np.uint16))
+        assert_values_bits(gv[..., :k], oc.kval[b, :, :n], vf)
+        assert_values_bits(hv[..., :k], oc.vval[b, :, :n], vf)
         if ks > k:  # padding is index 0, value +0
-            assert not gi[..., k:].any() and not gv[..., k:].view(np.uint16).any()
-            assert not hi[..., k:].any() and not hv[..., k:].view(np.uint16).any()
+            assert not gi[..., k:].any() and not gv[..., k:].view(np.uint8).any()
+            assert not hi[..., k:].any() and not hv[..., k:].view(np.uint8).any()
     if R > 0:
         kb, vb = (x.cpu().numpy() for x in dec.cache.buffer_views())
         rk, rv = oc.ring_f16()
@@ -234,6 +238,12 @@ DECODE_CASES = {
     "k100": (2, 4, 2, 24, 100, (400, 30), 0, {}),
     "all_dense": (2, 8, 2, 256, 32, (200, 256), 0, {}),
     "drift": (1, 8, 2, 64, 32, (3000,), 0, dict(drift_amp=0.5)),
+    # 8-bit values (E4M3): the same streams with one byte per value
+    "fp8_g4_k32": (3, 8, 2, 64, 32, (1500, 800, 70), 0, dict(value_format=1)),
+    "fp8_g4_k64_saturating": (2, 8, 2, 128, 64, (1700, 1301), 0,
+                              dict(outlier_channels=4, outlier_scale=200.0, value_format=1)),
+    "fp8_g8_k16": (2, 16, 2, 16, 16, (500, 300), 128, dict(value_format=1)),
+    "fp8_g1_k128_R0": (2, 1, 1, 0, 128, (300, 129), 64, dict(value_format=1)),
 }
 
 
@@ -292,12 +302,12 @@ def test_decode_inactive_and_ragged():
 # whole steps chained on the GPU vs oracle steps
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cfg", ["config1_full", "config3_small"])
+@pytest.mark.parametrize("cfg", ["config1_full", "config3_small", "config3_small_fp8"])
 def test_step_chain(cfg):
     if cfg == "config1_full":
         w = wl.config(1)
     else:
-        w = wl.config(3).scaled(B=2, ctx=(700, 531), R=16, steps=5)
+        w = wl.config(3).scaled(B=2, ctx=(700, 531), R=16, steps=5, value_format=int(cfg.endswith("fp8")))
     oc, *_ = oracle_state(w)
     P = wl.projection_qk(w)
     dec = make_decoder(oc, P)
@@ -317,16 +327,17 @@ def test_step_chain(cfg):
             r = int(pos[b]) - w.R
             if r >= 0:
                 np.testing.assert_array_equal(rows[0][b, :, r, :w.k], oc.kidx[b, :, r])
-                np.testing.assert_array_equal(rows[3][b, :, r, :w.k].astype(np.float64), oc.vval[b, :, r])
+                assert_values_bits(rows[3][b, :, r, :w.k], oc.vval[b, :, r], w.value_format)
 
 
 # ---------------------------------------------------------------------------
 # prefill -> hybrid cache
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("R,k", [(128, 32), (0, 64), (300, 16)])
-def test_prefill_convert(R, k):
-    w = wl.Workload("pre", 3, 8, 2, R, k, (1200, 77, 301), seed=21 + R, outlier_channels=4, outlier_scale=8.0)
+@pytest.mark.parametrize("R,k,vf", [(128, 32, 0), (0, 64, 0), (300, 16, 0), (128, 32, 1), (0, 64, 1)])
+def test_prefill_convert(R, k, vf):
+    w = wl.Workload("pre", 3, 8, 2, R, k, (1200, 77, 301), seed=21 + R, outlier_channels=4, outlier_scale=8.0,
+                    value_format=vf)
     oc, K, V, Ts = oracle_state(w)
     P = wl.projection_qk(w)
     dec = make_decoder(oc, P)
@@ -337,10 +348,10 @@ def test_prefill_convert(R, k):
         n = max(0, int(Ts[b]) - R)
         # values: fp32 -> fp16 on both sides, then integer top-k: bit exact
         np.testing.assert_array_equal(rows[2][b, :, :n, :k], oc.vidx[b, :, :n])
-        np.testing.assert_array_equal(rows[3][b, :, :n, :k].astype(np.float64), oc.vval[b, :, :n])
+        assert_values_bits(rows[3][b, :, :n, :k], oc.vval[b, :, :n], vf)
         # keys: double products rounded once to fp16 on both sides
         np.testing.assert_array_equal(rows[0][b, :, :n, :k], oc.kidx[b, :, :n])
-        np.testing.assert_array_equal(rows[1][b, :, :n, :k].astype(np.float64), oc.kval[b, :, :n])
+        assert_values_bits(rows[1][b, :, :n, :k], oc.kval[b, :, :n], vf)
     if R > 0:
         kb, vb = (x.cpu().numpy().astype(np.float64) for x in dec.cache.buffer_views())
         for b in range(w.B):
