@@ -58,15 +58,16 @@ def _declare(L):
     L.so_rope.argtypes = [_i, _pd, _d, _d, _pd]
     L.so_project.argtypes = [_i, _pd, _d, _d, _pd, _pd]
     L.so_prune.argtypes = [_i, _i, _pd, _pu8, _pd]
-    L.so_attend.argtypes = [_i, _i, _pd, _l, _i, _pu8, _pd, _pu8, _pd, _l, _pd, _pd, _pd, _pd]
-    L.so_prefill.argtypes = [_i, _i, _i, _i, _i, _l, _l, _pl, _pd, _pd, _pd, _d,
+    L.so_attend.argtypes = [_i, _i, _pd, _l, _i, _pu8, _pd, _i, _pu8, _pd, _l, _pd, _pd, _pd, _pd]
+    L.so_prefill.argtypes = [_i, _i, _i, _i, _i, _i, _l, _l, _pl, _pd, _pd, _pd, _d,
                              _pu8, _pd, _pu8, _pd, _pd, _pd, _i, _i]
     L.so_prefill.restype = _i
     L.so_project_batch.argtypes = [_i, _i, _i, _i, _pd, _pd, _pl, _pd, _d, _pd, _pd]
-    L.so_append_batch.argtypes = [_i, _i, _i, _i, _i, _l, _pl, _pd, _pd, _pu8, _pd, _pu8, _pd, _pd, _pd, _i]
+    L.so_append_batch.argtypes = [_i, _i, _i, _i, _i, _i, _l, _pl, _pd, _pd, _pu8, _pd, _pu8, _pd, _pd, _pd, _i]
     L.so_append_batch.restype = _i
-    L.so_decode_batch.argtypes = [_i, _i, _i, _i, _i, _i, _l, _pl, _pd, _pu8, _pd, _pu8, _pd, _pd, _pd, _pd, _i]
-    L.so_step.argtypes = [_i, _i, _i, _i, _i, _i, _l, _pl, _pd, _pd, _pd, _pd, _d,
+    L.so_decode_batch.argtypes = [_i, _i, _i, _i, _i, _i, _i, _l, _pl, _pd, _pu8, _pd, _pu8, _pd, _pd, _pd, _pd,
+                                  _i]
+    L.so_step.argtypes = [_i, _i, _i, _i, _i, _i, _i, _l, _pl, _pd, _pd, _pd, _pd, _d,
                           _pu8, _pd, _pu8, _pd, _pd, _pd, _pd, _pd, _pd, _i, _i]
     L.so_step.restype = _i
     return L
@@ -123,24 +124,25 @@ def prune(x, k: int):
 
 
 def attend(qhat, kidx, kval, vidx, vval, kd, vd) -> np.ndarray:
-    """Hybrid attention of one unit: qhat [g][d]; sparse rows kidx/kval/vidx/
-    vval [n][k] (n may be 0); dense rows kd/vd [nd][d] (nd may be 0).
-    Returns out [g][d] (float64)."""
+    """Hybrid attention of one unit: qhat [g][d]; sparse key rows kidx/kval
+    [n][k] and value rows vidx/vval [n][kv] (n may be 0); dense rows kd/vd
+    [nd][d] (nd may be 0).  Returns out [g][d] (float64)."""
     qhat = _f64(np.atleast_2d(qhat))
     g, d = qhat.shape
     kval, vval = _f64(kval), _f64(vval)
     n, k = kval.shape
+    kv = vval.shape[1]
     kd, vd = _f64(kd).reshape(-1, d), _f64(vd).reshape(-1, d)
     nd = kd.shape[0]
     # the C side never reads past n / nd rows; pad empty arrays to one row
     pad = lambda a, cols, dt: a if a.shape[0] else np.zeros((1, cols), dt)
     kidx = pad(np.ascontiguousarray(kidx, np.uint8).reshape(n, k), k, np.uint8)
-    vidx = pad(np.ascontiguousarray(vidx, np.uint8).reshape(n, k), k, np.uint8)
-    kval, vval = pad(kval, k, np.float64), pad(vval, k, np.float64)
+    vidx = pad(np.ascontiguousarray(vidx, np.uint8).reshape(n, kv), kv, np.uint8)
+    kval, vval = pad(kval, k, np.float64), pad(vval, kv, np.float64)
     kd, vd = pad(kd, d, np.float64), pad(vd, d, np.float64)
     out = np.zeros((g, d))
     scratch = np.zeros(n + nd + 1)
-    lib().so_attend(d, g, qhat, n, k, kidx, kval, vidx, vval, nd, kd, vd, out, scratch)
+    lib().so_attend(d, g, qhat, n, k, kidx, kval, kv, vidx, vval, nd, kd, vd, out, scratch)
     return out
 
 
@@ -150,23 +152,26 @@ def attend(qhat, kidx, kval, vidx, vval, kd, vd) -> np.ndarray:
 
 class OracleCache:
     """The hybrid cache of a batch in logical layout (float64, binary16-exact
-    values; with value_format 1 the sparse values are E4M3-exact): sparse rows
-    [B][H][ncap][k] and dense buffer [B][H][R][d]."""
+    values; with value_format 1 the sparse values are E4M3-exact): key rows
+    [B][H][ncap][k], value rows [B][H][ncap][k_v] (k_v = k unless given) and
+    dense buffer [B][H][R][d]."""
 
-    def __init__(self, B: int, N_h: int, H_kv: int, d: int, R: int, k: int, ncap: int, value_format: int = 0):
+    def __init__(self, B: int, N_h: int, H_kv: int, d: int, R: int, k: int, ncap: int, value_format: int = 0,
+                 k_v: int | None = None):
         self.B, self.N_h, self.H_kv, self.d, self.R, self.k, self.ncap = B, N_h, H_kv, d, R, k, ncap
+        self.k_v = int(k_v) if k_v else k
         self.value_format = int(value_format)
         self.kidx = np.zeros((B, H_kv, ncap, k), np.uint8)
-        self.vidx = np.zeros_like(self.kidx)
+        self.vidx = np.zeros((B, H_kv, ncap, self.k_v), np.uint8)
         self.kval = np.zeros((B, H_kv, ncap, k))
-        self.vval = np.zeros_like(self.kval)
+        self.vval = np.zeros((B, H_kv, ncap, self.k_v))
         self.ringk = np.zeros((B, H_kv, max(R, 1), d))
         self.ringv = np.zeros_like(self.ringk)
 
     @classmethod
     def for_workload(cls, w, ncap: int | None = None):
         return cls(w.B, w.N_h, w.H_kv, w.d_h, w.R, w.k, w.n_cap() if ncap is None else ncap,
-                   getattr(w, "value_format", 0))
+                   getattr(w, "value_format", 0), getattr(w, "k_v", 0) or None)
 
     def _state(self):
         return (self.kidx, self.kval, self.vidx, self.vval, self.ringk, self.ringv)
@@ -175,7 +180,7 @@ class OracleCache:
         """Kraw, Vraw [B][H][Tmax][d]; T[b] prefilled tokens (positions 0..T-1)."""
         Kraw, Vraw = _f64(Kraw), _f64(Vraw)
         T = np.ascontiguousarray(T, np.int64)
-        err = lib().so_prefill(self.B, self.H_kv, self.d, self.R, self.k, self.ncap, Kraw.shape[2], T,
+        err = lib().so_prefill(self.B, self.H_kv, self.d, self.R, self.k, self.k_v, self.ncap, Kraw.shape[2], T,
                                Kraw, Vraw, _f64(P), float(base), *self._state(),
                                nthreads or default_threads(), self.value_format)
         if err:
@@ -189,7 +194,7 @@ class OracleCache:
         return qhat, khat
 
     def append(self, khat, vhat, pos):
-        err = lib().so_append_batch(self.B, self.H_kv, self.d, self.R, self.k, self.ncap,
+        err = lib().so_append_batch(self.B, self.H_kv, self.d, self.R, self.k, self.k_v, self.ncap,
                                     np.ascontiguousarray(pos, np.int64), _f64(khat), _f64(vhat), *self._state(),
                                     self.value_format)
         if err:
@@ -197,7 +202,7 @@ class OracleCache:
 
     def decode(self, qhat, pos, nthreads: int | None = None):
         out = np.zeros((self.B, self.N_h, self.d))
-        lib().so_decode_batch(self.B, self.N_h, self.H_kv, self.d, self.R, self.k, self.ncap,
+        lib().so_decode_batch(self.B, self.N_h, self.H_kv, self.d, self.R, self.k, self.k_v, self.ncap,
                               np.ascontiguousarray(pos, np.int64), _f64(qhat), *self._state(), out,
                               nthreads or default_threads())
         return out
@@ -207,7 +212,7 @@ class OracleCache:
         qhat = np.zeros((self.B, self.N_h, self.d))
         khat = np.zeros((self.B, self.H_kv, self.d))
         out = np.zeros((self.B, self.N_h, self.d))
-        err = lib().so_step(self.B, self.N_h, self.H_kv, self.d, self.R, self.k, self.ncap,
+        err = lib().so_step(self.B, self.N_h, self.H_kv, self.d, self.R, self.k, self.k_v, self.ncap,
                             np.ascontiguousarray(pos, np.int64), _f64(q), _f64(kraw), _f64(vnew), _f64(P),
                             float(base), *self._state(), qhat, khat, out, nthreads or default_threads(),
                             self.value_format)

@@ -198,11 +198,13 @@ void so_prune(int d, int k, const double *x, uint8_t *idx, double *val)
  *   score of dense token t  = (q . kd_t) / sqrt(d)
  *   a = softmax over all n + nd scores together
  *   out = sum_t a_t v_t, sparse v_t scattered to its stored indices.
- * Sparse rows hold exactly k entries each (row t at t*k).  scratch must hold
- * n + nd doubles.  out is in the rotated value basis. */
+ * Sparse key rows hold exactly k entries each (row t at t*k), value rows kv
+ * entries (row t at t*kv; kv = k unless keys and values keep different
+ * counts, the key/value ablation of [SWAN] Appendix A.5, Table 2).  scratch
+ * must hold n + nd doubles.  out is in the rotated value basis. */
 void so_attend(int d, int g, const double *qhat,
                long n, int k, const uint8_t *kidx, const double *kval,
-               const uint8_t *vidx, const double *vval,
+               int kv, const uint8_t *vidx, const double *vval,
                long nd, const double *kd, const double *vd,
                double *out, double *scratch)
 {
@@ -235,8 +237,8 @@ void so_attend(int d, int g, const double *qhat,
             o[c] = 0.0;
         for (long t = 0; t < n; ++t) {
             double a = scratch[t] / sum;
-            for (int i = 0; i < k; ++i)
-                o[vidx[(size_t)t * k + i]] += a * vval[(size_t)t * k + i];
+            for (int i = 0; i < kv; ++i)
+                o[vidx[(size_t)t * kv + i]] += a * vval[(size_t)t * kv + i];
         }
         for (long t = 0; t < nd; ++t) {
             double a = scratch[n + t] / sum;
@@ -248,8 +250,9 @@ void so_attend(int d, int g, const double *qhat,
 
 /* ------------------------------------------------------------------------ */
 /* Batched state operations.  Logical layout, all row-major:                 */
-/*   kidx, vidx  uint8  [B][H][ncap][k]     sparse rows, row t = token t     */
-/*   kval, vval  double [B][H][ncap][k]     binary16-exact values            */
+/*   kidx, kval  uint8, double [B][H][ncap][k]   key rows, row t = token t  */
+/*   vidx, vval  uint8, double [B][H][ncap][kv]  value rows (kv = k unless    */
+/*               keys and values keep different counts)                      */
 /*   ringk,ringv double [B][H][R][d]        dense buffer, slot = pos mod R   */
 /* ([PAGE3] section 3.2: circular buffer, slot = t mod W)                    */
 /* ------------------------------------------------------------------------ */
@@ -270,7 +273,7 @@ static void so_prune_store(int d, int k, int vfmt, const double *x, uint8_t *idx
             val[i] = so_round_e4m3(val[i]);
 }
 
-static void so_append_unit(int d, int R, int k, long ncap, long pos,
+static void so_append_unit(int d, int R, int k, int kv, long ncap, long pos,
                            const double *khat, const double *vhat,
                            uint8_t *kidx, double *kval, uint8_t *vidx, double *vval,
                            double *ringk, double *ringv, int vfmt, int *err)
@@ -279,7 +282,7 @@ static void so_append_unit(int d, int R, int k, long ncap, long pos,
     if (R == 0) {
         if (pos >= ncap) { *err = 1; return; }
         so_prune_store(d, k, vfmt, khat, kidx + (size_t)pos * k, kval + (size_t)pos * k);
-        so_prune_store(d, k, vfmt, vhat, vidx + (size_t)pos * k, vval + (size_t)pos * k);
+        so_prune_store(d, kv, vfmt, vhat, vidx + (size_t)pos * kv, vval + (size_t)pos * kv);
         return;
     }
     long slot = pos % R;
@@ -287,7 +290,7 @@ static void so_append_unit(int d, int R, int k, long ncap, long pos,
         long row = pos - R;  /* the evicted token's position = its sparse row */
         if (row >= ncap) { *err = 1; return; }
         so_prune_store(d, k, vfmt, ringk + (size_t)slot * d, kidx + (size_t)row * k, kval + (size_t)row * k);
-        so_prune_store(d, k, vfmt, ringv + (size_t)slot * d, vidx + (size_t)row * k, vval + (size_t)row * k);
+        so_prune_store(d, kv, vfmt, ringv + (size_t)slot * d, vidx + (size_t)row * kv, vval + (size_t)row * kv);
     }
     memcpy(ringk + (size_t)slot * d, khat, sizeof(double) * d);
     memcpy(ringv + (size_t)slot * d, vhat, sizeof(double) * d);
@@ -298,7 +301,7 @@ static void so_append_unit(int d, int R, int k, long ncap, long pos,
  * their own position and P_QK, keys and values are rounded to binary16, and
  * the tokens are appended in order.  Returns nonzero if a sequence needs
  * more than ncap sparse rows. */
-int so_prefill(int B, int H, int d, int R, int k, long ncap, long Tmax, const long *T,
+int so_prefill(int B, int H, int d, int R, int k, int kv, long ncap, long Tmax, const long *T,
                const double *Kraw, const double *Vraw, const double *P, double base,
                uint8_t *kidx, double *kval, uint8_t *vidx, double *vval,
                double *ringk, double *ringv, int nthreads, int vfmt)
@@ -317,9 +320,9 @@ int so_prefill(int B, int H, int d, int R, int k, long ncap, long Tmax, const lo
                     kh[c] = so_round_f16(kh[c]);
                     vh[c] = so_round_f16(vr[c]);
                 }
-                so_append_unit(d, R, k, ncap, t, kh, vh,
+                so_append_unit(d, R, k, kv, ncap, t, kh, vh,
                                kidx + unit_off(b, h, H, (size_t)ncap * k), kval + unit_off(b, h, H, (size_t)ncap * k),
-                               vidx + unit_off(b, h, H, (size_t)ncap * k), vval + unit_off(b, h, H, (size_t)ncap * k),
+                               vidx + unit_off(b, h, H, (size_t)ncap * kv), vval + unit_off(b, h, H, (size_t)ncap * kv),
                                ringk + unit_off(b, h, H, (size_t)R * d), ringv + unit_off(b, h, H, (size_t)R * d),
                                vfmt, &err);
             }
@@ -343,7 +346,7 @@ void so_project_batch(int B, int N, int H, int d, const double *q, const double 
 }
 
 /* Append only: round khat/vhat [B][H][d] to binary16 and append at pos[b]. */
-int so_append_batch(int B, int H, int d, int R, int k, long ncap, const long *pos,
+int so_append_batch(int B, int H, int d, int R, int k, int kv, long ncap, const long *pos,
                     const double *khat, const double *vhat,
                     uint8_t *kidx, double *kval, uint8_t *vidx, double *vval,
                     double *ringk, double *ringv, int vfmt)
@@ -356,9 +359,9 @@ int so_append_batch(int B, int H, int d, int R, int k, long ncap, const long *po
                 kh[c] = so_round_f16(khat[((size_t)b * H + h) * d + c]);
                 vh[c] = so_round_f16(vhat[((size_t)b * H + h) * d + c]);
             }
-            so_append_unit(d, R, k, ncap, pos[b], kh, vh,
+            so_append_unit(d, R, k, kv, ncap, pos[b], kh, vh,
                            kidx + unit_off(b, h, H, (size_t)ncap * k), kval + unit_off(b, h, H, (size_t)ncap * k),
-                           vidx + unit_off(b, h, H, (size_t)ncap * k), vval + unit_off(b, h, H, (size_t)ncap * k),
+                           vidx + unit_off(b, h, H, (size_t)ncap * kv), vval + unit_off(b, h, H, (size_t)ncap * kv),
                            ringk + unit_off(b, h, H, (size_t)R * d), ringv + unit_off(b, h, H, (size_t)R * d), vfmt,
                            &err);
         }
@@ -368,7 +371,7 @@ int so_append_batch(int B, int H, int d, int R, int k, long ncap, const long *po
 /* Attention only, for every unit, with the cache state as it stands after
  * the token at pos[b] was appended: n = max(0, pos+1-R) sparse rows and
  * min(pos+1, R) buffered tokens.  qhat [B][N][d] -> out [B][N][d]. */
-void so_decode_batch(int B, int N, int H, int d, int R, int k, long ncap, const long *pos,
+void so_decode_batch(int B, int N, int H, int d, int R, int k, int kv, long ncap, const long *pos,
                      const double *qhat,
                      const uint8_t *kidx, const double *kval, const uint8_t *vidx, const double *vval,
                      const double *ringk, const double *ringv, double *out, int nthreads)
@@ -385,7 +388,8 @@ void so_decode_batch(int B, int N, int H, int d, int R, int k, long ncap, const 
             so_attend(d, g, qhat + ((size_t)b * N + (size_t)h * g) * d,
                       n, k,
                       kidx + unit_off(b, h, H, (size_t)ncap * k), kval + unit_off(b, h, H, (size_t)ncap * k),
-                      vidx + unit_off(b, h, H, (size_t)ncap * k), vval + unit_off(b, h, H, (size_t)ncap * k),
+                      kv,
+                      vidx + unit_off(b, h, H, (size_t)ncap * kv), vval + unit_off(b, h, H, (size_t)ncap * kv),
                       nd, ringk + unit_off(b, h, H, (size_t)R * d), ringv + unit_off(b, h, H, (size_t)R * d),
                       out + ((size_t)b * N + (size_t)h * g) * d, scratch);
             free(scratch);
@@ -396,15 +400,15 @@ void so_decode_batch(int B, int N, int H, int d, int R, int k, long ncap, const 
  * query and key, append the rounded key and value (evicting and pruning the
  * oldest buffered token), then attend.  Outputs qhat (double, unrounded),
  * khat (binary16-rounded) and out.  Returns nonzero on sparse overflow. */
-int so_step(int B, int N, int H, int d, int R, int k, long ncap, const long *pos,
+int so_step(int B, int N, int H, int d, int R, int k, int kv, long ncap, const long *pos,
             const double *q, const double *kraw, const double *vnew, const double *P, double base,
             uint8_t *kidx, double *kval, uint8_t *vidx, double *vval, double *ringk, double *ringv,
             double *qhat, double *khat, double *out, int nthreads, int vfmt)
 {
     so_project_batch(B, N, H, d, q, kraw, pos, P, base, qhat, khat);
-    int err = so_append_batch(B, H, d, R, k, ncap, pos, khat, vnew, kidx, kval, vidx, vval, ringk, ringv, vfmt);
+    int err = so_append_batch(B, H, d, R, k, kv, ncap, pos, khat, vnew, kidx, kval, vidx, vval, ringk, ringv, vfmt);
     for (size_t i = 0; i < (size_t)B * H * d; ++i)
         khat[i] = so_round_f16(khat[i]);
-    so_decode_batch(B, N, H, d, R, k, ncap, pos, qhat, kidx, kval, vidx, vval, ringk, ringv, out, nthreads);
+    so_decode_batch(B, N, H, d, R, k, kv, ncap, pos, qhat, kidx, kval, vidx, vval, ringk, ringv, out, nthreads);
     return err;
 }

@@ -19,8 +19,10 @@ MUTANTS = {
     "prune_signed": ("keys[c].mag = fabs(x[c]);", "keys[c].mag = x[c];"),
     "scale_k": ("double scale = 1.0 / sqrt((double)d);", "double scale = 1.0 / sqrt((double)k);"),
     "dense_half": ("scratch[n + t] = s * scale;", "scratch[n + t] = s * scale * 0.5;"),
-    "v_uses_k_index": ("o[vidx[(size_t)t * k + i]] += a * vval[(size_t)t * k + i];",
-                       "o[kidx[(size_t)t * k + i]] += a * vval[(size_t)t * k + i];"),
+    "v_uses_k_index": ("o[vidx[(size_t)t * kv + i]] += a * vval[(size_t)t * kv + i];",
+                       "o[kidx[(size_t)t * kv + i]] += a * vval[(size_t)t * kv + i];"),
+    "v_pruned_with_key_count": ("so_prune_store(d, kv, vfmt, ringv + (size_t)slot * d",
+                                "so_prune_store(d, k, vfmt, ringv + (size_t)slot * d"),
     "evict_row": ("long row = pos - R;", "long row = pos - R + 1;"),
     "ring_slot": ("long slot = pos % R;", "long slot = (pos + 1) % R;"),
     "round_ties_away": ("double r = nearbyint(ax / ulp) * ulp;", "double r = round(ax / ulp) * ulp;"),

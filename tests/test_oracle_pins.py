@@ -434,3 +434,58 @@ def test_fp8_rows_keep_the_fp16_selection():
     np.testing.assert_array_equal(oracle.round_e4m3(a.vval), b8.vval)
     np.testing.assert_array_equal(a.ringk, b8.ringk)  # the dense buffer stays fp16
     assert np.abs(b8.vval).max() == 448.0
+
+
+# ---------------------------------------------------------------------------
+# keys and values keeping different counts (SWAN Appendix A.5, Table 2: the
+# key/value retention ablation, TopK_R + TopV_R = 1)
+# ---------------------------------------------------------------------------
+
+def test_asymmetric_rows_are_the_symmetric_rows_of_each_count():
+    """With k keys and k_v values kept, the key rows are those of a cache that
+    keeps k of both and the value rows those of one that keeps k_v of both."""
+    r = np.random.default_rng(31)
+    B, N, H, R, ncap, T = 2, 4, 2, 4, 24, [20, 13]
+    K = r.standard_normal((B, H, 20, D))
+    V = r.standard_normal((B, H, 20, D))
+    P = np.stack([np.linalg.qr(r.standard_normal((D, D)))[0] for _ in range(H)])
+    for k, kv in ((77, 51), (51, 77), (8, 120)):
+        a = oracle.OracleCache(B, N, H, D, R, k, ncap, k_v=kv)
+        ks = oracle.OracleCache(B, N, H, D, R, k, ncap)
+        vs = oracle.OracleCache(B, N, H, D, R, kv, ncap)
+        for c in (a, ks, vs):
+            c.prefill(K, V, np.array(T, np.int64), P)
+        np.testing.assert_array_equal(a.kidx, ks.kidx)
+        np.testing.assert_array_equal(a.kval, ks.kval)
+        np.testing.assert_array_equal(a.vidx, vs.vidx)
+        np.testing.assert_array_equal(a.vval, vs.vval)
+
+
+def test_asymmetric_decode_equals_densified_attention():
+    """Brute force: densify the pruned key rows (k entries) and value rows
+    (k_v entries) into 128-vectors and run textbook softmax attention."""
+    r = np.random.default_rng(32)
+    B, N, H, R, ncap = 1, 2, 1, 3, 12
+    k, kv = 40, 90
+    oc = oracle.OracleCache(B, N, H, D, R, k, ncap, k_v=kv)
+    K = r.standard_normal((B, H, 11, D))
+    V = r.standard_normal((B, H, 11, D))
+    oc.prefill(K, V, np.array([11], np.int64), np.eye(D)[None])
+    q = r.standard_normal((B, N, D))
+    pos = np.array([10], np.int64)  # attend to the 11 prefilled tokens: 8 sparse + 3 buffered
+    out = oc.decode(q, pos)
+    n = 11 - R
+    Kd = np.zeros((n, D))
+    Vd = np.zeros((n, D))
+    for t in range(n):
+        Kd[t, oc.kidx[0, 0, t]] = oc.kval[0, 0, t]
+        Vd[t, oc.vidx[0, 0, t]] = oc.vval[0, 0, t]
+    slots = [(t % R) for t in range(n, 11)]
+    Kall = np.concatenate([Kd, oc.ringk[0, 0, slots]])
+    Vall = np.concatenate([Vd, oc.ringv[0, 0, slots]])
+    for h in range(N):
+        s = Kall @ q[0, h] / np.sqrt(D)
+        a = np.exp(s - s.max())
+        a /= a.sum()
+        np.testing.assert_allclose(out[0, h], a @ Vall, rtol=1e-12, atol=1e-14)
+    assert (oc.kidx[0, 0, :n] != 0).sum(axis=1).min() >= k - 1 and oc.vidx.shape[-1] == kv
