@@ -82,6 +82,9 @@ def main():
     ap.add_argument("--split-tokens", type=int, default=0, help="work rows per wave (0 = automatic)")
     ap.add_argument("--values", choices=("fp16", "fp8"), default="fp16",
                     help="storage of the sparse values (fp8: E4M3, one byte each)")
+    ap.add_argument("--kv-share", type=float, default=0.0,
+                    help="keys keep this share of the workload's k + k coordinates and values the rest "
+                         "(e.g. 0.6: TopK_R 0.6 / TopV_R 0.4 of the same budget); 0 = equal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle stepping time of the sample")
@@ -107,6 +110,9 @@ def main():
     w = wl.config(args.config)
     if args.values == "fp8":
         w = w.scaled(value_format=1)
+    if args.kv_share > 0:
+        kk = int(round(2 * w.k * args.kv_share))
+        w = w.scaled(k=kk, k_v=2 * w.k - kk)
     vbytes = 1 if w.value_format else 2
     if args.steps > w.steps:
         w = w.scaled(steps=args.steps)
@@ -200,9 +206,9 @@ def main():
         pos = inputs[s][3].cpu().numpy()
         n = [max(0, int(p) + 1 - w.R) for p in pos]
         f = [min(int(p) + 1, w.R) for p in pos]
-        split_bytes.append(acc.split_kernel_bytes(n, w.H_kv, w.N_h, f, w.k, value_bytes=vbytes))
-        dec_bytes.append(acc.decode_bytes(n, w.H_kv, w.N_h, f, w.k, value_bytes=vbytes))
-        flops.append(acc.decode_flops(n, w.H_kv, w.N_h, f, w.k))
+        split_bytes.append(acc.split_kernel_bytes(n, w.H_kv, w.N_h, f, w.k, value_bytes=vbytes, k_v=w.k_v))
+        dec_bytes.append(acc.decode_bytes(n, w.H_kv, w.N_h, f, w.k, value_bytes=vbytes, k_v=w.k_v))
+        flops.append(acc.decode_flops(n, w.H_kv, w.N_h, f, w.k, k_v=w.k_v))
     split_avg_ms = float(np.mean(split_ms))
     # bytes of the last step's launch over the back-to-back duration
     achieved = float(split_bytes[-1]) / (split_b2b_ms * 1e-3) / 1e9
@@ -213,7 +219,7 @@ def main():
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if (tr.get("kernel_source_sha") == kernel_source_hash() and tr.get("workload") == w.name
-                and tr.get("value_format", 0) == w.value_format):
+                and tr.get("value_format", 0) == w.value_format and not w.k_v):
             traffic = tr.get("hbm_bytes_per_launch")
 
     if args.copy_calibration_mib > 0:
@@ -238,9 +244,10 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded N(0,1) raw keys/queries, stored-basis values, random orthogonal P_QK)",
-        "config": {"workload": f"config {args.config}: {w.name}" + (", fp8 values" if w.value_format else ""),
+        "config": {"workload": f"config {args.config}: {w.name}" + (", fp8 values" if w.value_format else "")
+                   + (f", k_K {w.k} / k_V {w.k_v}" if w.k_v else ""),
                    "B": w.B, "N_h": w.N_h, "H_kv": w.H_kv,
-                   "d_h": w.d_h, "ctx_first_step": int(w.ctx[0]), "R": w.R, "k": w.k,
+                   "d_h": w.d_h, "ctx_first_step": int(w.ctx[0]), "R": w.R, "k": w.k, "k_v": w.k_v or w.k,
                    "storage": f"{'fp8 E4M3' if w.value_format else 'fp16'} values, uint8 indices, fp16 dense buffer",
                    "split_waves": nsplit,
                    "split_tokens": dec.dims.split_tokens or "auto"},

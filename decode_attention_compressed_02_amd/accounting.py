@@ -66,31 +66,31 @@ def break_even_length(b: int, k: int, d_h: int = 128) -> float:
 # ---------------------------------------------------------------------------
 
 def split_kernel_bytes(n_per_seq, H_kv: int, N_h: int, R_fill_per_seq, k: int, d_h: int = 128,
-                       value_bytes: int = 2) -> int:
+                       value_bytes: int = 2, k_v: int = 0) -> int:
     """Algorithmic HBM bytes of one launch of the split (streaming) kernel:
-    every sparse row read once (K and V: k one-byte indices and k values of
-    value_bytes each -- 6k bytes per token per kv-head with fp16 values, 4k
-    with fp8), every buffered token read once (K and V fp16, 4 d_h bytes),
-    and the fp32 rotated queries read once.  Partials (a few percent) are
-    not counted."""
-    sparse = sum(int(n) for n in n_per_seq) * H_kv * 2 * k * (1 + value_bytes)
+    every sparse row read once (k key and k_v value entries, k_v = k unless
+    given, each a one-byte index and a value of value_bytes -- 6k bytes per
+    token per kv-head with fp16 values, 4k with fp8), every buffered token
+    read once (K and V fp16, 4 d_h bytes), and the fp32 rotated queries read
+    once.  Partials (a few percent) are not counted."""
+    sparse = sum(int(n) for n in n_per_seq) * H_kv * (k + (k_v or k)) * (1 + value_bytes)
     dense = sum(int(r) for r in R_fill_per_seq) * H_kv * 4 * d_h
     q_in = len(list(n_per_seq)) * N_h * d_h * 4
     return sparse + dense + q_in
 
 
 def decode_bytes(n_per_seq, H_kv: int, N_h: int, R_fill_per_seq, k: int, d_h: int = 128,
-                 value_bytes: int = 2) -> int:
+                 value_bytes: int = 2, k_v: int = 0) -> int:
     """Algorithmic bytes of the whole decode (split + reduce): the split
     kernel's bytes plus the fp32 outputs written once."""
     B = len(list(n_per_seq))
-    return split_kernel_bytes(n_per_seq, H_kv, N_h, R_fill_per_seq, k, d_h, value_bytes) + B * N_h * d_h * 4
+    return split_kernel_bytes(n_per_seq, H_kv, N_h, R_fill_per_seq, k, d_h, value_bytes, k_v) + B * N_h * d_h * 4
 
 
-def decode_flops(n_per_seq, H_kv: int, N_h: int, R_fill_per_seq, k: int, d_h: int = 128) -> float:
+def decode_flops(n_per_seq, H_kv: int, N_h: int, R_fill_per_seq, k: int, d_h: int = 128, k_v: int = 0) -> float:
     """Multiply-add FLOPs (2 per MAC) of scores and outputs over all heads."""
     g = N_h // H_kv
     tot = 0.0
     for n, r in zip(n_per_seq, R_fill_per_seq):
-        tot += H_kv * g * (4.0 * n * k + 4.0 * r * d_h)
+        tot += H_kv * g * (2.0 * n * (k + (k_v or k)) + 4.0 * r * d_h)
     return tot

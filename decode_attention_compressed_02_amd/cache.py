@@ -16,12 +16,12 @@ class HybridCache:
 
     def __init__(self, dims: S.swan_dims, device="cuda", block_table: torch.Tensor | None = None):
         self.dims = dims
-        n_idx, n_val, n_buf = S.swan_cache_bytes(dims)
+        n_kidx, n_kval, n_vidx, n_vval, n_buf = S.swan_cache_bytes(dims)
         z = lambda n, dt: torch.zeros(max(n, 1), dtype=dt, device=device)
-        self.k_idx, self.v_idx = z(n_idx, torch.uint8), z(n_idx, torch.uint8)
+        self.k_idx, self.v_idx = z(n_kidx, torch.uint8), z(n_vidx, torch.uint8)
         # sparse values: fp16, or E4M3 bytes (held as uint8: torch has no arithmetic on them here)
         vdt, vb = (torch.uint8, 1) if dims.value_format == S.SWAN_VALUES_FP8_E4M3 else (torch.float16, 2)
-        self.k_val, self.v_val = z(n_val // vb, vdt), z(n_val // vb, vdt)
+        self.k_val, self.v_val = z(n_kval // vb, vdt), z(n_vval // vb, vdt)
         self.k_buf, self.v_buf = z(n_buf // 2, torch.float16), z(n_buf // 2, torch.float16)
         self.block_table = None
         if dims.block_size > 0:
@@ -33,6 +33,10 @@ class HybridCache:
     @property
     def k_stride(self) -> int:
         return S.swan_row_stride(self.dims.k)
+
+    @property
+    def v_stride(self) -> int:
+        return S.swan_row_stride(self.dims.k_v or self.dims.k)
 
     def set_block_table(self, bt: torch.Tensor):
         d = self.dims
@@ -48,17 +52,20 @@ class HybridCache:
                                         p(self.k_buf), p(self.v_buf), p(self.block_table))
         return self._struct
 
-    # shaped views (contiguous layout) for inspection
+    # shaped views for inspection: (k_idx, k_val, v_idx, v_val), rows of the
+    # key and the value stride
     def sparse_views(self):
-        d, ks = self.dims, self.k_stride
-        if d.block_size > 0:
-            shp = (d.num_blocks, d.H_kv, d.block_size, ks)
-        else:
-            shp = (d.B, d.H_kv, d.n_cap, ks)
-        n = 1
-        for s in shp:
-            n *= s
-        return tuple(t[:n].view(shp) for t in (self.k_idx, self.k_val, self.v_idx, self.v_val))
+        d = self.dims
+        lead = (d.num_blocks, d.H_kv, d.block_size) if d.block_size > 0 else (d.B, d.H_kv, d.n_cap)
+        out = []
+        for t, ks in ((self.k_idx, self.k_stride), (self.k_val, self.k_stride), (self.v_idx, self.v_stride),
+                      (self.v_val, self.v_stride)):
+            shp = lead + (ks,)
+            n = 1
+            for x in shp:
+                n *= x
+            out.append(t[:n].view(shp))
+        return tuple(out)
 
     def buffer_views(self):
         d = self.dims

@@ -55,10 +55,23 @@ swan_status check_dims(const swan_dims *d)
         return fail(SWAN_ERR_INVALID_ARG, "split_tokens = %d must be 0 or a positive multiple of 64", d->split_tokens);
     if (d->value_format != SWAN_VALUES_FP16 && d->value_format != SWAN_VALUES_FP8_E4M3)
         return fail(SWAN_ERR_UNSUPPORTED, "value_format = %d, supported: 0 (fp16), 1 (fp8 E4M3)", d->value_format);
+    if (d->k_v < 0 || d->k_v > d->d_h) return fail(SWAN_ERR_INVALID_ARG, "k_v = %d outside 0..%d", d->k_v, d->d_h);
+    if (d->k_v > 0) {
+        const int ks = row_stride(d->k), ksv = row_stride(d->k_v);
+        if (ksv != ks && ksv != 2 * ks && 2 * ksv != ks)
+            return fail(SWAN_ERR_UNSUPPORTED, "k = %d and k_v = %d: stored row widths %d and %d, supported when equal "
+                                              "or one twice the other", d->k, d->k_v, ks, ksv);
+    }
     return SWAN_OK;
 }
 
 int value_bytes(const swan_dims *d) { return d->value_format == SWAN_VALUES_FP8_E4M3 ? 1 : 2; }
+// kept value coordinates (k unless keys and values keep different counts)
+int kept_v(const swan_dims *d) { return d->k_v > 0 ? d->k_v : d->k; }
+int row_bytes(const swan_dims *d)
+{
+    return swan::sparse_row_bytes(row_stride(d->k), row_stride(kept_v(d)), value_bytes(d));
+}
 
 int64_t row_cap(const swan_dims *d)
 {
@@ -79,6 +92,7 @@ swan::SparseGeom geom(const swan_dims *d, const swan_cache *c)
     swan::SparseGeom g;
     g.H = d->H_kv;
     g.ks = row_stride(d->k);
+    g.ks_v = row_stride(kept_v(d));
     g.n_cap = d->n_cap;
     g.bs = d->block_size;
     g.max_blocks = d->max_blocks;
@@ -102,11 +116,11 @@ struct Plan {
 // the rows per wave instead.
 Plan plan(const swan_dims *d, int32_t max_pos)
 {
-    const int g = d->N_h / d->H_kv, ks = row_stride(d->k);
-    const int64_t total_max = (int64_t)d->B * d->H_kv * swan::unit_work(max_pos, d->R, row_cap(d), ks).len;
+    const int g = d->N_h / d->H_kv, ks = row_stride(d->k), ksv = row_stride(kept_v(d));
+    const int64_t total_max = (int64_t)d->B * d->H_kv * swan::unit_work(max_pos, d->R, row_cap(d), row_bytes(d)).len;
     int slots = INT32_MAX;
     if (d->split_tokens == 0) {
-        slots = swan::kCUs * swan::split_waves_per_cu(g, ks);
+        slots = swan::kCUs * swan::split_waves_per_cu(g, ks > ksv ? ks : ksv);
     }
     Plan p;
     p.W = (int)swan::active_waves(total_max, slots, d->split_tokens);
@@ -166,17 +180,19 @@ const char *swan_last_error(void) { return g_err; }
 
 int32_t swan_row_stride(int32_t k) { return row_stride(k); }
 
-swan_status swan_cache_bytes(const swan_dims *d, size_t out[3])
+swan_status swan_cache_bytes(const swan_dims *d, size_t out[5])
 {
     swan_status st = check_dims(d);
     if (st) return st;
     if (!out) return fail(SWAN_ERR_INVALID_ARG, "out is NULL");
-    const size_t ks = (size_t)row_stride(d->k);
+    const size_t ks = (size_t)row_stride(d->k), ksv = (size_t)row_stride(kept_v(d));
     const size_t rows = d->block_size > 0 ? (size_t)d->num_blocks * d->H_kv * d->block_size
                                           : (size_t)d->B * d->H_kv * d->n_cap;
     out[0] = rows * ks;
     out[1] = rows * ks * (size_t)value_bytes(d);
-    out[2] = (size_t)d->B * d->H_kv * d->R * swan::kD * 2;
+    out[2] = rows * ksv;
+    out[3] = rows * ksv * (size_t)value_bytes(d);
+    out[4] = (size_t)d->B * d->H_kv * d->R * swan::kD * 2;
     return SWAN_OK;
 }
 
@@ -207,6 +223,7 @@ swan_status swan_append_evict(const swan_dims *d, const swan_cache *c, const int
     a.H = d->H_kv;
     a.R = d->R;
     a.k = d->k;
+    a.k_v = kept_v(d);
     a.geom = geom(d, c);
     a.kidx = c->k_idx;
     a.vidx = c->v_idx;
@@ -239,6 +256,7 @@ swan_status swan_project_append(const swan_dims *d, const swan_cache *c, const f
     a.H = d->H_kv;
     a.R = d->R;
     a.k = d->k;
+    a.k_v = kept_v(d);
     a.geom = geom(d, c);
     a.kidx = c->k_idx;
     a.vidx = c->v_idx;
@@ -275,6 +293,7 @@ static swan::SplitArgs split_args(const swan_dims *d, const swan_cache *c, const
     a.W = p.W;
     a.split_tokens = d->split_tokens;
     a.k = d->k;
+    a.k_v = kept_v(d);
     a.row_cap = (int)row_cap(d);
     a.geom = geom(d, c);
     a.pos = pos;
@@ -316,7 +335,7 @@ swan_status swan_decode_reduce(const swan_dims *d, const int32_t *pos, int32_t m
     r.R = d->R;
     r.W = p.W;
     r.split_tokens = d->split_tokens;
-    r.ks = row_stride(d->k);
+    r.row_bytes = row_bytes(d);
     r.row_cap = (int)row_cap(d);
     r.pos = pos;
     r.part_o = (const float *)ws;
@@ -357,6 +376,7 @@ swan_status swan_prefill_convert(const swan_dims *d, const swan_cache *c, const 
     a.H = d->H_kv;
     a.R = d->R;
     a.k = d->k;
+    a.k_v = kept_v(d);
     a.T_stride = T_stride;
     a.max_len = max_len;
     a.geom = geom(d, c);
@@ -385,13 +405,15 @@ swan_status swan_copy_blocks(const swan_dims *d, const swan_cache *c, const int3
     if (count == 0) return SWAN_OK;
     if (!src || !dst) return fail(SWAN_ERR_INVALID_ARG, "NULL block id array");
     if (count > 65535) return fail(SWAN_ERR_INVALID_ARG, "count = %d > 65535", count);
-    if (((int64_t)d->H_kv * d->block_size * row_stride(d->k)) % 16)
+    if (((int64_t)d->H_kv * d->block_size * row_stride(d->k)) % 16 ||
+        ((int64_t)d->H_kv * d->block_size * row_stride(kept_v(d))) % 16)
         return fail(SWAN_ERR_UNSUPPORTED, "a block of an index plane (H_kv * block_size * k_stride bytes) must be a "
                                           "multiple of 16 bytes");
     swan::CopyBlocksArgs a;
     a.count = count;
     a.num_blocks = d->num_blocks;
-    a.block_bytes_idx = (int64_t)d->H_kv * d->block_size * row_stride(d->k);
+    a.block_bytes_kidx = (int64_t)d->H_kv * d->block_size * row_stride(d->k);
+    a.block_bytes_vidx = (int64_t)d->H_kv * d->block_size * row_stride(kept_v(d));
     a.vbytes = value_bytes(d);
     a.kidx = c->k_idx;
     a.vidx = c->v_idx;

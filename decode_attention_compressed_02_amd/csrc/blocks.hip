@@ -20,7 +20,8 @@ __global__ __launch_bounds__(256) void k_copy_blocks(CopyBlocksArgs a)
     // ids outside the pool are a caller error: the pair is skipped
     if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks || src == dst) return;
     uint8_t *base = plane == 0 ? a.kidx : plane == 1 ? a.vidx : plane == 2 ? a.kval : a.vval;
-    const int64_t bytes = plane < 2 ? a.block_bytes_idx : a.vbytes * a.block_bytes_idx;
+    const int64_t idx_bytes = (plane & 1) ? a.block_bytes_vidx : a.block_bytes_kidx; // planes 0, 2 keys; 1, 3 values
+    const int64_t bytes = plane < 2 ? idx_bytes : a.vbytes * idx_bytes;
     const cpy_u32x4 *s = (const cpy_u32x4 *)(base + (int64_t)src * bytes);
     cpy_u32x4 *d = (cpy_u32x4 *)(base + (int64_t)dst * bytes);
     for (int64_t j = threadIdx.x; j < bytes / 16; j += 256) d[j] = s[j];

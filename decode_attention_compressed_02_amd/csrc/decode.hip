@@ -34,13 +34,13 @@ __global__ __launch_bounds__(128) void k_reduce(ReduceArgs a)
 
     int64_t tot = 0, before = 0;
     for (int bb = t; bb < a.B; bb += 128) {
-        const int64_t len = seq_work(a.pos, bb, a.R, a.row_cap, a.ks);
+        const int64_t len = seq_work(a.pos, bb, a.R, a.row_cap, a.row_bytes);
         tot += len;
         if (bb < b) before += len;
     }
     tot = block_sum128(tot, red);
     before = block_sum128(before, red);
-    const int64_t len = unit_work(a.pos[b], a.R, a.row_cap, a.ks).len;
+    const int64_t len = unit_work(a.pos[b], a.R, a.row_cap, a.row_bytes).len;
     if (len == 0) {
         *out = 0.f;
         return;

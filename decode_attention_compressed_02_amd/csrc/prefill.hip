@@ -79,10 +79,11 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a)
             const uint16_t lo = which ? vh[tt][lane] : kh[tt][lane];
             const uint16_t hi = which ? vh[tt][lane + 64] : kh[tt][lane + 64];
             if (t < T - a.R) {
-                const int64_t off = t < row_cap ? row_offset_rt(a.geom, b, h, t) : -1;
-                if (off >= 0)
-                    wave_prune_row(lane, lo, hi, a.k, a.geom.ks, (which ? a.vidx : a.kidx) + off,
-                                   (which ? a.vval : a.kval) + off * a.geom.vbytes, a.geom.vbytes);
+                const int64_t slot = t < row_cap ? row_slot_rt(a.geom, b, h, t) : -1;
+                const int kk = which ? a.k_v : a.k, ks = which ? a.geom.ks_v : a.geom.ks;
+                if (slot >= 0)
+                    wave_prune_row(lane, lo, hi, kk, ks, (which ? a.vidx : a.kidx) + slot * ks,
+                                   (which ? a.vval : a.kval) + slot * ks * a.geom.vbytes, a.geom.vbytes);
             } else {
                 uint16_t *buf = (which ? a.vbuf : a.kbuf) + (u * a.R + t % a.R) * kD;
                 buf[lane] = lo;

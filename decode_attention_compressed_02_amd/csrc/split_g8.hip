@@ -1,12 +1,13 @@
-// split_g8.hip -- the split-pass kernels for GQA groups of 8 query heads
-// (contiguous and paged rows, every stored row width).
+// split_g8.hip -- the split-pass kernels for GQA groups of 8 query heads,
+// contiguous rows, every pair of stored key and value row widths; paged rows
+// are instantiated in split_g8_paged.hip so the two compile in parallel.
 #include "split_kernel.h"
 
 namespace swan {
 
 hipError_t launch_split_g8(const SplitArgs &a, hipStream_t s)
 {
-    return a.geom.bs > 0 ? launch_split_g<8, true>(a, s) : launch_split_g<8, false>(a, s);
+    return a.geom.bs > 0 ? launch_split_g8_paged(a, s) : launch_split_g<8, false>(a, s);
 }
 
 } // namespace swan

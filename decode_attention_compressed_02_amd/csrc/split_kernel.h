@@ -202,9 +202,9 @@ __device__ __forceinline__ int64_t wave_scan(int64_t v)
 
 // work rows of the units of sequences [0, B) (per kv head), summed over the
 // lanes of a wave or a block's waves alike
-__device__ __forceinline__ int64_t seq_work(const int32_t *pos, int b, int R, int64_t row_cap, int ks)
+__device__ __forceinline__ int64_t seq_work(const int32_t *pos, int b, int R, int64_t row_cap, int row_bytes)
 {
-    return unit_work(pos[b], R, row_cap, ks).len;
+    return unit_work(pos[b], R, row_cap, row_bytes).len;
 }
 
 // G consecutive floats of LDS at p (16-byte aligned for G >= 4)
@@ -380,30 +380,34 @@ constexpr int kKeepLoadOrder = 0x1 | 0x2 | 0x4 | 0x8 | 0x80 | 0x100 | 0x200 | 0x
 // ---------------------------------------------------------------------------
 
 // Ring depth of the sparse stream: about SWAN_INFLIGHT_BYTES per lane in
-// flight (2 (1 + VB) E bytes per row slice of the four planes), between 2
+// flight (slice_bytes: a lane's slice of a row in the four planes), between 2
 // and 8 slots.
 #ifndef SWAN_INFLIGHT_BYTES
 #define SWAN_INFLIGHT_BYTES 192
 #endif
-__host__ __device__ constexpr int split_depth(int E, int VB)
+__host__ __device__ constexpr int split_depth(int slice_bytes)
 {
-    const int slice = 2 * (1 + VB) * E;
-    const int d = (SWAN_INFLIGHT_BYTES + slice - 1) / slice;
+    const int d = (SWAN_INFLIGHT_BYTES + slice_bytes - 1) / slice_bytes;
     return d < 2 ? 2 : (d > 8 ? 8 : d);
 }
 
-template <int G, int KS, bool PAGED, bool PAD, int VB>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS)))) void k_split(SplitArgs a)
+template <int G, int KS, int KSV, bool PAGED, bool PAD, int VB>
+__global__ __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV)))) void k_split(SplitArgs a)
 {
-    constexpr int E = split_entries(G, KS);
-    constexpr int LPT = KS / E;     // lanes per row
-    constexpr int TPI = kWave / LPT; // rows per iteration = accumulator copies
-    // fp8 values: the same bytes in flight in more slots, except where the
-    // register budget of two waves per SIMD has no room for them
-    constexpr int D = split_depth(E, split_waves_per_simd(G, KS) == 2 ? 2 : VB);
+    constexpr int KSM = KS > KSV ? KS : KSV;
+    constexpr int TPI = split_slots(G, KSM); // rows per iteration = accumulator copies
+    constexpr int LPT = kWave / TPI;         // lanes per row
+    constexpr int E = split_entries(G, KS, KSM), EV = split_entries(G, KSV, KSM); // key / value entries a lane
+    constexpr int kRowBytes = sparse_row_bytes(KS, KSV, VB);
+    // fp8 values and narrower planes: the same bytes in flight in more slots,
+    // except where the register budget of two waves per SIMD has no room for
+    // them (there the depth is that of fp16 rows of the wider width)
+    constexpr bool kTwoWaves = split_waves_per_simd(G, KSM) == 2;
+    constexpr int D = split_depth(kTwoWaves ? 3 * 2 * (E > EV ? E : EV) : (1 + VB) * (E + EV));
     constexpr int NACC = TPI * kD * G;
-    static_assert(LPT * E == KS && TPI * LPT == kWave, "bad split shape");
-    static_assert(split_lds_bytes(G, KS) == 4 * (kD * G + NACC), "host and device disagree on LDS size");
+    static_assert(LPT * E == KS && LPT * EV == KSV && E >= 1 && EV >= 1 && E <= 16 && EV <= 16, "bad split shape");
+    static_assert(split_lds_bytes(G, KSM) == 4 * (kD * G + NACC), "host and device disagree on LDS size");
     // g = 4 with 16 row slots keeps sparse scores transposed, one (row slot,
     // head) per lane; otherwise every lane of a row slot holds all g scores
     constexpr bool kT = (G == 4 && TPI == 16);
@@ -418,12 +422,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
     // sequence base + l; the first 64 sequences stay in registers for the
     // search below (one pass when B <= 64).
     const int32_t pos0 = lane < a.B ? a.pos[lane] : -1;
-    const int64_t len0 = lane < a.B ? unit_work(pos0, a.R, a.row_cap, KS).len * a.H : 0;
+    const int64_t len0 = lane < a.B ? unit_work(pos0, a.R, a.row_cap, kRowBytes).len * a.H : 0;
     const int64_t end0 = wave_scan(len0);
     int64_t total = lane_value(end0, kWave - 1);
     for (int base = kWave; base < a.B; base += kWave) {
         const int bb = base + lane;
-        total += lane_value(wave_scan(bb < a.B ? seq_work(a.pos, bb, a.R, a.row_cap, KS) * a.H : 0), kWave - 1);
+        total += lane_value(wave_scan(bb < a.B ? seq_work(a.pos, bb, a.R, a.row_cap, kRowBytes) * a.H : 0), kWave - 1);
     }
     const int64_t V = active_waves(total, a.W, a.split_tokens);
     if (w >= V) return;
@@ -442,7 +446,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
             int64_t run = lane_value(end0, kWave - 1);
             for (int base = kWave; base < a.B; base += kWave) {
                 const int bb = base + lane;
-                const int64_t len = bb < a.B ? seq_work(a.pos, bb, a.R, a.row_cap, KS) * a.H : 0;
+                const int64_t len = bb < a.B ? seq_work(a.pos, bb, a.R, a.row_cap, kRowBytes) * a.H : 0;
                 const int64_t end = run + wave_scan(len);
                 const uint64_t hit2 = __ballot(bb < a.B && end > x0);
                 if (hit2) {
@@ -457,7 +461,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
     }
     for (; b < a.B && P < x1; ++b) {
         const int32_t pb = b < kWave ? __builtin_amdgcn_readlane(pos0, b) : __builtin_amdgcn_readfirstlane(a.pos[b]);
-        const UnitWork uw = unit_work(pb, a.R, a.row_cap, KS);
+        const UnitWork uw = unit_work(pb, a.R, a.row_cap, kRowBytes);
         for (int h = (uw.len > 0 && x0 > P) ? (int)((x0 - P) / uw.len) : 0;
              uw.len > 0 && h < a.H && P + h * uw.len < x1; ++h) {
             // the piece [lo, hi) of unit (b, h): sparse rows [t0, t1) and buffered tokens [d0, d1)
@@ -582,34 +586,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
                 const uint8_t *kidx = a.kidx, *vidx = a.vidx;
                 const uint8_t *kval = a.kval, *vval = a.vval; // VB bytes per entry
                 if constexpr (!PAGED) { // per-unit base in scalar registers, 32-bit lane offsets
-                    const int64_t ub = ((int64_t)b * a.H + h) * a.geom.n_cap * KS;
-                    kidx += ub;
-                    vidx += ub;
-                    kval += ub * VB;
-                    vval += ub * VB;
+                    const int64_t ub = ((int64_t)b * a.H + h) * a.geom.n_cap; // the unit's first row slot
+                    kidx += ub * KS;
+                    vidx += ub * KSV;
+                    kval += ub * KS * VB;
+                    vval += ub * KSV * VB;
                 }
-                // entry offset of this lane's slice of row r0 + tl (rows past t1
-                // re-read the last row and are masked); paged rows whose block-table
-                // entry is not a block of the pool read block 0 and are dropped
+                // row slot of row r0 + tl (rows past t1 re-read the last row and
+                // are masked); paged rows whose block-table entry is not a block of
+                // the pool read block 0 and are dropped
                 auto slice = [&](int r0, bool &ok) -> uint32_t {
                     const int r = min(r0 + tl, t1 - 1);
                     if constexpr (PAGED) {
                         const int blk = a.geom.bt[(int64_t)b * a.geom.max_blocks + r / a.geom.bs];
                         ok = blk >= 0 && blk < a.geom.num_blocks;
                         const int bb = ok ? blk : 0;
-                        return (uint32_t)(((bb * a.H + h) * a.geom.bs + r % a.geom.bs) * KS + sub * E);
+                        return (uint32_t)((bb * a.H + h) * a.geom.bs + r % a.geom.bs);
                     } else {
                         ok = true;
-                        return (uint32_t)(r * KS + sub * E);
+                        return (uint32_t)r;
                     }
                 };
                 KSlot<E, VB> rk[D];
-                VSlot<E, VB> rv[D];
+                VSlot<EV, VB> rv[D];
                 // Contiguous rows: a buffer resource per plane covers rows r0 .. t1-1
                 // (scalar arithmetic); each lane reads its slice at a fixed offset and
                 // rows past t1 read zeros (masked by valid).  Paged rows go through the
                 // block table one row at a time.
-                const uint32_t lane_off = (uint32_t)(tl * KS + sub * E);
+                const uint32_t lane_off = (uint32_t)(tl * KS + sub * E);     // key planes
+                const uint32_t lane_off_v = (uint32_t)(tl * KSV + sub * EV); // value planes
                 // Paged pools whose blocks hold a multiple of TPI rows: the TPI rows
                 // of a ring slot start at a multiple of TPI (t0 and TPS are multiples
                 // of 64), so they lie in one block, whose id is wave-uniform and
@@ -617,9 +622,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
                 // buffer resource on that block like the contiguous layout.  Other
                 // block sizes look the block up per row.
                 const bool slot_blocks = PAGED && a.geom.bs % TPI == 0;
-                // Paged: first entry of the slot at r0 and the number of its rows to
-                // read; rows past t1 read nothing (zeros) and are masked by row, rows
-                // of a block outside the pool read nothing and clear ok.
+                // Paged: the row slot of the ring slot at r0 and the number of its rows
+                // to read; rows past t1 read nothing (zeros) and are masked by row,
+                // rows of a block outside the pool read nothing and clear ok.
                 auto slot_base = [&](int r0, uint32_t &rows, bool &ok) -> int64_t {
                     ok = true;
                     rows = 0;
@@ -630,7 +635,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
                         return 0;
                     }
                     rows = (uint32_t)min(t1 - r0, TPI);
-                    return (((int64_t)blk * a.H + h) * a.geom.bs + r0 % a.geom.bs) * KS;
+                    return ((int64_t)blk * a.H + h) * a.geom.bs + r0 % a.geom.bs;
                 };
                 // Ring slot d of the pass starting at row rp.  Contiguous rows: one
                 // buffer resource per plane and pass, covering rows rp .. t1-1 (the
@@ -639,12 +644,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
                 auto load_k = [&](int rp, int d, KSlot<E, VB> &st) {
                     const int r0 = rp + d * TPI;
                     if (PAGED && !slot_blocks) {
-                        const uint32_t o = slice(r0, st.ok);
+                        const int64_t o = (int64_t)slice(r0, st.ok) * KS + sub * E;
                         load_words<E>(kidx + o, st.ki);
-                        load_words<VB * E>(kval + (int64_t)o * VB, st.kv);
+                        load_words<VB * E>(kval + o * VB, st.kv);
                     } else if constexpr (PAGED) {
                         uint32_t rows;
-                        const int64_t base = slot_base(r0, rows, st.ok);
+                        const int64_t base = slot_base(r0, rows, st.ok) * KS;
                         buffer_words<E>(buffer_rsrc(kidx + base, rows * KS), lane_off, st.ki);
                         buffer_words<VB * E>(buffer_rsrc(kval + base * VB, rows * KS * VB), VB * lane_off, st.kv);
                     } else {
@@ -654,29 +659,31 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
                         buffer_words<VB * E>(buffer_rsrc(kval + (int64_t)rp * KS * VB, rows * KS * VB), VB * off, st.kv);
                     }
                 };
-                auto load_v = [&](int rp, int d, VSlot<E, VB> &st) {
+                auto load_v = [&](int rp, int d, VSlot<EV, VB> &st) {
                     const int r0 = rp + d * TPI;
                     if (PAGED && !slot_blocks) {
                         bool ok;
-                        const uint32_t o = slice(r0, ok);
-                        load_words<E>(vidx + o, st.vi);
-                        load_words<VB * E>(vval + (int64_t)o * VB, st.vv);
+                        const int64_t o = (int64_t)slice(r0, ok) * KSV + sub * EV;
+                        load_words<EV>(vidx + o, st.vi);
+                        load_words<VB * EV>(vval + o * VB, st.vv);
                     } else if constexpr (PAGED) {
                         uint32_t rows;
                         bool ok;
-                        const int64_t base = slot_base(r0, rows, ok);
-                        buffer_words<E>(buffer_rsrc(vidx + base, rows * KS), lane_off, st.vi);
-                        buffer_words<VB * E>(buffer_rsrc(vval + base * VB, rows * KS * VB), VB * lane_off, st.vv);
+                        const int64_t base = slot_base(r0, rows, ok) * KSV;
+                        buffer_words<EV>(buffer_rsrc(vidx + base, rows * KSV), lane_off_v, st.vi);
+                        buffer_words<VB * EV>(buffer_rsrc(vval + base * VB, rows * KSV * VB), VB * lane_off_v, st.vv);
                     } else {
-                        const uint32_t rows = (uint32_t)max(t1 - rp, 0), off = lane_off + d * TPI * KS;
-                        buffer_words<E>(buffer_rsrc(vidx + (int64_t)rp * KS, rows * KS), off, st.vi);
-                        buffer_words<VB * E>(buffer_rsrc(vval + (int64_t)rp * KS * VB, rows * KS * VB), VB * off, st.vv);
+                        const uint32_t rows = (uint32_t)max(t1 - rp, 0), off = lane_off_v + d * TPI * KSV;
+                        buffer_words<EV>(buffer_rsrc(vidx + (int64_t)rp * KSV, rows * KSV), off, st.vi);
+                        buffer_words<VB * EV>(buffer_rsrc(vval + (int64_t)rp * KSV * VB, rows * KSV * VB), VB * off,
+                                              st.vv);
                     }
                 };
-                // entries at row positions >= k are padding (index 0, value +0): they
-                // add nothing to a score, but their write-back could overwrite the
-                // update of a kept entry at index 0, so they are not written
-                const int kept = a.k - sub * E;
+                // value entries at row positions >= k_v are padding (index 0, value
+                // +0): they add nothing, but their write-back could overwrite the
+                // update of a kept entry at index 0, so they are not written (key
+                // padding only adds q[0] * 0 to a score)
+                const int kept = a.k_v - sub * EV;
 
                 // Software pipeline over passes of D * TPI rows: while the values of
                 // pass i are scattered, the scores of pass i + 1 are gathered, so the
@@ -799,18 +806,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
                         // both LDS batches in flight before any arithmetic: the value
                         // reads of pass rb and the key gathers of pass rb + P
                         const KSlot<E, VB> &ks = rk[d];
-                        const VSlot<E, VB> &vs = rv[d];
-                        float o[E][G], q[E][G];
-                        float *vaddr[E];
+                        const VSlot<EV, VB> &vs = rv[d];
+                        float o[EV][G], q[E][G];
+                        float *vaddr[EV];
 #pragma unroll
-                        for (int e = 0; e < E; ++e) {
+                        for (int e = 0; e < EV; ++e) {
                             if constexpr (TPI * G * 4 == 256) // 16 slots x 4 heads: one v_perm per address
                                 vaddr[e] = (float *)((char *)acc + acc_offset_256(vs.vi, e, (uint32_t)(tl * G * 4)));
                             else
                                 vaddr[e] = my_acc + byte_at(vs.vi, e) * (TPI * G);
                         }
 #pragma unroll
-                        for (int e = 0; e < E; ++e) lds_get<G>(vaddr[e], o[e]);
+                        for (int e = 0; e < EV; ++e) lds_get<G>(vaddr[e], o[e]);
 #pragma unroll
                         for (int e = 0; e < E; ++e) lds_get<G>(qs + byte_at(ks.ki, e) * G, q[e]);
                         // values of pass rb
@@ -827,13 +834,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
                             }
                         }
 #pragma unroll
-                        for (int e = 0; e < E; ++e) {
+                        for (int e = 0; e < EV; ++e) {
                             const float v = value_at<VB>(vs.vv, e);
 #pragma unroll
                             for (int hh = 0; hh < G; ++hh) o[e][hh] = fmaf(w[hh], v, o[e][hh]);
                         }
 #pragma unroll
-                        for (int e = 0; e < E; ++e)
+                        for (int e = 0; e < EV; ++e)
                             if (!PAD || e < kept) lds_put<G>(vaddr[e], o[e]);
                         // scores of pass rb + P
                         const int r1 = rb + P + d * TPI;
@@ -913,34 +920,44 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(split_waves_
 // launchers
 // ---------------------------------------------------------------------------
 
-template <int G, int KS, bool PAGED, int VB>
+template <int G, int KS, int KSV, bool PAGED, int VB>
 inline void launch_split_v(const SplitArgs &a, hipStream_t s)
 {
     const dim3 grid(a.W), block(kWave);
-    if (a.k < KS)
-        hipLaunchKernelGGL((k_split<G, KS, PAGED, true, VB>), grid, block, 0, s, a);
+    if (a.k_v < KSV)
+        hipLaunchKernelGGL((k_split<G, KS, KSV, PAGED, true, VB>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((k_split<G, KS, PAGED, false, VB>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_split<G, KS, KSV, PAGED, false, VB>), grid, block, 0, s, a);
 }
 
-template <int G, int KS, bool PAGED>
+template <int G, int KS, int KSV, bool PAGED>
 inline void launch_split_k(const SplitArgs &a, hipStream_t s)
 {
     if (a.geom.vbytes == 1)
-        launch_split_v<G, KS, PAGED, 1>(a, s);
+        launch_split_v<G, KS, KSV, PAGED, 1>(a, s);
     else
-        launch_split_v<G, KS, PAGED, 2>(a, s);
+        launch_split_v<G, KS, KSV, PAGED, 2>(a, s);
 }
 
+// key row width x value row width: equal, or one twice the other
 template <int G, bool PAGED>
 inline hipError_t launch_split_g(const SplitArgs &a, hipStream_t s)
 {
-    switch (a.geom.ks) {
-    case 8: launch_split_k<G, 8, PAGED>(a, s); break;
-    case 16: launch_split_k<G, 16, PAGED>(a, s); break;
-    case 32: launch_split_k<G, 32, PAGED>(a, s); break;
-    case 64: launch_split_k<G, 64, PAGED>(a, s); break;
-    case 128: launch_split_k<G, 128, PAGED>(a, s); break;
+    const int ks = a.geom.ks, ksv = a.geom.ks_v;
+    switch (ks * 1000 + ksv) {
+    case 8008: launch_split_k<G, 8, 8, PAGED>(a, s); break;
+    case 8016: launch_split_k<G, 8, 16, PAGED>(a, s); break;
+    case 16008: launch_split_k<G, 16, 8, PAGED>(a, s); break;
+    case 16016: launch_split_k<G, 16, 16, PAGED>(a, s); break;
+    case 16032: launch_split_k<G, 16, 32, PAGED>(a, s); break;
+    case 32016: launch_split_k<G, 32, 16, PAGED>(a, s); break;
+    case 32032: launch_split_k<G, 32, 32, PAGED>(a, s); break;
+    case 32064: launch_split_k<G, 32, 64, PAGED>(a, s); break;
+    case 64032: launch_split_k<G, 64, 32, PAGED>(a, s); break;
+    case 64064: launch_split_k<G, 64, 64, PAGED>(a, s); break;
+    case 64128: launch_split_k<G, 64, 128, PAGED>(a, s); break;
+    case 128064: launch_split_k<G, 128, 64, PAGED>(a, s); break;
+    case 128128: launch_split_k<G, 128, 128, PAGED>(a, s); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

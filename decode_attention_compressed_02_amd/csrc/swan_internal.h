@@ -87,7 +87,8 @@ __host__ __device__ inline uint8_t h2e4m3(uint16_t h)
 // Where the sparse rows of one (sequence, kv head) live.
 struct SparseGeom {
     int H;          // kv heads
-    int ks;         // entries per stored row
+    int ks;         // entries per stored key row
+    int ks_v;       // entries per stored value row (ks unless keys and values keep different counts)
     int n_cap;      // contiguous: rows per unit
     int bs;         // paged: rows per block (0 = contiguous)
     int max_blocks; // paged: block-table width
@@ -96,25 +97,26 @@ struct SparseGeom {
     const int32_t *bt;
 };
 
-// Entry offset of the start of sparse row r of unit (b, h), r below the
-// unit's row capacity.  Paged: -1 when the block-table entry is not a block
-// of the pool (a caller error), so kernels skip the row instead of
-// addressing outside the planes.
+// Row slot of sparse row r of unit (b, h), r below the unit's row
+// capacity: the row starts at entry slot * ks of a key plane and slot * ks_v
+// of a value plane.  Paged: -1 when the block-table entry is not a block of
+// the pool (a caller error), so kernels skip the row instead of addressing
+// outside the planes.
 template <bool PAGED>
-__device__ __forceinline__ int64_t row_offset(const SparseGeom &g, int b, int h, int r)
+__device__ __forceinline__ int64_t row_slot(const SparseGeom &g, int b, int h, int r)
 {
     if constexpr (PAGED) {
         const int blk = g.bt[(int64_t)b * g.max_blocks + r / g.bs];
         if (blk < 0 || blk >= g.num_blocks) return -1;
-        return (((int64_t)blk * g.H + h) * g.bs + (r % g.bs)) * g.ks;
+        return ((int64_t)blk * g.H + h) * g.bs + (r % g.bs);
     } else {
-        return (((int64_t)b * g.H + h) * g.n_cap + r) * g.ks;
+        return ((int64_t)b * g.H + h) * g.n_cap + r;
     }
 }
 
-__device__ __forceinline__ int64_t row_offset_rt(const SparseGeom &g, int b, int h, int r)
+__device__ __forceinline__ int64_t row_slot_rt(const SparseGeom &g, int b, int h, int r)
 {
-    return g.bs > 0 ? row_offset<true>(g, b, h, r) : row_offset<false>(g, b, h, r);
+    return g.bs > 0 ? row_slot<true>(g, b, h, r) : row_slot<false>(g, b, h, r);
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (lane == 0) ? 0ull : ((~0ull) >> (64 - lane)); }
@@ -181,7 +183,7 @@ struct ProjectArgs {
 hipError_t launch_project(const ProjectArgs &a, hipStream_t s);
 
 struct AppendArgs {
-    int B, H, R, k;
+    int B, H, R, k, k_v; // kept key and value coordinates
     SparseGeom geom;
     uint8_t *kidx, *vidx;
     uint8_t *kval, *vval; // value planes, geom.vbytes bytes per entry
@@ -204,19 +206,19 @@ __device__ inline void append_token(const AppendArgs &a, int b, int h, int wave,
     const int64_t u = (int64_t)b * a.H + h;
     uint8_t *idx = wave == 0 ? a.kidx : a.vidx;
     uint8_t *val = wave == 0 ? a.kval : a.vval;
-    const int vb = a.geom.vbytes;
+    const int vb = a.geom.vbytes, kk = wave == 0 ? a.k : a.k_v, ks = wave == 0 ? a.geom.ks : a.geom.ks_v;
     const int row_cap = a.geom.bs > 0 ? a.geom.max_blocks * a.geom.bs : a.geom.n_cap;
     if (a.R == 0) {
-        const int64_t off = p < row_cap ? row_offset_rt(a.geom, b, h, p) : -1;
-        if (off >= 0) wave_prune_row(lane, lo, hi, a.k, a.geom.ks, idx + off, val + off * vb, vb);
+        const int64_t slot = p < row_cap ? row_slot_rt(a.geom, b, h, p) : -1;
+        if (slot >= 0) wave_prune_row(lane, lo, hi, kk, ks, idx + slot * ks, val + slot * ks * vb, vb);
         return;
     }
     uint16_t *buf = (wave == 0 ? a.kbuf : a.vbuf) + (u * a.R + p % a.R) * kD;
     if (p >= a.R) { // the slot holds token p - R, the oldest one
         const uint16_t olo = buf[lane], ohi = buf[lane + 64];
         const int r = p - a.R;
-        const int64_t off = r < row_cap ? row_offset_rt(a.geom, b, h, r) : -1;
-        if (off >= 0) wave_prune_row(lane, olo, ohi, a.k, a.geom.ks, idx + off, val + off * vb, vb);
+        const int64_t slot = r < row_cap ? row_slot_rt(a.geom, b, h, r) : -1;
+        if (slot >= 0) wave_prune_row(lane, olo, ohi, kk, ks, idx + slot * ks, val + slot * ks * vb, vb);
     }
     buf[lane] = lo;
     buf[lane + 64] = hi;
@@ -226,38 +228,34 @@ __device__ inline void append_token(const AppendArgs &a, int b, int h, int wave,
 // unit's new key inside the workgroup, not for the whole grid)
 hipError_t launch_project_append(const ProjectArgs &p, const AppendArgs &a, hipStream_t s);
 
-// Shape of the sparse stream in the split kernel for GQA group G and stored
-// row width KS.  TPI rows (tokens) are in flight per wave iteration, one per
-// accumulator slot, and lane l works on row slot l % TPI; KS / E lanes share
-// a row, each loading E consecutive entries.  A 128-bit LDS access is served
-// in 16-lane phases over 16 bank quads, and the accumulators are laid out as
-// acc[c][slot][g], so with 16 slots the 16 lanes of a phase always hit 16
-// different quads: the value scatter runs without bank conflicts whatever
-// the indices are.  G = 8 keeps 8 slots (LDS size), and very wide rows cap E.
-// Rows of 64 or more entries also use 8 slots: half the accumulator LDS lets
-// two waves share a SIMD, and with 8 or more entries per lane the row sums
-// stay cheap; measured faster than 16 slots at one wave per SIMD.
-__host__ __device__ constexpr int split_slots(int G, int KS) { return (G <= 4 && KS <= 32) ? 16 : 8; }
+// Shape of the sparse stream in the split kernel for GQA group G, stored key
+// rows of KS entries and value rows of KSV entries (KSmax the wider).  TPI
+// rows (tokens) are in flight per wave iteration, one per accumulator slot,
+// and lane l works on row slot l % TPI; the 64 / TPI lanes of a row each load
+// E = KS TPI / 64 consecutive key entries and EV = KSV TPI / 64 value entries.
+// A 128-bit LDS access is served in 16-lane phases over 16 bank quads, and
+// the accumulators are laid out as acc[c][slot][g], so with 16 slots the 16
+// lanes of a phase always hit 16 different quads: the value scatter runs
+// without bank conflicts whatever the indices are.  G = 8 keeps 8 slots (LDS
+// size).  Rows of 64 or more entries also use 8 slots: half the accumulator
+// LDS lets two waves share a SIMD, and with 8 or more entries per lane the
+// row sums stay cheap; measured faster than 16 slots at one wave per SIMD.
+__host__ __device__ constexpr int split_slots(int G, int KSmax) { return (G <= 4 && KSmax <= 32) ? 16 : 8; }
 // resident waves per SIMD the split kernel is compiled for (register budget:
 // 256 registers a lane at two waves; wider rows and g = 8 need more)
-__host__ __device__ constexpr int split_waves_per_simd(int G, int KS) { return (G <= 4 && KS == 64) ? 2 : 1; }
-__host__ __device__ constexpr int split_entries(int G, int KS)
-{
-    const int slots = split_slots(G, KS);
-    const int e = KS * slots / 64;
-    return e < 1 ? 1 : (e > 16 ? 16 : e);
-}
-__host__ __device__ constexpr int split_token_slots(int G, int KS) { return 64 * split_entries(G, KS) / KS; }
+__host__ __device__ constexpr int split_waves_per_simd(int G, int KSmax) { return (G <= 4 && KSmax == 64) ? 2 : 1; }
+// entries per lane of a row of KS entries (1..16 for KS in 8..128)
+__host__ __device__ constexpr int split_entries(int G, int KS, int KSmax) { return KS * split_slots(G, KSmax) / 64; }
 // LDS bytes of one split workgroup: the scaled queries plus the accumulator slots
-__host__ __device__ constexpr int split_lds_bytes(int G, int KS)
+__host__ __device__ constexpr int split_lds_bytes(int G, int KSmax)
 {
-    return 4 * kD * G * (1 + split_token_slots(G, KS));
+    return 4 * kD * G * (1 + split_slots(G, KSmax));
 }
 // split waves resident on one CU: the LDS footprint and, for g >= 4, the
 // register budget above (g <= 2 fits at least two waves per SIMD)
-__host__ __device__ constexpr int split_waves_per_cu(int G, int KS)
+__host__ __device__ constexpr int split_waves_per_cu(int G, int KSmax)
 {
-    const int by_lds = kLdsPerCU / split_lds_bytes(G, KS), by_regs = G >= 4 ? 4 * split_waves_per_simd(G, KS) : 8;
+    const int by_lds = kLdsPerCU / split_lds_bytes(G, KSmax), by_regs = G >= 4 ? 4 * split_waves_per_simd(G, KSmax) : 8;
     const int w = by_lds < by_regs ? by_lds : by_regs;
     return w < 1 ? 1 : w;
 }
@@ -266,7 +264,7 @@ __host__ __device__ constexpr int split_waves_per_cu(int G, int KS)
 // Each unit (sequence b, kv head h) is a run of work rows in one virtual
 // sequence over all units, b-major then h: one per sparse row plus, per
 // buffered token, its bytes relative to a sparse row (a buffered token
-// streams 2 x 256 bytes, a sparse row 2 x 3 KS).  The T work rows of the
+// streams 2 x 256 bytes, a sparse row (1 + value bytes) (KS + KSV)).  The T work rows of the
 // batch are cut into V nearly equal ranges, wave w taking [w T / V,
 // (w + 1) T / V) (rounded down), so every wave streams about the same bytes
 // whatever the mix of lengths; when V is a multiple of the unit count and
@@ -280,20 +278,22 @@ __host__ __device__ constexpr int split_waves_per_cu(int G, int KS)
 constexpr int kSparseQuantum = 16; // a multiple of the rows per ring slot
 constexpr int kMinWaveRows = 64;
 
-// work rows of buffered tokens [0, f) for stored rows of ks entries
-__host__ __device__ inline int64_t dense_work(int64_t f, int ks) { return (f * 256 + 3 * ks - 1) / (3 * ks); }
+// work rows of buffered tokens [0, f) when a stored sparse row (key and
+// value planes) is row_bytes bytes
+__host__ __device__ inline int64_t dense_work(int64_t f, int row_bytes) { return (f * 512 + row_bytes - 1) / row_bytes; }
+__host__ __device__ constexpr int sparse_row_bytes(int ks, int ks_v, int vbytes) { return (1 + vbytes) * (ks + ks_v); }
 
 struct UnitWork {
     int64_t n, f, len; // sparse rows, buffered tokens, work rows
 };
-__host__ __device__ inline UnitWork unit_work(int32_t pos, int R, int64_t row_cap, int ks)
+__host__ __device__ inline UnitWork unit_work(int32_t pos, int R, int64_t row_cap, int row_bytes)
 {
     const int64_t ctx = (int64_t)pos + 1; // <= 0: inactive sequence
     UnitWork u;
     u.n = ctx > R ? ctx - R : 0;
     if (u.n > row_cap) u.n = row_cap;
     u.f = ctx <= 0 ? 0 : (ctx < R ? ctx : R);
-    u.len = u.n + dense_work(u.f, ks);
+    u.len = u.n + dense_work(u.f, row_bytes);
     return u;
 }
 // first sparse row of the piece starting at work row x of the unit (0 <= x
@@ -321,7 +321,7 @@ struct SplitArgs {
     int B, N_h, H, R;
     int W;            // waves of the split pass (the grid)
     int split_tokens; // about this many work rows per wave; 0: spread the batch over W waves
-    int k;            // kept entries per row; entries k..ks-1 are padding
+    int k, k_v;       // kept key and value entries per row; the rest of a stored row is padding
     int row_cap;      // sparse rows addressable per unit
     SparseGeom geom;
     const int32_t *pos;
@@ -337,9 +337,13 @@ hipError_t launch_split_g1(const SplitArgs &a, hipStream_t s);
 hipError_t launch_split_g2(const SplitArgs &a, hipStream_t s);
 hipError_t launch_split_g4(const SplitArgs &a, hipStream_t s);
 hipError_t launch_split_g8(const SplitArgs &a, hipStream_t s);
+hipError_t launch_split_g1_paged(const SplitArgs &a, hipStream_t s);
+hipError_t launch_split_g2_paged(const SplitArgs &a, hipStream_t s);
+hipError_t launch_split_g4_paged(const SplitArgs &a, hipStream_t s);
+hipError_t launch_split_g8_paged(const SplitArgs &a, hipStream_t s);
 
 struct ReduceArgs {
-    int B, N_h, H, R, W, split_tokens, ks, row_cap;
+    int B, N_h, H, R, W, split_tokens, row_bytes, row_cap;
     const int32_t *pos;
     const float *part_o, *part_ml;
     float *o_hat;
@@ -347,7 +351,7 @@ struct ReduceArgs {
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
 
 struct PrefillArgs {
-    int B, H, R, k;
+    int B, H, R, k, k_v;
     int64_t T_stride;
     int max_len;
     SparseGeom geom;
@@ -362,8 +366,8 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 
 struct CopyBlocksArgs {
     int count, num_blocks;
-    int64_t block_bytes_idx; // bytes of one block of an index plane (value planes: vbytes times)
-    int vbytes;
+    int64_t block_bytes_kidx, block_bytes_vidx; // bytes of one block of the key / value index plane
+    int vbytes;                                 // value planes: vbytes times their index plane
     uint8_t *kidx, *vidx;
     uint8_t *kval, *vval;
     const int32_t *src, *dst;

@@ -26,8 +26,8 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # sources that define the split kernel; a traffic figure is valid only for them
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_compressed_02_amd", "csrc", f)
-                  for f in ("split_kernel.h", "split_g1.hip", "split_g2.hip", "split_g4.hip", "split_g8.hip",
-                            "decode.hip", "swan_internal.h")]
+                  for f in ("split_kernel.h", "decode.hip", "swan_internal.h")
+                  + tuple(f"split_g{g}{p}.hip" for g in (1, 2, 4, 8) for p in ("", "_paged"))]
 COPY_KERNEL_HINT = "copy"  # torch's device-to-device copy kernel names contain this
 
 

@@ -33,13 +33,14 @@ def build_decoder(w: wl.Workload, split_tokens: int = 0, extra_steps: int = 0):
         pool = shared_prefix_pool(B, rows, steps, w.block_size, w.shared_prefix, lambda n: wl.pool_order(w, n),
                                   w.pool_slack)
         dims = S.make_dims(w.B, w.N_h, w.H_kv, w.R, w.k, block_size=w.block_size, max_blocks=pool.max_blocks,
-                           num_blocks=pool.num_blocks, split_tokens=split_tokens, value_format=w.value_format)
+                           num_blocks=pool.num_blocks, split_tokens=split_tokens, value_format=w.value_format,
+                           k_v=w.k_v)
         dec = PagedSwanDecoder(dims, P, pool, w.rope_base)
         _log(f"paged pool: {pool.num_blocks} blocks of {w.block_size} rows, "
              f"{int((pool.ref > 1).sum())} shared (reference count {int(pool.ref.max())})")
     else:
         dims = S.make_dims(w.B, w.N_h, w.H_kv, w.R, w.k, n_cap=w.n_cap() + extra_steps + 64,
-                           split_tokens=split_tokens, value_format=w.value_format)
+                           split_tokens=split_tokens, value_format=w.value_format, k_v=w.k_v)
         dec = SwanDecoder(dims, P, w.rope_base)
     K = torch.empty((B, H, Tm, 128), dtype=torch.float32, device="cuda")
     V = torch.empty_like(K)

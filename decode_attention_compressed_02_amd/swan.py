@@ -30,7 +30,7 @@ class SwanError(RuntimeError):
 
 class swan_dims(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("B", "N_h", "H_kv", "d_h", "R", "k", "n_cap", "block_size", "max_blocks",
-                                         "num_blocks", "split_tokens", "value_format")]
+                                         "num_blocks", "split_tokens", "value_format", "k_v")]
 
     def __repr__(self):
         return "swan_dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -104,8 +104,9 @@ SWAN_VALUES_FP16, SWAN_VALUES_FP8_E4M3 = 0, 1
 
 
 def make_dims(B, N_h, H_kv, R, k, n_cap=0, d_h=128, block_size=0, max_blocks=0, num_blocks=0, split_tokens=0,
-              value_format=SWAN_VALUES_FP16):
-    return swan_dims(B, N_h, H_kv, d_h, R, k, n_cap, block_size, max_blocks, num_blocks, split_tokens, value_format)
+              value_format=SWAN_VALUES_FP16, k_v=0):
+    return swan_dims(B, N_h, H_kv, d_h, R, k, n_cap, block_size, max_blocks, num_blocks, split_tokens, value_format,
+                     k_v)
 
 
 def swan_row_stride(k: int) -> int:
@@ -113,7 +114,8 @@ def swan_row_stride(k: int) -> int:
 
 
 def swan_cache_bytes(dims: swan_dims):
-    out = (C.c_size_t * 3)()
+    """(k_idx, k_val, v_idx, v_val, k_buf = v_buf) bytes."""
+    out = (C.c_size_t * 5)()
     _check(lib().swan_cache_bytes(C.byref(dims), out))
     return tuple(int(x) for x in out)
 

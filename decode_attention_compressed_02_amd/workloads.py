@@ -63,6 +63,7 @@ class Workload:
     shared_prefix: int = 0  # tokens whose K/V are identical across all sequences
     pool_slack: int = 0  # extra free blocks in the paged pool
     value_format: int = 0  # sparse values: 0 fp16, 1 fp8 E4M3 (storage only; the inputs are the same)
+    k_v: int = 0  # value coordinates kept, 0 = k (keys and values keeping different shares)
 
     @property
     def g(self) -> int:

@@ -44,16 +44,18 @@
  *
  * Cache layout (all planes caller-allocated, sizes from swan_cache_bytes)
  * ------------
- * Each sparse row stores k_stride = swan_row_stride(k) entries (k rounded up
- * to a power of two, at least 8, so a row splits evenly over 8-entry lane
- * slices); entries k..k_stride-1 are padding with index 0 and value +0, which
+ * Each sparse key row stores k_stride = swan_row_stride(k) entries and each
+ * value row v_stride = swan_row_stride(k_v ? k_v : k) (the count rounded up
+ * to a power of two, at least 8, so a row splits evenly over lane slices);
+ * entries past the kept count are padding with index 0 and value +0, which
  * contribute nothing to scores or outputs.
  *   contiguous (block_size == 0):
- *     k_idx, v_idx  uint8   [B][H_kv][n_cap][k_stride]
- *     k_val, v_val  fp16 or fp8 (value_format) [B][H_kv][n_cap][k_stride]
+ *     k_idx         uint8   [B][H_kv][n_cap][k_stride]
+ *     k_val         fp16 or fp8 (value_format) [B][H_kv][n_cap][k_stride]
+ *     v_idx, v_val  likewise with v_stride
  *   paged (block_size > 0, "Reuse, Evict, or Limit Earlier Context" 1.2):
- *     k_idx, v_idx  uint8   [num_blocks][H_kv][block_size][k_stride]
- *     k_val, v_val  fp16 or fp8 [num_blocks][H_kv][block_size][k_stride]
+ *     k_idx, k_val  [num_blocks][H_kv][block_size][k_stride]
+ *     v_idx, v_val  [num_blocks][H_kv][block_size][v_stride]
  *     block_table   int32   [B][max_blocks]: sparse row t of sequence b is
  *                   slot t % block_size of block block_table[b][t / block_size]
  *   dense buffer:
@@ -95,6 +97,10 @@ typedef struct swan_dims {
     int32_t num_blocks;   /* paged: blocks in the pool                             */
     int32_t split_tokens; /* decode: work rows per wave (multiple of 64), 0 = auto */
     int32_t value_format; /* sparse values: SWAN_VALUES_FP16 (0) or SWAN_VALUES_FP8_E4M3 */
+    int32_t k_v;          /* coordinates kept per pruned value vector, 0 = k (keys keep k)
+                             (SWAN Appendix A.5, Table 2: keys and values may keep
+                             different shares of d_h); swan_row_stride(k_v) must equal
+                             swan_row_stride(k), twice it or half of it */
 } swan_dims;
 
 /* Storage of the values of sparse rows (the dense buffer is always fp16).
@@ -127,10 +133,10 @@ const char *swan_last_error(void);
 /* Entries stored per sparse row: k rounded up to a power of two, >= 8. */
 int32_t swan_row_stride(int32_t k);
 
-/* Bytes of each cache plane for `dims` (host): out[0] = k_idx (= v_idx),
- * out[1] = k_val (= v_val), out[2] = k_buf (= v_buf).  Returns the status of
- * validating dims. */
-swan_status swan_cache_bytes(const swan_dims *dims, size_t out[3]);
+/* Bytes of each cache plane for `dims` (host): out[0] = k_idx, out[1] =
+ * k_val, out[2] = v_idx, out[3] = v_val, out[4] = k_buf (= v_buf).  Returns
+ * the status of validating dims. */
+swan_status swan_cache_bytes(const swan_dims *dims, size_t out[5]);
 
 /*
  * Step 1 -- runtime projection (SWAN section 4.1: RoPE cannot be absorbed
@@ -161,8 +167,9 @@ swan_status swan_project_qk(const swan_dims *dims, const float *q, const float *
  * For R > 0 the token at pos - R (if pos >= R) is read from slot pos mod R,
  * pruned into sparse row pos - R, and the new token takes the slot.  For
  * R == 0 the new token is pruned straight into sparse row pos.  Pruning keeps
- * the k coordinates first in the order (|x| descending as fp16 magnitude,
- * index ascending) and copies their values bit for bit.  In the paged layout
+ * the k (values: k_v) coordinates first in the order (|x| descending as fp16
+ * magnitude, index ascending) and copies their values bit for bit (8-bit
+ * values: rounds them to E4M3 as described above).  In the paged layout
  * the block holding the new row must be allocated and exclusively owned by
  * the sequence (copy-on-write is the caller's job).
  */

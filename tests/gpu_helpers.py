@@ -20,7 +20,8 @@ def rel_l2_max(got, want):
 def dims_for(oc, split_tokens=0, block_size=0, max_blocks=0, num_blocks=0):
     return S.make_dims(oc.B, oc.N_h, oc.H_kv, oc.R, oc.k, n_cap=oc.ncap if block_size == 0 else 0,
                        block_size=block_size, max_blocks=max_blocks, num_blocks=num_blocks,
-                       split_tokens=split_tokens, value_format=oc.value_format)
+                       split_tokens=split_tokens, value_format=oc.value_format,
+                       k_v=oc.k_v if oc.k_v != oc.k else 0)
 
 
 def value_storage(v, value_format):
@@ -53,10 +54,11 @@ def upload(cache: HybridCache, oc, block_table: np.ndarray | None = None, rows=N
     paged layout only rows < rows[b] of sequence b are written (default: all
     ncap), so that a short sequence sharing blocks with a longer one does not
     overwrite the longer one's rows."""
-    d, ks, k = cache.dims, cache.k_stride, oc.k
+    d = cache.dims
     planes = cache.sparse_views()
     src = (oc.kidx, value_storage(oc.kval, d.value_format), oc.vidx, value_storage(oc.vval, d.value_format))
     for dst, s in zip(planes, src):
+        k = s.shape[-1]  # kept entries of this plane (k or k_v)
         host = np.zeros(tuple(dst.shape), dtype=s.dtype)
         if d.block_size == 0:
             host[:, :, :oc.ncap, :k] = s

@@ -38,14 +38,18 @@ def test_row_stride_and_sizes():
     assert [S.swan_row_stride(k) for k in (1, 7, 8, 9, 16, 24, 32, 33, 64, 100, 128)] == \
         [8, 8, 8, 16, 16, 32, 32, 64, 64, 128, 128]
     d = S.make_dims(16, 32, 8, 256, 32, n_cap=32528)
-    n_idx, n_val, n_buf = S.swan_cache_bytes(d)
-    assert n_idx == 16 * 8 * 32528 * 32 and n_val == 2 * n_idx
+    n_idx, n_val, nv_idx, nv_val, n_buf = S.swan_cache_bytes(d)
+    assert n_idx == 16 * 8 * 32528 * 32 and n_val == 2 * n_idx and (nv_idx, nv_val) == (n_idx, n_val)
     assert n_buf == 16 * 8 * 256 * 128 * 2
     dp = S.make_dims(32, 32, 8, 64, 64, block_size=16, max_blocks=1024, num_blocks=20000)
     assert S.swan_cache_bytes(dp)[0] == 20000 * 8 * 16 * 64
     # 8-bit values: one byte per value entry, the dense buffer stays fp16
     d8 = S.make_dims(16, 32, 8, 256, 32, n_cap=32528, value_format=S.SWAN_VALUES_FP8_E4M3)
-    assert S.swan_cache_bytes(d8) == (n_idx, n_idx, n_buf)
+    assert S.swan_cache_bytes(d8) == (n_idx, n_idx, n_idx, n_idx, n_buf)
+    # keys keep 77 (stride 128), values 51 (stride 64)
+    da = S.make_dims(2, 8, 2, 16, 77, n_cap=100, k_v=51)
+    rows = 2 * 2 * 100
+    assert S.swan_cache_bytes(da) == (rows * 128, rows * 256, rows * 64, rows * 128, 2 * 2 * 16 * 128 * 2)
 
 
 def test_split_plan():
@@ -197,6 +201,10 @@ cases = [
     ("B = 0", proj(dims(B=0)), E),
     ("split_tokens not /64", dec(dims(split_tokens=100)), E),
     ("value format 2", proj(dims(value_format=2)), U),
+    ("k_v > d_h", proj(dims(k_v=129)), E),
+    ("k_v < 0", proj(dims(k_v=-1)), E),
+    ("k_v stride 4x k's", dec(dims(k=8, k_v=32)), U),
+    ("k_v stride 8x k's", app(dims(k=128, k_v=16)), U),
     ("value format -1", dec(dims(value_format=-1)), U),
     ("null q", proj(dims(), q=N), E),
     ("null k_hat out", proj(dims(), kh=N), E),

@@ -124,12 +124,25 @@ def tie_values(r, shape):
 @pytest.mark.parametrize("paged", [False, True])
 @pytest.mark.parametrize("vf", [0, 1])
 def test_append_evict_bit_exact(k, R, paged, vf):
-    r = rng(1000 + k * 7 + R * 3 + paged + 17 * vf)
+    _append_case(k, k, R, paged, vf)
+
+
+@pytest.mark.parametrize("k,kv", [(77, 51), (51, 77), (20, 40), (100, 60), (16, 8)])
+@pytest.mark.parametrize("R", [0, 16])
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("vf", [0, 1])
+def test_append_evict_asymmetric(k, kv, R, paged, vf):
+    """Keys keep k and values k_v coordinates (rows of different widths)."""
+    _append_case(k, kv, R, paged, vf)
+
+
+def _append_case(k, kv, R, paged, vf):
+    r = rng(1000 + k * 7 + kv * 13 + R * 3 + paged + 17 * vf)
     B, N, H = 3, 4, 2
     T = [40, 9, 0]  # tokens already cached per sequence
     ncap = 48
     w = wl.Workload("app", B, N, H, R, k, tuple(t + 1 for t in T), seed=11 + k + R)
-    oc = oracle.OracleCache(B, N, H, D, R, k, ncap, value_format=vf)
+    oc = oracle.OracleCache(B, N, H, D, R, k, ncap, value_format=vf, k_v=kv)
     K = r.standard_normal((B, H, max(T), D)).astype(np.float32)
     V = r.standard_normal((B, H, max(T), D)).astype(np.float32)
     V[:, :, ::3] = tie_values(r, V[:, :, ::3].shape)
@@ -157,18 +170,19 @@ def test_append_evict_bit_exact(k, R, paged, vf):
     torch.cuda.synchronize()
     oc.append(khat, vhat.astype(np.float64), pos)
     rows = download_rows(dec.cache, B, H, ncap, bt)
-    ks = S.swan_row_stride(k)
+    ks, ksv = S.swan_row_stride(k), S.swan_row_stride(kv)
+    assert rows[0].shape[-1] == ks and rows[2].shape[-1] == ksv
     n_after = [max(0, t + 1 - R) for t in T]
     for b in range(B):
         n = n_after[b]
         gi, gv, hi, hv = (x[b, :, :n] for x in rows)
         np.testing.assert_array_equal(gi[..., :k], oc.kidx[b, :, :n])
-        np.testing.assert_array_equal(hi[..., :k], oc.vidx[b, :, :n])
+        np.testing.assert_array_equal(hi[..., :kv], oc.vidx[b, :, :n])
         assert_values_bits(gv[..., :k], oc.kval[b, :, :n], vf)
-        assert_values_bits(hv[..., :k], oc.vval[b, :, :n], vf)
-        if ks > k:  # padding is index 0, value +0
-            assert not gi[..., k:].any() and not gv[..., k:].view(np.uint8).any()
-            assert not hi[..., k:].any() and not hv[..., k:].view(np.uint8).any()
+        assert_values_bits(hv[..., :kv], oc.vval[b, :, :n], vf)
+        # padding is index 0, value +0
+        assert not gi[..., k:].any() and not gv[..., k:].view(np.uint8).any()
+        assert not hi[..., kv:].any() and not hv[..., kv:].view(np.uint8).any()
     if R > 0:
         kb, vb = (x.cpu().numpy() for x in dec.cache.buffer_views())
         rk, rv = oc.ring_f16()
@@ -245,6 +259,13 @@ DECODE_CASES = {
                               dict(outlier_channels=4, outlier_scale=200.0, value_format=1)),
     "fp8_g8_k16": (2, 16, 2, 16, 16, (500, 300), 128, dict(value_format=1)),
     "fp8_g1_k128_R0": (2, 1, 1, 0, 128, (300, 129), 64, dict(value_format=1)),
+    # keys and values keeping different counts (TopK_R / TopV_R of the ablation)
+    "kv_77_51_g4": (2, 8, 2, 64, 77, (1500, 333), 0, dict(k_v=51)),
+    "kv_51_77_g4_fp8": (2, 8, 2, 64, 51, (1500, 333), 0, dict(k_v=77, value_format=1)),
+    "kv_20_40_g4": (3, 8, 2, 32, 20, (900, 700, 40), 64, dict(k_v=40)),
+    "kv_40_20_g8": (2, 16, 2, 16, 40, (600, 300), 0, dict(k_v=20)),
+    "kv_100_60_g2": (2, 4, 2, 8, 100, (500, 128), 0, dict(k_v=60)),
+    "kv_16_8_g1": (2, 1, 1, 16, 16, (400, 90), 64, dict(k_v=8)),
 }
 
 
@@ -303,12 +324,14 @@ def test_decode_inactive_and_ragged():
 # whole steps chained on the GPU vs oracle steps
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cfg", ["config1_full", "config3_small", "config3_small_fp8"])
+@pytest.mark.parametrize("cfg", ["config1_full", "config3_small", "config3_small_fp8", "config3_small_kv"])
 def test_step_chain(cfg):
     if cfg == "config1_full":
         w = wl.config(1)
     else:
         w = wl.config(3).scaled(B=2, ctx=(700, 531), R=16, steps=5, value_format=int(cfg.endswith("fp8")))
+        if cfg.endswith("kv"):  # TopK_R 0.6 / TopV_R 0.4 of the same budget
+            w = w.scaled(k=38, k_v=26)
     oc, *_ = oracle_state(w)
     P = wl.projection_qk(w)
     dec = make_decoder(oc, P)
@@ -328,17 +351,19 @@ def test_step_chain(cfg):
             r = int(pos[b]) - w.R
             if r >= 0:
                 np.testing.assert_array_equal(rows[0][b, :, r, :w.k], oc.kidx[b, :, r])
-                assert_values_bits(rows[3][b, :, r, :w.k], oc.vval[b, :, r], w.value_format)
+                assert_values_bits(rows[3][b, :, r, :w.k_v or w.k], oc.vval[b, :, r], w.value_format)
 
 
 # ---------------------------------------------------------------------------
 # prefill -> hybrid cache
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("R,k,vf", [(128, 32, 0), (0, 64, 0), (300, 16, 0), (128, 32, 1), (0, 64, 1)])
-def test_prefill_convert(R, k, vf):
+@pytest.mark.parametrize("R,k,vf,kv", [(128, 32, 0, 0), (0, 64, 0, 0), (300, 16, 0, 0), (128, 32, 1, 0),
+                                       (0, 64, 1, 0), (128, 77, 0, 51), (64, 51, 1, 77)])
+def test_prefill_convert(R, k, vf, kv):
     w = wl.Workload("pre", 3, 8, 2, R, k, (1200, 77, 301), seed=21 + R, outlier_channels=4, outlier_scale=8.0,
-                    value_format=vf)
+                    value_format=vf, k_v=kv)
+    kv = kv or k
     oc, K, V, Ts = oracle_state(w)
     P = wl.projection_qk(w)
     dec = make_decoder(oc, P)
@@ -348,8 +373,8 @@ def test_prefill_convert(R, k, vf):
     for b in range(w.B):
         n = max(0, int(Ts[b]) - R)
         # values: fp32 -> fp16 on both sides, then integer top-k: bit exact
-        np.testing.assert_array_equal(rows[2][b, :, :n, :k], oc.vidx[b, :, :n])
-        assert_values_bits(rows[3][b, :, :n, :k], oc.vval[b, :, :n], vf)
+        np.testing.assert_array_equal(rows[2][b, :, :n, :kv], oc.vidx[b, :, :n])
+        assert_values_bits(rows[3][b, :, :n, :kv], oc.vval[b, :, :n], vf)
         # keys: double products rounded once to fp16 on both sides
         np.testing.assert_array_equal(rows[0][b, :, :n, :k], oc.kidx[b, :, :n])
         assert_values_bits(rows[1][b, :, :n, :k], oc.kval[b, :, :n], vf)
