@@ -253,6 +253,9 @@ DECODE_CASES = {
     "k100": (2, 4, 2, 24, 100, (400, 30), 0, {}),
     "all_dense": (2, 8, 2, 256, 32, (200, 256), 0, {}),
     "drift": (1, 8, 2, 64, 32, (3000,), 0, dict(drift_amp=0.5)),
+    # one unit cut into a few hundred pieces (the reduce loops over chunks of
+    # its 128 threads)
+    "g8_one_unit_many_pieces": (1, 8, 1, 64, 32, (20000,), 64, {}),
     # 8-bit values (E4M3): the same streams with one byte per value
     "fp8_g4_k32": (3, 8, 2, 64, 32, (1500, 800, 70), 0, dict(value_format=1)),
     "fp8_g4_k64_saturating": (2, 8, 2, 128, 64, (1700, 1301), 0,
