@@ -9,8 +9,8 @@
 // bytes across the 128 threads of a quarter; P_QK is L2-resident across the
 // sequences of a batch), and the four partial sums meet in LDS.  The 4 d_h^2
 // FLOPs per head of SWAN appendix A.2 are tiny next to the decode stream: the
-// kernel is latency-bound, so the row walk is cut four ways and its loads are
-// issued eight at a time.
+// kernel is latency-bound, so the row walk is cut four ways and every load is
+// issued before the first barrier.
 //
 // The arithmetic is in double: the new key is rounded once to fp16 and its
 // top-k coordinates are chosen on those fp16 magnitudes, so a key computed
@@ -24,53 +24,82 @@ namespace swan {
 constexpr int kProjThreads = 512;
 constexpr int kProjRows = kD / (kProjThreads / kD); // rows of P per thread group
 
-// With APPEND the first two waves then append the unit's new key (from LDS)
-// and value to the cache, as k_append does.
+// With APPEND the workgroup also appends the unit's new key and value.  The
+// value needs no projection and the token leaving the buffer needs nothing
+// of the new one, so the last two waves append the value and evict the
+// oldest key while the rotation angles are computed; only the new key's
+// placement waits for the projection.  Every load that depends on no other
+// (raw vectors, rows of P_QK, the old buffer entries) is issued at the start.
 template <int G, bool APPEND>
 __global__ __launch_bounds__(kProjThreads) void k_project(ProjectArgs a, AppendArgs ap)
 {
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int j = tid % kD, quarter = tid / kD;
+    const int j = tid % kD, quarter = tid / kD, wave = tid / kWave, lane = tid % kWave;
+    constexpr int kWaves = kProjThreads / kWave;
     __shared__ double xs[G + 1][kD];
     __shared__ double part[kProjThreads / kD - 1][G + 1][kD];
     __shared__ double cs[kD / 2], sn[kD / 2];
     __shared__ uint16_t khs[APPEND ? kD : 1];
 
-    const int p = max(a.pos[b], 0);
+    // RoPE items (vector v, pair i) = tid, tid + 512, ...: v < G are the
+    // query heads of the group, v = G the key
+    constexpr int kItems = (G + 1) * (kD / 2), kPer = (kItems + kProjThreads - 1) / kProjThreads;
+    float x0[kPer], x1[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int e = tid + r * kProjThreads, v = e / (kD / 2), i = e % (kD / 2);
+        x0[r] = x1[r] = 0.f;
+        if (e < kItems) {
+            const float *x = (v < G) ? a.q + ((int64_t)b * a.N_h + h * G + v) * kD : a.k + ((int64_t)b * a.H + h) * kD;
+            x0[r] = x[i];
+            x1[r] = x[i + kD / 2];
+        }
+    }
+    const int c0 = quarter * kProjRows;
+    float pr[kProjRows];
+    {
+        const float *P = a.P + (int64_t)h * kD * kD + (int64_t)c0 * kD + j;
+#pragma unroll
+        for (int u = 0; u < kProjRows; ++u) pr[u] = P[u * kD];
+    }
+    if constexpr (APPEND) {
+        if (wave == kWaves - 1) {
+            const int64_t u = (int64_t)b * ap.H + h;
+            append_token(ap, b, h, 1, lane, f2h(ap.v_hat[u * kD + lane]), f2h(ap.v_hat[u * kD + lane + 64]));
+        } else if (wave == kWaves - 2) {
+            evict_token(ap, b, h, 0, lane);
+        }
+    }
     if (tid < kD / 2) {
         // angle in double: at positions ~1e5 a float angle is off by ~1e-2 rad
         const double theta = pow((double)a.base, -(double)tid / (double)(kD / 2));
-        double s, c;
-        sincos((double)p * theta, &s, &c);
-        cs[tid] = c;
-        sn[tid] = s;
+        const int p = max(a.pos[b], 0);
+        double sv, cv;
+        sincos((double)p * theta, &sv, &cv);
+        cs[tid] = cv;
+        sn[tid] = sv;
     }
     __syncthreads();
-    // RoPE: pair (i, i + 64) rotated by angle_i; 512 threads cover 8 vectors per pass
-    for (int v = tid / (kD / 2); v < G + 1; v += kProjThreads / (kD / 2)) {
-        const int i = tid % (kD / 2);
-        const float *x = (v < G) ? a.q + ((int64_t)b * a.N_h + h * G + v) * kD : a.k + ((int64_t)b * a.H + h) * kD;
-        const double x0 = x[i], x1 = x[i + kD / 2];
-        xs[v][i] = x0 * cs[i] - x1 * sn[i];
-        xs[v][i + kD / 2] = x1 * cs[i] + x0 * sn[i];
+    // RoPE: pair (i, i + 64) rotated by angle_i
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int e = tid + r * kProjThreads, v = e / (kD / 2), i = e % (kD / 2);
+        if (e < kItems) {
+            const double y0 = x0[r], y1 = x1[r];
+            xs[v][i] = y0 * cs[i] - y1 * sn[i];
+            xs[v][i + kD / 2] = y1 * cs[i] + y0 * sn[i];
+        }
     }
     __syncthreads();
 
+    // thread (quarter, j): rows c0 .. c0 + 31 of P_QK for output coordinate j
     double acc[G + 1];
 #pragma unroll
     for (int v = 0; v < G + 1; ++v) acc[v] = 0.0;
-    const int c0 = quarter * kProjRows;
-    const float *P = a.P + (int64_t)h * kD * kD + (int64_t)c0 * kD + j;
 #pragma unroll
-    for (int cb = 0; cb < kProjRows; cb += 8) {
-        float pr[8];
+    for (int u = 0; u < kProjRows; ++u)
 #pragma unroll
-        for (int u = 0; u < 8; ++u) pr[u] = P[(cb + u) * kD];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-            for (int v = 0; v < G + 1; ++v) acc[v] = fma(xs[v][c0 + cb + u], (double)pr[u], acc[v]);
-    }
+        for (int v = 0; v < G + 1; ++v) acc[v] = fma(xs[v][c0 + u], (double)pr[u], acc[v]);
     if (quarter > 0) {
 #pragma unroll
         for (int v = 0; v < G + 1; ++v) part[quarter - 1][v][j] = acc[v];
@@ -89,13 +118,7 @@ __global__ __launch_bounds__(kProjThreads) void k_project(ProjectArgs a, AppendA
     }
     if constexpr (APPEND) {
         __syncthreads();
-        const int wave = tid / kWave, lane = tid % kWave;
-        if (wave < 2) {
-            const int64_t u = (int64_t)b * a.H + h;
-            const uint16_t lo = wave == 0 ? khs[lane] : f2h(ap.v_hat[u * kD + lane]);
-            const uint16_t hi = wave == 0 ? khs[lane + 64] : f2h(ap.v_hat[u * kD + lane + 64]);
-            append_token(ap, b, h, wave, lane, lo, hi);
-        }
+        if (wave == 0) place_token(ap, b, h, 0, lane, khs[lane], khs[lane + 64]);
     }
 }
 

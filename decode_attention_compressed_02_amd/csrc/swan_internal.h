@@ -194,34 +194,54 @@ struct AppendArgs {
 };
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 
-// Append of one token to unit (b, h) by one wave: `wave` 0 handles the key,
-// 1 the value; (lo, hi) are the token's fp16 coordinates lane and lane + 64.
-// The token leaving the circular buffer (slot = position mod R) is pruned into
-// its sparse row first; with R = 0 the new token is pruned straight into row
-// pos.  Inactive sequences (pos < 0) append nothing.
-__device__ inline void append_token(const AppendArgs &a, int b, int h, int wave, int lane, uint16_t lo, uint16_t hi)
+// Append of one token to unit (b, h) by one wave, in two parts: `wave` 0
+// handles the key, 1 the value; (lo, hi) are the token's fp16 coordinates
+// lane and lane + 64.  evict_token prunes the token leaving the circular
+// buffer (slot = position mod R, holding token pos - R) into its sparse row;
+// it needs nothing of the new token, so it may run before the new key is
+// known.  place_token then writes the new token into that slot; with R = 0 it
+// prunes the new token straight into row pos.  Inactive sequences (pos < 0)
+// append nothing.  The two parts must run in this order (the slot is read
+// before it is overwritten).
+__device__ inline void evict_token(const AppendArgs &a, int b, int h, int wave, int lane)
+{
+    const int p = a.pos[b];
+    if (p < a.R || a.R == 0) return; // also p < 0
+    const int64_t u = (int64_t)b * a.H + h;
+    const uint16_t *buf = (wave == 0 ? a.kbuf : a.vbuf) + (u * a.R + p % a.R) * kD;
+    const uint16_t olo = buf[lane], ohi = buf[lane + 64];
+    const int r = p - a.R;
+    const int row_cap = a.geom.bs > 0 ? a.geom.max_blocks * a.geom.bs : a.geom.n_cap;
+    const int64_t slot = r < row_cap ? row_slot_rt(a.geom, b, h, r) : -1;
+    if (slot < 0) return;
+    const int vb = a.geom.vbytes, kk = wave == 0 ? a.k : a.k_v, ks = wave == 0 ? a.geom.ks : a.geom.ks_v;
+    wave_prune_row(lane, olo, ohi, kk, ks, (wave == 0 ? a.kidx : a.vidx) + slot * ks,
+                   (wave == 0 ? a.kval : a.vval) + slot * ks * vb, vb);
+}
+
+__device__ inline void place_token(const AppendArgs &a, int b, int h, int wave, int lane, uint16_t lo, uint16_t hi)
 {
     const int p = a.pos[b];
     if (p < 0) return;
     const int64_t u = (int64_t)b * a.H + h;
-    uint8_t *idx = wave == 0 ? a.kidx : a.vidx;
-    uint8_t *val = wave == 0 ? a.kval : a.vval;
-    const int vb = a.geom.vbytes, kk = wave == 0 ? a.k : a.k_v, ks = wave == 0 ? a.geom.ks : a.geom.ks_v;
-    const int row_cap = a.geom.bs > 0 ? a.geom.max_blocks * a.geom.bs : a.geom.n_cap;
     if (a.R == 0) {
+        const int row_cap = a.geom.bs > 0 ? a.geom.max_blocks * a.geom.bs : a.geom.n_cap;
         const int64_t slot = p < row_cap ? row_slot_rt(a.geom, b, h, p) : -1;
-        if (slot >= 0) wave_prune_row(lane, lo, hi, kk, ks, idx + slot * ks, val + slot * ks * vb, vb);
+        if (slot < 0) return;
+        const int vb = a.geom.vbytes, kk = wave == 0 ? a.k : a.k_v, ks = wave == 0 ? a.geom.ks : a.geom.ks_v;
+        wave_prune_row(lane, lo, hi, kk, ks, (wave == 0 ? a.kidx : a.vidx) + slot * ks,
+                       (wave == 0 ? a.kval : a.vval) + slot * ks * vb, vb);
         return;
     }
     uint16_t *buf = (wave == 0 ? a.kbuf : a.vbuf) + (u * a.R + p % a.R) * kD;
-    if (p >= a.R) { // the slot holds token p - R, the oldest one
-        const uint16_t olo = buf[lane], ohi = buf[lane + 64];
-        const int r = p - a.R;
-        const int64_t slot = r < row_cap ? row_slot_rt(a.geom, b, h, r) : -1;
-        if (slot >= 0) wave_prune_row(lane, olo, ohi, kk, ks, idx + slot * ks, val + slot * ks * vb, vb);
-    }
     buf[lane] = lo;
     buf[lane + 64] = hi;
+}
+
+__device__ inline void append_token(const AppendArgs &a, int b, int h, int wave, int lane, uint16_t lo, uint16_t hi)
+{
+    evict_token(a, b, h, wave, lane);
+    place_token(a, b, h, wave, lane, lo, hi);
 }
 
 // projection and append of a step in one launch (the append waits for the
