@@ -138,28 +138,31 @@ __device__ __forceinline__ void wave_prune_row(int lane, uint16_t lo, uint16_t h
             ((uint16_t *)val_row)[o] = v;
     };
     const uint32_t mlo = lo & 0x7fffu, mhi = hi & 0x7fffu;
-    int rank_lo = 0, rank_hi = 0;
-#pragma unroll 8
-    for (int j = 0; j < 64; ++j) {
-        // coordinate j (lower half) against this lane's two coordinates
-        const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)mlo, j);
-        rank_lo += (a > mlo) | ((a == mlo) & (j < lane));
-        rank_hi += (a >= mhi);                       // j < lane + 64 always
-        // coordinate j + 64 (upper half)
-        const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)mhi, j);
-        rank_lo += (c > mlo);                        // j + 64 > lane always
-        rank_hi += (c > mhi) | ((c == mhi) & (j < lane));
+    // T = the k-th largest magnitude, found bit by bit from the top: the
+    // largest T with at least k magnitudes >= T (ballots and popcounts only)
+    uint32_t T = 0;
+#pragma unroll
+    for (int bit = 14; bit >= 0; --bit) {
+        const uint32_t c = T | (1u << bit);
+        if (__popcll(__ballot(mlo >= c)) + __popcll(__ballot(mhi >= c)) >= k) T = c;
     }
-    const bool keep_lo = rank_lo < k, keep_hi = rank_hi < k;
+    // rank of a coordinate = #(larger magnitudes) + #(equal magnitudes at
+    // smaller indices); it is < k for every magnitude above T and for the
+    // first k - #(above T) coordinates equal to T in index order (the lower
+    // half's indices precede the upper half's)
+    const int need = k - (__popcll(__ballot(mlo > T)) + __popcll(__ballot(mhi > T)));
+    const uint64_t eq_lo = __ballot(mlo == T), eq_hi = __ballot(mhi == T);
+    const uint64_t below = lanemask_lt(lane);
+    const bool keep_lo = mlo > T || (mlo == T && __popcll(eq_lo & below) < need);
+    const bool keep_hi = mhi > T || (mhi == T && __popcll(eq_lo) + __popcll(eq_hi & below) < need);
     const uint64_t blo = __ballot(keep_lo), bhi = __ballot(keep_hi);
-    const uint64_t lt = lanemask_lt(lane);
     if (keep_lo) {
-        const int o = __popcll(blo & lt);
+        const int o = __popcll(blo & below);
         idx_row[o] = (uint8_t)lane;
         put(o, lo);
     }
     if (keep_hi) {
-        const int o = __popcll(blo) + __popcll(bhi & lt);
+        const int o = __popcll(blo) + __popcll(bhi & below);
         idx_row[o] = (uint8_t)(lane + 64);
         put(o, hi);
     }
