@@ -144,6 +144,7 @@ class PagedPool:
         self._free = [int(x) for x in order[::-1]]  # pop() hands out order[0] first
         self.table = np.full((B, max_blocks), -1, np.int32)
         self.version = 0  # bumped whenever a table entry changes
+        self._dirty = []  # flat table slots changed since the last take_dirty()
 
     @property
     def free_blocks(self) -> int:
@@ -169,6 +170,7 @@ class PagedPool:
             raise ValueError(f"logical block {logical} of sequence {b} is already mapped")
         blk = self.alloc()
         self.table[b, logical] = blk
+        self._dirty.append(b * self.max_blocks + logical)
         self.version += 1
         return blk
 
@@ -183,6 +185,7 @@ class PagedPool:
                 raise ValueError(f"logical block {lb} of sequence {dst} is already mapped")
             self.table[dst, lb] = blk
             self.ref[blk] += 1
+            self._dirty.append(dst * self.max_blocks + lb)
         self.version += 1
 
     def prepare_write(self, b: int, row: int):
@@ -201,6 +204,7 @@ class PagedPool:
         new = self.alloc()  # may raise before anything changed
         self._decref(blk)
         self.table[b, lb] = new
+        self._dirty.append(b * self.max_blocks + lb)
         self.version += 1
         return blk, new
 
@@ -212,14 +216,22 @@ class PagedPool:
             if blk >= 0:
                 self._decref(blk)
                 self.table[b, lb] = -1
+                self._dirty.append(b * self.max_blocks + lb)
         self.version += 1
+
+    def take_dirty(self):
+        """(slot, block id) pairs of the table entries changed since the last
+        call, slot = b * max_blocks + logical block; clears the record."""
+        slots = np.unique(np.asarray(self._dirty, np.int64))
+        self._dirty = []
+        return np.stack([slots, self.table.reshape(-1)[slots]], axis=1).astype(np.int32)
 
 
 class PagedSwanDecoder(SwanDecoder):
     """SwanDecoder over a paged pool: before each step the rows the step will
-    append are made writable (block allocation or copy-on-write, copies
-    enqueued with swan_copy_blocks) and the block table is refreshed on the
-    device; then project -> append/evict -> decode as usual."""
+    append are made writable (block allocation or copy-on-write), and the
+    copies and changed table entries reach the device by value through
+    swan_paged_update; then project -> append/evict -> decode as usual."""
 
     def __init__(self, dims: S.swan_dims, P_qk: torch.Tensor, pool: PagedPool, rope_base: float = 10000.0,
                  device="cuda"):
@@ -230,6 +242,7 @@ class PagedSwanDecoder(SwanDecoder):
         self._bt_version = -1
         bt = torch.from_numpy(pool.table.copy()).to(device)
         super().__init__(dims, P_qk, rope_base, device, block_table=bt)
+        pool.take_dirty()  # the upload above holds every entry
         self._bt_version = pool.version
 
     def _to_device(self, arr, out=None):
@@ -242,10 +255,26 @@ class PagedSwanDecoder(SwanDecoder):
         out.copy_(staging, non_blocking=True)
         return out
 
-    def sync_table(self):
-        if self._bt_version != self.pool.version:
+    # above this many changed entries a whole-table upload is cheaper than
+    # entries carried in launch arguments (192 a launch)
+    FULL_UPLOAD_ENTRIES = 4096
+
+    def sync_table(self, copies=None, stream=None):
+        """Bring the device table up to the pool's and enqueue the copy-on-write
+        copies (host pairs (src, dst)).  Changed entries and copies travel in
+        the arguments of swan_paged_update launches, so the step waits on no
+        host-to-device copy; a table never uploaded, or with very many changes,
+        is uploaded whole."""
+        copies = np.zeros((0, 2), np.int32) if copies is None else np.asarray(copies, np.int32).reshape(-1, 2)
+        if self._bt_version == self.pool.version and len(copies) == 0:
+            return
+        entries = self.pool.take_dirty()
+        if self._bt_version < 0 or len(entries) > self.FULL_UPLOAD_ENTRIES:
             self._to_device(self.pool.table, self.cache.block_table)
-            self._bt_version = self.pool.version
+            entries = entries[:0]
+        if len(entries) or len(copies):
+            S.swan_paged_update(self.dims, self.cache.struct(), self.cache.block_table, entries, copies, stream)
+        self._bt_version = self.pool.version
 
     def prepare_step(self, pos_host, stream=None):
         """Host side of a step at positions pos_host[b]: returns the number of
@@ -262,10 +291,7 @@ class PagedSwanDecoder(SwanDecoder):
             cp = self.pool.prepare_write(b, row)
             if cp is not None:
                 pairs.append(cp)
-        if pairs:
-            ids = self._to_device(np.array(pairs, np.int32).T.copy())
-            S.swan_copy_blocks(self.dims, self.cache.struct(), ids[0], ids[1], stream)
-        self.sync_table()
+        self.sync_table(pairs, stream)
         return len(pairs)
 
     def step_paged(self, q, k, v_hat, pos, pos_host, stream=None):

@@ -424,4 +424,62 @@ swan_status swan_copy_blocks(const swan_dims *d, const swan_cache *c, const int3
     return hip_status(swan::launch_copy_blocks(a, (hipStream_t)stream), "swan_copy_blocks launch");
 }
 
+swan_status swan_paged_update(const swan_dims *d, const swan_cache *c, int32_t *block_table, const int32_t *entries,
+                              int32_t n_entries, const int32_t *copies, int32_t n_copies, void *stream)
+{
+    swan_status st = check_dims(d);
+    if (st) return st;
+    if (d->block_size <= 0) return fail(SWAN_ERR_INVALID_ARG, "swan_paged_update needs the paged layout (block_size > 0)");
+    if ((st = check_cache(d, c, false))) return st;
+    if (!block_table || block_table != c->block_table)
+        return fail(SWAN_ERR_INVALID_ARG, "block_table must be the table cache->block_table points at");
+    if (n_entries < 0 || n_copies < 0) return fail(SWAN_ERR_INVALID_ARG, "negative count");
+    if ((n_entries > 0 && !entries) || (n_copies > 0 && !copies)) return fail(SWAN_ERR_INVALID_ARG, "NULL pair array");
+    const int64_t n_slots = (int64_t)d->B * d->max_blocks;
+    for (int32_t i = 0; i < n_entries; ++i) {
+        const int32_t at = entries[2 * i], id = entries[2 * i + 1];
+        if (at < 0 || at >= n_slots || id < -1 || id >= d->num_blocks)
+            return fail(SWAN_ERR_INVALID_ARG, "entry %d = (%d, %d): slot outside [0, %lld) or block outside [-1, %d)", i,
+                        at, id, (long long)n_slots, d->num_blocks);
+    }
+    for (int32_t i = 0; i < n_copies; ++i) {
+        const int32_t src = copies[2 * i], dst = copies[2 * i + 1];
+        if (src < 0 || src >= d->num_blocks || dst < 0 || dst >= d->num_blocks || src == dst)
+            return fail(SWAN_ERR_INVALID_ARG, "copy %d = (%d, %d): ids outside [0, %d) or equal", i, src, dst,
+                        d->num_blocks);
+    }
+    if (n_copies > 0 && (((int64_t)d->H_kv * d->block_size * row_stride(d->k)) % 16 ||
+                         ((int64_t)d->H_kv * d->block_size * row_stride(kept_v(d))) % 16))
+        return fail(SWAN_ERR_UNSUPPORTED, "a block of an index plane (H_kv * block_size * k_stride bytes) must be a "
+                                          "multiple of 16 bytes");
+    swan::PagedUpdateArgs a;
+    a.num_blocks = d->num_blocks;
+    a.block_bytes_kidx = (int64_t)d->H_kv * d->block_size * row_stride(d->k);
+    a.block_bytes_vidx = (int64_t)d->H_kv * d->block_size * row_stride(kept_v(d));
+    a.vbytes = value_bytes(d);
+    a.kidx = c->k_idx;
+    a.vidx = c->v_idx;
+    a.kval = (uint8_t *)c->k_val;
+    a.vval = (uint8_t *)c->v_val;
+    a.table = block_table;
+    // as many launches as the pairs need; each carries its share by value
+    int32_t e = 0, k = 0;
+    while (e < n_entries || k < n_copies) {
+        a.n_entries = n_entries - e < swan::kUpdateEntries ? n_entries - e : swan::kUpdateEntries;
+        a.n_copies = n_copies - k < swan::kUpdateCopies ? n_copies - k : swan::kUpdateCopies;
+        for (int i = 0; i < a.n_entries; ++i) {
+            a.entry[i][0] = entries[2 * (e + i)];
+            a.entry[i][1] = entries[2 * (e + i) + 1];
+        }
+        for (int i = 0; i < a.n_copies; ++i) {
+            a.copy[i][0] = copies[2 * (k + i)];
+            a.copy[i][1] = copies[2 * (k + i) + 1];
+        }
+        if ((st = hip_status(swan::launch_paged_update(a, (hipStream_t)stream), "swan_paged_update launch"))) return st;
+        e += a.n_entries;
+        k += a.n_copies;
+    }
+    return SWAN_OK;
+}
+
 } // extern "C"

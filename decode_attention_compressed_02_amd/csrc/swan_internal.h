@@ -397,4 +397,20 @@ struct CopyBlocksArgs {
 };
 hipError_t launch_copy_blocks(const CopyBlocksArgs &a, hipStream_t s);
 
+// Block-table writes and copy-on-write copies of a paged step carried in the
+// launch's own arguments (no host-to-device copy on the stream): workgroup 0
+// writes the table entries, workgroup 1 + 4 i + p copies plane p of copy i.
+constexpr int kUpdateEntries = 192, kUpdateCopies = 32; // per launch
+struct PagedUpdateArgs {
+    int n_entries, n_copies, num_blocks;
+    int64_t block_bytes_kidx, block_bytes_vidx;
+    int vbytes;
+    uint8_t *kidx, *vidx;
+    uint8_t *kval, *vval;
+    int32_t *table;
+    int32_t entry[kUpdateEntries][2]; // (b * max_blocks + j, block id)
+    int32_t copy[kUpdateCopies][2];   // (src, dst)
+};
+hipError_t launch_paged_update(const PagedUpdateArgs &a, hipStream_t s);
+
 } // namespace swan

@@ -19,7 +19,7 @@ SWAN_OK, SWAN_ERR_INVALID_ARG, SWAN_ERR_UNSUPPORTED, SWAN_ERR_CAPACITY, SWAN_ERR
 EXPORTS = ("swan_status_str", "swan_last_error", "swan_row_stride", "swan_cache_bytes", "swan_project_qk",
            "swan_append_evict", "swan_decode_workspace_bytes", "swan_decode_num_splits", "swan_decode_attn",
            "swan_decode_split", "swan_decode_reduce", "swan_prefill_convert", "swan_copy_blocks",
-           "swan_project_append")
+           "swan_project_append", "swan_paged_update")
 
 
 class SwanError(RuntimeError):
@@ -68,6 +68,7 @@ def lib():
             "swan_decode_reduce": ([D, V, I32, V, SZ, V, V], C.c_int),
             "swan_prefill_convert": ([D, Cc, V, I32, I64, V, V, V, F, V], C.c_int),
             "swan_copy_blocks": ([D, Cc, V, V, I32, V], C.c_int),
+            "swan_paged_update": ([D, Cc, V, V, I32, V, I32, V], C.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -193,3 +194,22 @@ def swan_copy_blocks(dims, cache, src, dst, stream=None):
         raise ValueError("src and dst must have the same length")
     _check(lib().swan_copy_blocks(C.byref(dims), C.byref(cache), _ptr(src, torch.int32, "src"),
                                   _ptr(dst, torch.int32, "dst"), int(src.numel()), _stream(stream)))
+
+
+def _host_pairs(a, what):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1, 2)) if a is not None else np.zeros((0, 2), np.int32)
+    if a.ndim != 2 or a.shape[1] != 2:
+        raise ValueError(f"{what} must be pairs")
+    return a
+
+
+def swan_paged_update(dims, cache, block_table, entries=None, copies=None, stream=None):
+    """Block-table writes (entries: host pairs (b * max_blocks + j, id)) and
+    copy-on-write copies (copies: host pairs (src, dst)) carried by value in
+    the launch arguments; block_table is the cache's device table."""
+    import torch
+    e, c = _host_pairs(entries, "entries"), _host_pairs(copies, "copies")
+    _check(lib().swan_paged_update(C.byref(dims), C.byref(cache), _ptr(block_table, torch.int32, "block_table"),
+                                   e.ctypes.data_as(C.c_void_p), int(e.shape[0]), c.ctypes.data_as(C.c_void_p),
+                                   int(c.shape[0]), _stream(stream)))

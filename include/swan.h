@@ -264,6 +264,29 @@ swan_status swan_prefill_convert(const swan_dims *dims, const swan_cache *cache,
 swan_status swan_copy_blocks(const swan_dims *dims, const swan_cache *cache, const int32_t *src, const int32_t *dst,
                              int32_t count, void *stream);
 
+/*
+ * The host side of a paged step handed to the device by value: block-table
+ * writes and copy-on-write copies (the bookkeeping of "Reuse, Evict, or
+ * Limit Earlier Context" sections 1.2-1.4) carried in the arguments of the
+ * launch itself, so the step enqueues no host-to-device copy.
+ *   block_table  int32 [B][max_blocks] (device): must be cache->block_table
+ *   entries      int32 [n_entries][2] (host): (b * max_blocks + j, id) sets
+ *                block_table[b][j] = id, id in -1..num_blocks-1
+ *   copies       int32 [n_copies][2] (host): (src, dst) block pairs, copied
+ *                in all four sparse planes as by swan_copy_blocks
+ * The host arrays are read before the call returns (any number of pairs;
+ * the library splits them over launches of up to 192 entries and 32
+ * copies).  Entries and copies are independent: a copy moves pool bytes, an
+ * entry changes which block a sequence maps.  Later work on the stream sees
+ * both.  Errors: INVALID_ARG for a contiguous layout, a table other than the
+ * cache's, negative counts, NULL arrays with a positive count, an entry or a
+ * pair outside the pool (nothing is launched then); UNSUPPORTED as for
+ * swan_copy_blocks.
+ */
+swan_status swan_paged_update(const swan_dims *dims, const swan_cache *cache, int32_t *block_table,
+                              const int32_t *entries, int32_t n_entries, const int32_t *copies, int32_t n_copies,
+                              void *stream);
+
 #ifdef __cplusplus
 }
 #endif

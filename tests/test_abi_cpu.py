@@ -186,6 +186,12 @@ def pa(d, c=cache, max_pos=50, **kw):
     a = dict(q=F, k=F, vh=F, pos=F, P=F, base=10000.0, qh=F, kh=F); a.update(kw)
     return L.swan_project_append(C.byref(d), C.byref(c), a['q'], a['k'], a['vh'], a['pos'], max_pos, a['P'],
                                  a['base'], a['qh'], a['kh'], st)
+pcache = S.swan_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x2000)
+pdims = lambda: dims(block_size=16, max_blocks=4, num_blocks=8)  # B 2: table slots 0..7
+def pairs(*xs):
+    return (C.c_int32 * max(1, len(xs)))(*xs)
+def upd(d, c=pcache, table=0x2000, entries=pairs(0, 3), ne=1, copies=pairs(1, 2), nc=1):
+    return L.swan_paged_update(C.byref(d), C.byref(c), C.c_void_p(table) if table else None, entries, ne, copies, nc, st)
 def pre(d, c=cache, max_len=40, T=64, **kw):
     a = dict(len=F, kr=F, vh=F, P=F); a.update(kw)
     return L.swan_prefill_convert(C.byref(d), C.byref(c), a['len'], max_len, T, a['kr'], a['vh'], a['P'], 10000.0, st)
@@ -241,6 +247,21 @@ cases = [
     ("copy blocks odd block bytes", L.swan_copy_blocks(C.byref(dims(H_kv=1, N_h=1, k=8, block_size=1, max_blocks=4, num_blocks=8)),
                                                        C.byref(S.swan_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)),
                                                        F, F, 1, st), U),
+]
+cases += [
+    ("paged update contiguous", upd(dims(), c=cache), E),
+    ("paged update other table", upd(pdims(), table=0x3000), E),
+    ("paged update null table", upd(pdims(), table=0), E),
+    ("paged update slot past the table", upd(pdims(), entries=pairs(8, 3)), E),
+    ("paged update negative slot", upd(pdims(), entries=pairs(-1, 3)), E),
+    ("paged update block past the pool", upd(pdims(), entries=pairs(0, 8)), E),
+    ("paged update block -2", upd(pdims(), entries=pairs(0, -2)), E),
+    ("paged update copy onto itself", upd(pdims(), copies=pairs(2, 2)), E),
+    ("paged update copy past the pool", upd(pdims(), copies=pairs(1, 9)), E),
+    ("paged update negative count", upd(pdims(), ne=-1), E),
+    ("paged update null entries", upd(pdims(), entries=None, ne=2), E),
+    ("paged update null copies", upd(pdims(), copies=None, nc=1), E),
+    ("paged update odd block bytes", upd(dims(H_kv=1, N_h=1, k=8, block_size=1, max_blocks=4, num_blocks=8)), U),
 ]
 bad = [(n, got, want) for n, got, want in cases if got != want]
 for n, got, want in bad: print("MISMATCH", n, got, want)

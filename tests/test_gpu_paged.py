@@ -60,6 +60,41 @@ def test_copy_blocks_moves_whole_blocks(vf):
         np.testing.assert_array_equal(got.view(np.uint8), want.view(np.uint8))
 
 
+@pytest.mark.parametrize("vf", [0, 1])
+def test_paged_update_by_value(vf):
+    """swan_paged_update: table entries and copies carried in launch arguments
+    give the same table and planes as a table upload plus swan_copy_blocks;
+    300 entries and 40 copies take two launches."""
+    B, N, H, bs, k, mb, nb = 4, 4, 2, 16, 32, 100, 96
+    dims = S.make_dims(B, N, H, 16, k, block_size=bs, max_blocks=mb, num_blocks=nb, value_format=vf)
+    from decode_attention_compressed_02_amd.cache import HybridCache
+    r = np.random.default_rng(1)
+    table0 = r.integers(-1, nb, size=(B, mb)).astype(np.int32)
+    bt = cuda(table0)
+    cache = HybridCache(dims, "cuda", bt)
+    planes = cache.sparse_views()
+    host = []
+    for p in planes:
+        h = (r.integers(0, 128, size=tuple(p.shape), dtype=np.uint8) if p.dtype == torch.uint8
+             else r.standard_normal(tuple(p.shape)).astype(np.float16))
+        p.copy_(torch.from_numpy(h))
+        host.append(h)
+    slots = r.choice(B * mb, size=300, replace=False)
+    entries = np.stack([slots, r.integers(-1, nb, size=300)], axis=1).astype(np.int32)
+    ids = r.permutation(nb)
+    copies = np.stack([ids[:40], ids[40:80]], axis=1).astype(np.int32)  # disjoint sources and targets
+    S.swan_paged_update(dims, cache.struct(), bt, entries, copies)
+    torch.cuda.synchronize()
+    want_t = table0.reshape(-1).copy()
+    want_t[entries[:, 0]] = entries[:, 1]
+    np.testing.assert_array_equal(bt.cpu().numpy().reshape(-1), want_t)
+    for p, h in zip(planes, host):
+        want = h.copy()
+        for a, b in copies:
+            want[b] = h[a]
+        np.testing.assert_array_equal(p.cpu().numpy().view(np.uint8), want.view(np.uint8))
+
+
 def build_pool(w, prefix_blocks, slack=8):
     rows = [max(0, w.history_len(b) - w.R) for b in range(w.B)]
     return shared_prefix_pool(w.B, rows, w.steps, w.block_size, prefix_blocks * w.block_size,

@@ -105,3 +105,27 @@ def test_exhaustion_leaves_state_unchanged():
 def test_pool_order_must_be_permutation():
     with pytest.raises(ValueError):
         PagedPool(num_blocks=4, B=1, max_blocks=2, block_size=16, order=[0, 1, 1, 3])
+
+
+def test_changed_entries_are_recorded():
+    """take_dirty() replays every table change since the last call: applied
+    to a copy of the table as it was, it gives the table as it is."""
+    pool = PagedPool(num_blocks=16, B=3, max_blocks=4, block_size=16)
+    for lb in range(2):
+        pool.map_new(0, lb)
+    pool.share(0, 1, 2)
+    pool.take_dirty()
+    before = pool.table.copy()
+    pool.prepare_write(1, 5)        # copy-on-write of a shared block
+    pool.prepare_write(2, 40)       # a fresh block
+    assert pool.prepare_write(1, 6) is None  # already owned: no change
+    pool.release(0)
+    e = pool.take_dirty()
+    assert e.dtype == np.int32 and e.shape[1] == 2
+    assert len(np.unique(e[:, 0])) == len(e)
+    replay = before.reshape(-1).copy()
+    replay[e[:, 0]] = e[:, 1]
+    np.testing.assert_array_equal(replay.reshape(pool.table.shape), pool.table)
+    changed = np.flatnonzero(before.reshape(-1) != pool.table.reshape(-1))
+    assert set(changed) <= set(e[:, 0].tolist())
+    assert len(pool.take_dirty()) == 0
