@@ -85,6 +85,8 @@ def main():
     ap.add_argument("--kv-share", type=float, default=0.0,
                     help="keys keep this share of the workload's k + k coordinates and values the rest "
                          "(e.g. 0.6: TopK_R 0.6 / TopV_R 0.4 of the same budget); 0 = equal")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as HIP graph replays (one captured graph per step's inputs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle stepping time of the sample")
@@ -167,9 +169,20 @@ def main():
     restore()
     torch.cuda.synchronize()
 
+    graphs = None
+    if args.graph:  # capturing records the launches and runs nothing: the state is unchanged
+        from decode_attention_compressed_02_amd.cache import StepGraph
+        graphs = [StepGraph(dec, *inputs[s][:4], max_pos=max_pos_all) for s in range(args.steps)]
+        torch.cuda.synchronize()
+
     t0 = time.perf_counter()
     for s in range(args.steps):
-        run_step(inputs[s], ph=pos_host[s])
+        if graphs is None:
+            run_step(inputs[s], ph=pos_host[s])
+        else:
+            if paged:  # host bookkeeping stays eager; its table writes travel by value
+                dec.prepare_step(pos_host[s])
+            graphs[s].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
@@ -250,7 +263,8 @@ def main():
                    "d_h": w.d_h, "ctx_first_step": int(w.ctx[0]), "R": w.R, "k": w.k, "k_v": w.k_v or w.k,
                    "storage": f"{'fp8 E4M3' if w.value_format else 'fp16'} values, uint8 indices, fp16 dense buffer",
                    "split_waves": nsplit,
-                   "split_tokens": dec.dims.split_tokens or "auto"},
+                   "split_tokens": dec.dims.split_tokens or "auto",
+                   "launch": "HIP graph per step" if args.graph else "eager"},
         "step_hbm_GBps": float(np.mean(dec_bytes)) / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": float(np.mean(dec_bytes)) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "split_kernel_ms_in_step": split_avg_ms,

@@ -119,6 +119,35 @@ class SwanDecoder:
         return self.decode(pos, max_pos, stream)
 
 
+class StepGraph:
+    """One decode step of `dec` (swan_project_append, then swan_decode_attn)
+    captured as a HIP graph over fixed device buffers: replay() reissues the
+    step's launches with one call and no per-launch host work.
+
+    Before each replay the caller writes the step's inputs into the buffers
+    given at capture (.q, .k, .v_hat, .pos); the output is dec.o_hat.  The
+    launches keep the arguments of the capture, including the work plan and
+    workspace sized for positions up to max_pos: every replayed position must
+    stay within max_pos and the cache's capacity (the host checks ran once,
+    at capture).  A paged decoder's host bookkeeping (prepare_step) runs
+    eagerly before each replay; it writes the device table by value, so the
+    graph sees the new blocks.  Nothing in the captured launches allocates
+    or clears memory."""
+
+    def __init__(self, dec: "SwanDecoder", q, k, v_hat, pos, max_pos: int):
+        self.dec, self.q, self.k, self.v_hat, self.pos, self.max_pos = dec, q, k, v_hat, pos, int(max_pos)
+        dec.ensure_workspace(self.max_pos)  # outside the capture: the replays never allocate
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            dec.project_append(q, k, v_hat, pos, self.max_pos)
+            dec.decode(pos, self.max_pos)
+
+    def replay(self) -> torch.Tensor:
+        self.graph.replay()
+        return self.dec.o_hat
+
+
 class PoolExhausted(RuntimeError):
     """The paged pool has no free block left."""
 
@@ -222,6 +251,8 @@ class PagedPool:
     def take_dirty(self):
         """(slot, block id) pairs of the table entries changed since the last
         call, slot = b * max_blocks + logical block; clears the record."""
+        if not self._dirty:
+            return np.zeros((0, 2), np.int32)
         slots = np.unique(np.asarray(self._dirty, np.int64))
         self._dirty = []
         return np.stack([slots, self.table.reshape(-1)[slots]], axis=1).astype(np.int32)
@@ -279,16 +310,17 @@ class PagedSwanDecoder(SwanDecoder):
     def prepare_step(self, pos_host, stream=None):
         """Host side of a step at positions pos_host[b]: returns the number of
         copy-on-write block copies enqueued."""
-        R = self.dims.R
+        R, pool = self.dims.R, self.pool
+        rows = np.asarray(pos_host, np.int64) - R
+        rows = np.where(rows < 0, -1, rows)
+        # most steps write into blocks the sequence already owns alone: only the
+        # others (unmapped, shared, or past the table) go through prepare_write
+        lb = np.where(rows >= 0, rows // pool.block_size, 0)
+        blk = pool.table[np.arange(len(rows)), np.minimum(lb, pool.max_blocks - 1)]
+        todo = (rows >= 0) & ((lb >= pool.max_blocks) | (blk < 0) | (pool.ref[np.maximum(blk, 0)] != 1))
         pairs = []
-        for b, p in enumerate(pos_host):
-            p = int(p)
-            if p < 0:
-                continue
-            row = p - R if R > 0 else p
-            if row < 0:
-                continue
-            cp = self.pool.prepare_write(b, row)
+        for b in np.flatnonzero(todo):
+            cp = pool.prepare_write(int(b), int(rows[b]))
             if cp is not None:
                 pairs.append(cp)
         self.sync_table(pairs, stream)
