@@ -28,7 +28,9 @@
 // address: no LDS atomics (floating-point LDS atomics are an order of
 // magnitude slower than plain accesses on gfx950).  Lane l serves slot
 // l % TPI; with TPI = 16 the 16 lanes of each 128-bit LDS phase fall in 16
-// different bank quads, so the scatter has no bank conflicts.  Partial sums
+// different bank quads, so the scatter has no bank conflicts.  (With TPI = 8
+// the two lanes of a slot in a phase can meet in a quad; a padded layout that
+// avoids it needs 2 KB more LDS per wave and measured slower.)  Partial sums
 // over the lanes of a row use DPP and the gfx950 permlane swaps, not LDS.
 //
 // Scores are in base-2 units (q_hat pre-scaled by log2(e)/sqrt(d_h)).  The
@@ -405,12 +407,14 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
     // them (there the depth is that of fp16 rows of the wider width)
     constexpr bool kTwoWaves = split_waves_per_simd(G, KSM) == 2;
     constexpr int D = split_depth(kTwoWaves ? 3 * 2 * (E > EV ? E : EV) : (1 + VB) * (E + EV));
-    constexpr int NACC = TPI * kD * G;
+    constexpr int CS = TPI * G; // accumulator floats per coordinate
+    constexpr int NACC = kD * CS;
     static_assert(LPT * E == KS && LPT * EV == KSV && E >= 1 && EV >= 1 && E <= 16 && EV <= 16, "bad split shape");
     static_assert(split_lds_bytes(G, KSM) == 4 * (kD * G + NACC), "host and device disagree on LDS size");
-    // g = 4 with 16 row slots keeps sparse scores transposed, one (row slot,
-    // head) per lane; otherwise every lane of a row slot holds all g scores
-    constexpr bool kT = (G == 4 && TPI == 16);
+    // g = 4 keeps sparse scores transposed, one (row slot, head) per lane (with
+    // 8 row slots each pair sits in two lanes); otherwise every lane of a row
+    // slot holds all g scores
+    constexpr bool kT = (G == 4 && (TPI == 16 || TPI == 8));
 
     __shared__ __attribute__((aligned(16))) float qs[kD * G];
     __shared__ __attribute__((aligned(16))) float acc[NACC];
@@ -570,7 +574,7 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
                     }
                 if (tl == 0) { // lanes 0..15 own coordinates c0..c0+7 of slot 0 (still zero)
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) lds_put<G>(acc + (c0 + i) * TPI * G, ar[i]);
+                    for (int i = 0; i < 8; ++i) lds_put<G>(acc + (c0 + i) * CS, ar[i]);
                 }
                 __syncthreads();
             }
@@ -582,7 +586,7 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
             // the V slots.  Slots are reloaded as soon as they are consumed.
             if (t0 < t1) {
                 const int tl = lane % TPI, sub = lane / TPI;
-                float *my_acc = acc + tl * G; // coordinate c of this slot: my_acc[c * TPI * G]
+                float *my_acc = acc + tl * G; // coordinate c of this slot: my_acc[c * CS]
                 const uint8_t *kidx = a.kidx, *vidx = a.vidx;
                 const uint8_t *kval = a.kval, *vval = a.vval; // VB bytes per entry
                 if constexpr (!PAGED) { // per-unit base in scalar registers, 32-bit lane offsets
@@ -703,6 +707,10 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
                 }
                 auto reduce_scores = [&](float (&sk)[G], bool valid, float (&out)[G]) {
                     if constexpr (kT) {
+                        if constexpr (TPI == 8) { // the two lanes of a slot in each 16-lane row
+#pragma unroll
+                            for (int hh = 0; hh < G; ++hh) sk[hh] += dpp<0x128>(sk[hh]);
+                        }
                         const float t = transposed_sum4(sk[0], sk[1], sk[2], sk[3]);
                         out[0] = valid ? t : -INFINITY;
                     } else {
@@ -811,10 +819,10 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
                         float *vaddr[EV];
 #pragma unroll
                         for (int e = 0; e < EV; ++e) {
-                            if constexpr (TPI * G * 4 == 256) // 16 slots x 4 heads: one v_perm per address
+                            if constexpr (CS * 4 == 256) // 16 slots x 4 heads: one v_perm per address
                                 vaddr[e] = (float *)((char *)acc + acc_offset_256(vs.vi, e, (uint32_t)(tl * G * 4)));
                             else
-                                vaddr[e] = my_acc + byte_at(vs.vi, e) * (TPI * G);
+                                vaddr[e] = my_acc + byte_at(vs.vi, e) * CS;
                         }
 #pragma unroll
                         for (int e = 0; e < EV; ++e) lds_get<G>(vaddr[e], o[e]);
@@ -868,10 +876,11 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
                 }
                 if constexpr (kT) {
                     // back to per-head registers: a row holds one head; its 16 lanes
-                    // hold the weight sums of the 16 row slots (once each)
+                    // hold the weight sums of the row slots (16 slots once each, or 8
+                    // slots twice each: halved, exactly)
                     float mh[4], lh[4];
                     transposed_broadcast4(m_me, mh);
-                    transposed_broadcast4(group_sum<16>(ls_me), lh);
+                    transposed_broadcast4(group_sum<16>(ls_me) * (TPI == 8 ? 0.5f : 1.0f), lh);
 #pragma unroll
                     for (int hh = 0; hh < G; ++hh) {
                         m[hh] = mh[hh];
@@ -900,10 +909,10 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
                 // so the 16 lanes of an LDS phase read 16 different bank quads
                 const int c = lane + half * kWave;
                 float o[G], t[G];
-                lds_get<G>(acc + (c * TPI + lane % TPI) * G, o);
+                lds_get<G>(acc + c * CS + (lane % TPI) * G, o);
 #pragma unroll
                 for (int cp = 1; cp < TPI; ++cp) {
-                    lds_get<G>(acc + (c * TPI + (lane + cp) % TPI) * G, t);
+                    lds_get<G>(acc + c * CS + ((lane + cp) % TPI) * G, t);
 #pragma unroll
                     for (int hh = 0; hh < G; ++hh) o[hh] += t[hh];
                 }
