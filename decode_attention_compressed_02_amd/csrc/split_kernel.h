@@ -619,33 +619,41 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
                 // block table one row at a time.
                 const uint32_t lane_off = (uint32_t)(tl * KS + sub * E);     // key planes
                 const uint32_t lane_off_v = (uint32_t)(tl * KSV + sub * EV); // value planes
-                // Paged pools whose blocks hold a multiple of TPI rows: the TPI rows
-                // of a ring slot start at a multiple of TPI (t0 and TPS are multiples
-                // of 64), so they lie in one block, whose id is wave-uniform and
-                // comes through the scalar cache.  The slot then reads through a
-                // buffer resource on that block like the contiguous layout.  Other
-                // block sizes look the block up per row.
-                const bool slot_blocks = PAGED && a.geom.bs % TPI == 0;
-                // Paged: the row slot of the ring slot at r0 and the number of its rows
-                // to read; rows past t1 read nothing (zeros) and are masked by row,
-                // rows of a block outside the pool read nothing and clear ok.
-                auto slot_base = [&](int r0, uint32_t &rows, bool &ok) -> int64_t {
-                    ok = true;
-                    rows = 0;
-                    if (r0 >= t1) return 0; // past the piece: the table may end here
-                    const int blk = a.geom.bt[(int64_t)b * a.geom.max_blocks + r0 / a.geom.bs];
-                    if (blk < 0 || blk >= a.geom.num_blocks) {
-                        ok = false;
-                        return 0;
-                    }
-                    rows = (uint32_t)min(t1 - r0, TPI);
-                    return ((int64_t)blk * a.H + h) * a.geom.bs + r0 % a.geom.bs;
+                // Paged pools whose blocks hold a power-of-two multiple of TPI rows:
+                // the TPI rows of a ring slot start at a multiple of TPI (t0 is a
+                // multiple of 16, passes of D x TPI rows), so they lie in one block, whose id is
+                // wave-uniform and comes through the scalar cache.  The slot then
+                // reads through a buffer resource on that block like the contiguous
+                // layout.  The ids of a pass's slots are fetched together at the top
+                // of the pass (one wait for all of them), used by the key loads and
+                // kept in scalar registers for the value loads of the next pass.
+                // Other block sizes look the block up per row.
+                const bool slot_blocks =
+                    PAGED && a.geom.bs % TPI == 0 && (a.geom.bs & (a.geom.bs - 1)) == 0;
+                const int bsh = PAGED ? __builtin_ctz((unsigned)a.geom.bs) : 0; // log2 of the block size
+                const int64_t tab = PAGED ? (int64_t)b * a.geom.max_blocks : 0;  // the sequence's table row
+                const int64_t blk_rows = PAGED ? (int64_t)a.H * a.geom.bs : 0;   // row slots of one block
+                const int64_t h_rows = PAGED ? (int64_t)h * a.geom.bs : 0;       // this head's rows in a block
+                // block id of the ring slot at row r0: -1 past the piece (the table may
+                // end there; the slot reads nothing), -2 an entry that is not a block of
+                // the pool (the slot reads nothing and its rows are dropped)
+                auto slot_block = [&](int r0) -> int {
+                    if (!PAGED || !slot_blocks || r0 >= t1) return -1;
+                    const int blk = a.geom.bt[tab + (r0 >> bsh)];
+                    return (blk >= 0 && blk < a.geom.num_blocks) ? blk : -2;
+                };
+                // row slot of the ring slot at r0 in block blk and the number of its rows
+                // to read (rows past t1 read zeros and are masked by row)
+                auto slot_base = [&](int r0, int blk, uint32_t &rows) -> int64_t {
+                    rows = blk >= 0 ? (uint32_t)min(t1 - r0, TPI) : 0u;
+                    return blk >= 0 ? (int64_t)blk * blk_rows + h_rows + (r0 & (a.geom.bs - 1)) : 0;
                 };
                 // Ring slot d of the pass starting at row rp.  Contiguous rows: one
                 // buffer resource per plane and pass, covering rows rp .. t1-1 (the
                 // rest read as zeros), and slot d at a constant offset from it, so
                 // the per-slot address work is an immediate offset.
-                auto load_k = [&](int rp, int d, KSlot<E, VB> &st) {
+                // (blk: the slot's block id from slot_block, paged pools only)
+                auto load_k = [&](int rp, int d, KSlot<E, VB> &st, int blk) {
                     const int r0 = rp + d * TPI;
                     if (PAGED && !slot_blocks) {
                         const int64_t o = (int64_t)slice(r0, st.ok) * KS + sub * E;
@@ -653,7 +661,8 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
                         load_words<VB * E>(kval + o * VB, st.kv);
                     } else if constexpr (PAGED) {
                         uint32_t rows;
-                        const int64_t base = slot_base(r0, rows, st.ok) * KS;
+                        st.ok = blk != -2;
+                        const int64_t base = slot_base(r0, blk, rows) * KS;
                         buffer_words<E>(buffer_rsrc(kidx + base, rows * KS), lane_off, st.ki);
                         buffer_words<VB * E>(buffer_rsrc(kval + base * VB, rows * KS * VB), VB * lane_off, st.kv);
                     } else {
@@ -663,7 +672,7 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
                         buffer_words<VB * E>(buffer_rsrc(kval + (int64_t)rp * KS * VB, rows * KS * VB), VB * off, st.kv);
                     }
                 };
-                auto load_v = [&](int rp, int d, VSlot<EV, VB> &st) {
+                auto load_v = [&](int rp, int d, VSlot<EV, VB> &st, int blk) {
                     const int r0 = rp + d * TPI;
                     if (PAGED && !slot_blocks) {
                         bool ok;
@@ -672,8 +681,7 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
                         load_words<VB * EV>(vval + o * VB, st.vv);
                     } else if constexpr (PAGED) {
                         uint32_t rows;
-                        bool ok;
-                        const int64_t base = slot_base(r0, rows, ok) * KSV;
+                        const int64_t base = slot_base(r0, blk, rows) * KSV;
                         buffer_words<EV>(buffer_rsrc(vidx + base, rows * KSV), lane_off_v, st.vi);
                         buffer_words<VB * EV>(buffer_rsrc(vval + base * VB, rows * KSV * VB), VB * lane_off_v, st.vv);
                     } else {
@@ -738,14 +746,22 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
                     }
                     reduce_scores(s, valid, sc);
                 };
+                // block ids of paged ring slots: bk for the pass whose keys were
+                // loaded last (its values load next), bn for the one after
+                int bk[D], bn[D];
 #pragma unroll
                 for (int d = 0; d < D; ++d) {
-                    load_k(t0, d, rk[d]);
+                    bk[d] = slot_block(t0 + d * TPI);
+                    bn[d] = slot_block(t0 + P + d * TPI);
+                }
+#pragma unroll
+                for (int d = 0; d < D; ++d) {
+                    load_k(t0, d, rk[d], bk[d]);
                     __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
                 }
 #pragma unroll
                 for (int d = 0; d < D; ++d) {
-                    load_v(t0, d, rv[d]);
+                    load_v(t0, d, rv[d], bk[d]);
                     __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
                 }
                 float sc[D][G];
@@ -753,11 +769,15 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
                 for (int d = 0; d < D; ++d) {
                     score(t0 + d * TPI, rk[d], sc[d]);
                     __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-                    load_k(t0 + P, d, rk[d]);
+                    load_k(t0 + P, d, rk[d], bn[d]);
                     __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
                 }
+#pragma unroll
+                for (int d = 0; d < D; ++d) bk[d] = bn[d];
 
                 for (int rb = t0; rb < t1; rb += P) {
+#pragma unroll
+                    for (int d = 0; d < D; ++d) bn[d] = slot_block(rb + 2 * P + d * TPI); // keys loaded this pass
                     // rescale test for pass rb (wave-uniform, rare)
                     float dm = -INFINITY;
 #pragma unroll
@@ -864,15 +884,17 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
                         }
                         reduce_scores(sk, valid, sn[d]);
                         __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-                        load_k(rb + 2 * P, d, rk[d]);
+                        load_k(rb + 2 * P, d, rk[d], bn[d]);
                         __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
-                        load_v(rb + P, d, rv[d]);
+                        load_v(rb + P, d, rv[d], bk[d]);
                         __builtin_amdgcn_sched_barrier(kKeepLoadOrder);
                     }
 #pragma unroll
-                    for (int d = 0; d < D; ++d)
+                    for (int d = 0; d < D; ++d) {
+                        bk[d] = bn[d];
 #pragma unroll
                         for (int hh = 0; hh < G; ++hh) sc[d][hh] = sn[d][hh];
+                    }
                 }
                 if constexpr (kT) {
                     // back to per-head registers: a row holds one head; its 16 lanes

@@ -275,6 +275,20 @@ DECODE_CASES = {
 @pytest.mark.parametrize("name", sorted(DECODE_CASES))
 @pytest.mark.parametrize("paged", [False, True])
 def test_decode_attn(name, paged):
+    _decode_case(name, 16 if paged else 0)
+
+
+# Block sizes other than 16: 8 is smaller than a 16-row ring slot (rows looked
+# up one at a time), 32 holds several slots (one block id per slot), 48 is a
+# multiple of 16 that is not a power of two (looked up per row).
+@pytest.mark.parametrize("name", ["g4_k32_many_splits", "g4_k64_outliers", "fp8_g8_k16"])
+@pytest.mark.parametrize("bs", [8, 32, 48])
+def test_decode_attn_block_sizes(name, bs):
+    _decode_case(name, bs)
+
+
+def _decode_case(name, bs):
+    paged = bs > 0
     B, N, H, R, k, ctx, split, extra = DECODE_CASES[name]
     w = wl.Workload(name, B, N, H, R, k, ctx, seed=zlib.crc32(name.encode()) % 1000, **extra)
     oc, K, V, Ts = oracle_state(w, ncap=max(w.n_cap(), 1))
@@ -287,7 +301,6 @@ def test_decode_attn(name, paged):
     want = oc.decode(q32.astype(np.float64), pos.astype(np.int64))
     bt, kw = None, {}
     if paged:
-        bs = 16
         mb = (oc.ncap + bs - 1) // bs
         nb = B * mb + 5
         bt = rng(3).permutation(nb)[:B * mb].reshape(B, mb).astype(np.int32)
@@ -297,7 +310,7 @@ def test_decode_attn(name, paged):
     dec.q_hat.copy_(cuda(q32))
     out = dec.decode(cuda(pos), int(pos.max())).cpu().numpy()
     err = rel_l2_max(out, want)
-    print(f"[{name} paged={paged}] splits={S.swan_decode_num_splits(dec.dims, int(pos.max()))} rel_l2={err:.2e}")
+    print(f"[{name} block_size={bs}] splits={S.swan_decode_num_splits(dec.dims, int(pos.max()))} rel_l2={err:.2e}")
     assert err < TOL
     # run-to-run determinism (fixed split and merge order)
     out2 = dec.decode(cuda(pos), int(pos.max())).cpu().numpy()
