@@ -393,7 +393,10 @@ __host__ __device__ constexpr int split_depth(int slice_bytes)
     return d < 2 ? 2 : (d > 8 ? 8 : d);
 }
 
-template <int G, int KS, int KSV, bool PAGED, bool PAD, int VB>
+// SLOTS (paged pools only): every ring slot of TPI rows lies in one block
+// (the block size is a power-of-two multiple of TPI, paged_slot_blocks);
+// otherwise paged rows are looked up one at a time
+template <int G, int KS, int KSV, bool PAGED, bool PAD, int VB, bool SLOTS>
 __global__ __launch_bounds__(64)
 __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV)))) void k_split(SplitArgs a)
 {
@@ -628,8 +631,7 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
                 // of the pass (one wait for all of them), used by the key loads and
                 // kept in scalar registers for the value loads of the next pass.
                 // Other block sizes look the block up per row.
-                const bool slot_blocks =
-                    PAGED && a.geom.bs % TPI == 0 && (a.geom.bs & (a.geom.bs - 1)) == 0;
+                constexpr bool slot_blocks = PAGED && SLOTS;
                 const int bsh = PAGED ? __builtin_ctz((unsigned)a.geom.bs) : 0; // log2 of the block size
                 const int64_t tab = PAGED ? (int64_t)b * a.geom.max_blocks : 0;  // the sequence's table row
                 const int64_t blk_rows = PAGED ? (int64_t)a.H * a.geom.bs : 0;   // row slots of one block
@@ -951,44 +953,44 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
 // launchers
 // ---------------------------------------------------------------------------
 
-template <int G, int KS, int KSV, bool PAGED, int VB>
+template <int G, int KS, int KSV, bool PAGED, int VB, bool SLOTS>
 inline void launch_split_v(const SplitArgs &a, hipStream_t s)
 {
     const dim3 grid(a.W), block(kWave);
     if (a.k_v < KSV)
-        hipLaunchKernelGGL((k_split<G, KS, KSV, PAGED, true, VB>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_split<G, KS, KSV, PAGED, true, VB, SLOTS>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((k_split<G, KS, KSV, PAGED, false, VB>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_split<G, KS, KSV, PAGED, false, VB, SLOTS>), grid, block, 0, s, a);
 }
 
-template <int G, int KS, int KSV, bool PAGED>
+template <int G, int KS, int KSV, bool PAGED, bool SLOTS>
 inline void launch_split_k(const SplitArgs &a, hipStream_t s)
 {
     if (a.geom.vbytes == 1)
-        launch_split_v<G, KS, KSV, PAGED, 1>(a, s);
+        launch_split_v<G, KS, KSV, PAGED, 1, SLOTS>(a, s);
     else
-        launch_split_v<G, KS, KSV, PAGED, 2>(a, s);
+        launch_split_v<G, KS, KSV, PAGED, 2, SLOTS>(a, s);
 }
 
 // key row width x value row width: equal, or one twice the other
-template <int G, bool PAGED>
+template <int G, bool PAGED, bool SLOTS = false>
 inline hipError_t launch_split_g(const SplitArgs &a, hipStream_t s)
 {
     const int ks = a.geom.ks, ksv = a.geom.ks_v;
     switch (ks * 1000 + ksv) {
-    case 8008: launch_split_k<G, 8, 8, PAGED>(a, s); break;
-    case 8016: launch_split_k<G, 8, 16, PAGED>(a, s); break;
-    case 16008: launch_split_k<G, 16, 8, PAGED>(a, s); break;
-    case 16016: launch_split_k<G, 16, 16, PAGED>(a, s); break;
-    case 16032: launch_split_k<G, 16, 32, PAGED>(a, s); break;
-    case 32016: launch_split_k<G, 32, 16, PAGED>(a, s); break;
-    case 32032: launch_split_k<G, 32, 32, PAGED>(a, s); break;
-    case 32064: launch_split_k<G, 32, 64, PAGED>(a, s); break;
-    case 64032: launch_split_k<G, 64, 32, PAGED>(a, s); break;
-    case 64064: launch_split_k<G, 64, 64, PAGED>(a, s); break;
-    case 64128: launch_split_k<G, 64, 128, PAGED>(a, s); break;
-    case 128064: launch_split_k<G, 128, 64, PAGED>(a, s); break;
-    case 128128: launch_split_k<G, 128, 128, PAGED>(a, s); break;
+    case 8008: launch_split_k<G, 8, 8, PAGED, SLOTS>(a, s); break;
+    case 8016: launch_split_k<G, 8, 16, PAGED, SLOTS>(a, s); break;
+    case 16008: launch_split_k<G, 16, 8, PAGED, SLOTS>(a, s); break;
+    case 16016: launch_split_k<G, 16, 16, PAGED, SLOTS>(a, s); break;
+    case 16032: launch_split_k<G, 16, 32, PAGED, SLOTS>(a, s); break;
+    case 32016: launch_split_k<G, 32, 16, PAGED, SLOTS>(a, s); break;
+    case 32032: launch_split_k<G, 32, 32, PAGED, SLOTS>(a, s); break;
+    case 32064: launch_split_k<G, 32, 64, PAGED, SLOTS>(a, s); break;
+    case 64032: launch_split_k<G, 64, 32, PAGED, SLOTS>(a, s); break;
+    case 64064: launch_split_k<G, 64, 64, PAGED, SLOTS>(a, s); break;
+    case 64128: launch_split_k<G, 64, 128, PAGED, SLOTS>(a, s); break;
+    case 128064: launch_split_k<G, 128, 64, PAGED, SLOTS>(a, s); break;
+    case 128128: launch_split_k<G, 128, 128, PAGED, SLOTS>(a, s); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -364,6 +364,18 @@ hipError_t launch_split_g1_paged(const SplitArgs &a, hipStream_t s);
 hipError_t launch_split_g2_paged(const SplitArgs &a, hipStream_t s);
 hipError_t launch_split_g4_paged(const SplitArgs &a, hipStream_t s);
 hipError_t launch_split_g8_paged(const SplitArgs &a, hipStream_t s);
+hipError_t launch_split_g1_paged_rows(const SplitArgs &a, hipStream_t s);
+hipError_t launch_split_g2_paged_rows(const SplitArgs &a, hipStream_t s);
+hipError_t launch_split_g4_paged_rows(const SplitArgs &a, hipStream_t s);
+hipError_t launch_split_g8_paged_rows(const SplitArgs &a, hipStream_t s);
+// Paged pools whose blocks hold a power-of-two multiple of the split pass's
+// ring-slot rows read each slot through one block (its id through the scalar
+// cache); other block sizes look the block up per row (the _rows kernels).
+inline bool paged_slot_blocks(int G, const SparseGeom &g)
+{
+    const int tpi = split_slots(G, g.ks > g.ks_v ? g.ks : g.ks_v);
+    return g.bs > 0 && g.bs % tpi == 0 && (g.bs & (g.bs - 1)) == 0;
+}
 
 struct ReduceArgs {
     int B, N_h, H, R, W, split_tokens, row_bytes, row_cap;
