@@ -90,6 +90,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle stepping time of the sample")
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="split launches timed one at a time after a 1 GiB cache-evicting fill (median); 0 = skip")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run plain device copies of this size (for calibrating HBM byte counters)")
     args = ap.parse_args()
@@ -226,6 +228,29 @@ def main():
     # bytes of the last step's launch over the back-to-back duration
     achieved = float(split_bytes[-1]) / (split_b2b_ms * 1e-3) / 1e9
 
+    # the split kernel from a cold last-level cache: before every other one of
+    # these launches a 1 GiB fill evicts the L2s and the 256 MB MALL, so a
+    # cache that fits the MALL (e.g. 202 MB) is streamed from HBM; events
+    # bracket the launch only, and the launches without the fill give the
+    # warm figure of the same protocol
+    split_cold_ms = split_single_ms = None
+    if args.cold_reps > 0:
+        pos, mp = inputs[args.steps - 1][3:5]
+        flush = torch.empty(2 ** 30, dtype=torch.uint8, device="cuda")
+        times = {True: [], False: []}
+        for i in range(2 * args.cold_reps):
+            evict = i % 2 == 0
+            if evict:
+                flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            S.swan_decode_split(dec.dims, dec.cache.struct(), pos, mp, dec.q_hat, dec.workspace)
+            b.record(stream)
+            torch.cuda.synchronize()
+            times[evict].append(a.elapsed_time(b))
+        del flush
+        split_cold_ms, split_single_ms = float(np.median(times[True])), float(np.median(times[False]))
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         from decode_attention_compressed_02_amd.profiling import kernel_source_hash
@@ -269,6 +294,9 @@ def main():
         "step_frac_of_peak": float(np.mean(dec_bytes)) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "split_kernel_ms_in_step": split_avg_ms,
         "split_kernel_ms_back_to_back": split_b2b_ms,
+        "split_kernel_ms_single_launch": split_single_ms,
+        "split_kernel_ms_cold_cache": split_cold_ms,
+        "split_cold_cache_GBps": (float(split_bytes[-1]) / (split_cold_ms * 1e-3) / 1e9) if split_cold_ms else None,
         "decode_gflops_per_step": float(np.mean(flops)) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
