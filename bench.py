@@ -34,11 +34,12 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, seqs: list[int], seconds: float, max_steps: int = 4096):
+def cpu_baseline(w, seqs: list[int], seconds: float, max_steps: int = 4096, threads: int | None = None):
     """The float64 oracle on a sample of the workload: the chosen sequences,
     all kv heads, consecutive decode steps from the workload's first step
-    until about `seconds` of stepping (prefill excluded).  Returns (KV
-    tokens/s, threads, seconds, sample description)."""
+    until about `seconds` of stepping (prefill excluded), on `threads` host
+    threads (default: all).  Returns (KV tokens/s, threads, seconds, sample
+    description)."""
     import oracle
     from decode_attention_compressed_02_amd import workloads as wl
 
@@ -51,7 +52,7 @@ def cpu_baseline(w, seqs: list[int], seconds: float, max_steps: int = 4096):
         kb, vb = wl.history(w, b)
         K[i, :, :kb.shape[1]], V[i, :, :vb.shape[1]] = kb, vb
     P = wl.projection_qk(w).astype(np.float64)
-    threads = oracle.default_threads()
+    threads = threads or oracle.default_threads()
     t0 = time.time()
     oc.prefill(K, V, np.array([sub.history_len(b) for b in range(sub.B)], np.int64), P, w.rope_base, threads)
     log(f"oracle prefill of the sample in {time.time() - t0:.1f}s")
@@ -292,6 +293,7 @@ def main():
                    "launch": "HIP graph per step" if args.graph else "eager"},
         "step_hbm_GBps": float(np.mean(dec_bytes)) / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": float(np.mean(dec_bytes)) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "head_tokens_per_s": value * w.H_kv,
         "split_kernel_ms_in_step": split_avg_ms,
         "split_kernel_ms_back_to_back": split_b2b_ms,
         "split_kernel_ms_single_launch": split_single_ms,
@@ -308,6 +310,10 @@ def main():
         v, cores, secs, desc = cpu_baseline(w, seqs, args.cpu_seconds)
         result["cpu_baseline"] = {"value": v, "unit": "KV tokens/s", "cores": cores, "kind": "oracle",
                                   "sample": desc, "seconds": secs}
+        # the same oracle on one thread, over one sequence (all kv heads)
+        v1, _, secs1, desc1 = cpu_baseline(w, seqs[:1], args.cpu_seconds / 4, threads=1)
+        result["cpu_baseline_1_thread"] = {"value": v1, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+                                           "sample": desc1, "seconds": secs1}
     print(json.dumps(result), flush=True)
 
 
