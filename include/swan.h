@@ -58,6 +58,9 @@
  *     v_idx, v_val  [num_blocks][H_kv][block_size][v_stride]
  *     block_table   int32   [B][max_blocks]: sparse row t of sequence b is
  *                   slot t % block_size of block block_table[b][t / block_size]
+ *     Any block_size >= 1 works.  Powers of two >= 16 are the fast path:
+ *     the decode reads each run of 8 or 16 rows through one block; other
+ *     sizes look the block up for every row.
  *   dense buffer:
  *     k_buf, v_buf  fp16    [B][H_kv][R][128], slot = position mod R
  * Every plane must be 16-byte aligned.
