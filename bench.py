@@ -9,8 +9,9 @@ stored basis, random orthogonal P_QK); the initial hybrid cache is built on
 the GPU from a 32767-token history with swan_prefill_convert.
 
 A timed step is the whole hot path: swan_project_append (projection and
-append/evict in one launch) -> swan_decode_split -> swan_decode_reduce, all
-inputs already resident in HBM.
+append/evict in one launch; on a paged pool swan_project_append_paged, which
+also carries the step's block-table writes and copy-on-write copies) ->
+swan_decode_split -> swan_decode_reduce, all inputs already resident in HBM.
 Prints one JSON line (rank 0).
 """
 from __future__ import annotations
@@ -143,9 +144,10 @@ def main():
 
     def run_step(x, ev=None, ph=None):
         q, kr, vn, pos, mp = x
-        if paged:  # host bookkeeping + copy-on-write copies + table refresh
-            dec.prepare_step(ph)
-        dec.project_append(q, kr, vn, pos, mp)
+        if paged:  # host bookkeeping, then table update + projection + append in one launch
+            dec.project_append_paged(q, kr, vn, pos, ph)
+        else:
+            dec.project_append(q, kr, vn, pos, mp)
         if ev is not None:
             ev[0].record(stream)
         S.swan_decode_split(dec.dims, dec.cache.struct(), pos, mp, dec.q_hat, dec.workspace)

@@ -307,9 +307,10 @@ class PagedSwanDecoder(SwanDecoder):
             S.swan_paged_update(self.dims, self.cache.struct(), self.cache.block_table, entries, copies, stream)
         self._bt_version = self.pool.version
 
-    def prepare_step(self, pos_host, stream=None):
-        """Host side of a step at positions pos_host[b]: returns the number of
-        copy-on-write block copies enqueued."""
+    def _make_writable(self, pos_host):
+        """Host bookkeeping of a step at positions pos_host[b]: the sparse row
+        each sequence writes (-1: none) and the copy-on-write copies it needs,
+        as (src, dst, row within the block)."""
         R, pool = self.dims.R, self.pool
         rows = np.asarray(pos_host, np.int64) - R
         rows = np.where(rows < 0, -1, rows)
@@ -318,17 +319,48 @@ class PagedSwanDecoder(SwanDecoder):
         lb = np.where(rows >= 0, rows // pool.block_size, 0)
         blk = pool.table[np.arange(len(rows)), np.minimum(lb, pool.max_blocks - 1)]
         todo = (rows >= 0) & ((lb >= pool.max_blocks) | (blk < 0) | (pool.ref[np.maximum(blk, 0)] != 1))
-        pairs = []
+        copies = []
         for b in np.flatnonzero(todo):
             cp = pool.prepare_write(int(b), int(rows[b]))
             if cp is not None:
-                pairs.append(cp)
-        self.sync_table(pairs, stream)
-        return len(pairs)
+                copies.append((cp[0], cp[1], int(rows[b]) % pool.block_size))
+        return rows, copies
+
+    def prepare_step(self, pos_host, stream=None):
+        """Host side of a step at positions pos_host[b], its copies and table
+        entries enqueued by swan_paged_update: returns the number of
+        copy-on-write block copies."""
+        _, copies = self._make_writable(pos_host)
+        self.sync_table([c[:2] for c in copies], stream)
+        return len(copies)
+
+    def project_append_paged(self, q, k, v_hat, pos, pos_host, stream=None):
+        """Host bookkeeping of a step, then its projection, append/evict and
+        table update in one launch (swan_project_append_paged).  Takes the
+        two-launch path (swan_paged_update, then swan_project_append) when
+        the device table was never uploaded or has too many changes, or when
+        a copy's source block is one this step appends into in place.  Returns
+        the number of copy-on-write block copies."""
+        rows, copies = self._make_writable(pos_host)
+        pool, max_pos = self.pool, int(max(pos_host))
+        w = np.flatnonzero(rows >= 0)
+        lb = np.minimum(rows[w] // pool.block_size, pool.max_blocks - 1)
+        appended = set(pool.table[w, lb].tolist())
+        if (self._bt_version < 0 or len(pool._dirty) > self.FULL_UPLOAD_ENTRIES
+                or any(c[0] in appended for c in copies)):
+            self.sync_table([c[:2] for c in copies], stream)
+            self.project_append(q, k, v_hat, pos, max_pos, stream)
+            return len(copies)
+        entries = pool.take_dirty()
+        S.swan_project_append_paged(self.dims, self.cache.struct(), q, k, v_hat, pos, max_pos, self.P_qk,
+                                    self.rope_base, self.q_hat, self.k_hat, self.cache.block_table, entries,
+                                    np.asarray(copies, np.int32).reshape(-1, 3), stream)
+        self._bt_version = pool.version
+        return len(copies)
 
     def step_paged(self, q, k, v_hat, pos, pos_host, stream=None):
-        self.prepare_step(pos_host, stream)
-        return self.step(q, k, v_hat, pos, int(max(pos_host)), stream)
+        self.project_append_paged(q, k, v_hat, pos, pos_host, stream)
+        return self.decode(pos, int(max(pos_host)), stream)
 
 
 def shared_prefix_pool(B: int, rows, steps: int, block_size: int, prefix_rows: int, order_fn, slack: int = 0):

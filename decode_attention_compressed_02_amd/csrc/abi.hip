@@ -5,6 +5,8 @@
 
 #include "swan_internal.h"
 
+#include <vector>
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -268,6 +270,86 @@ swan_status swan_project_append(const swan_dims *d, const swan_cache *c, const f
     a.k_hat = k_hat;
     a.v_hat = v_hat;
     return hip_status(swan::launch_project_append(p, a, (hipStream_t)stream), "swan_project_append launch");
+}
+
+swan_status swan_project_append_paged(const swan_dims *d, const swan_cache *c, const float *q, const float *k,
+                                      const float *v_hat, const int32_t *pos, int32_t max_pos, const float *P_qk,
+                                      float rope_base, float *q_hat, uint16_t *k_hat, int32_t *block_table,
+                                      const int32_t *entries, int32_t n_entries, const int32_t *copies,
+                                      int32_t n_copies, void *stream)
+{
+    swan_status st = check_dims(d);
+    if (st) return st;
+    if (d->block_size <= 0)
+        return fail(SWAN_ERR_INVALID_ARG, "swan_project_append_paged needs the paged layout (block_size > 0)");
+    if ((st = check_cache(d, c, true))) return st;
+    if (!block_table || block_table != c->block_table)
+        return fail(SWAN_ERR_INVALID_ARG, "block_table must be the table cache->block_table points at");
+    if (n_entries < 0 || n_copies < 0) return fail(SWAN_ERR_INVALID_ARG, "negative count");
+    if ((n_entries > 0 && !entries) || (n_copies > 0 && !copies)) return fail(SWAN_ERR_INVALID_ARG, "NULL pair array");
+    const int64_t n_slots = (int64_t)d->B * d->max_blocks;
+    for (int32_t i = 0; i < n_entries; ++i) {
+        const int32_t at = entries[2 * i], id = entries[2 * i + 1];
+        if (at < 0 || at >= n_slots || id < -1 || id >= d->num_blocks)
+            return fail(SWAN_ERR_INVALID_ARG, "entry %d = (%d, %d): slot outside [0, %lld) or block outside [-1, %d)", i,
+                        at, id, (long long)n_slots, d->num_blocks);
+        for (int32_t j = 0; j < i; ++j)
+            if (entries[2 * j] == at) return fail(SWAN_ERR_INVALID_ARG, "entries %d and %d write the same slot %d", j, i, at);
+    }
+    for (int32_t i = 0; i < n_copies; ++i) {
+        const int32_t src = copies[3 * i], dst = copies[3 * i + 1], skip = copies[3 * i + 2];
+        if (src < 0 || src >= d->num_blocks || dst < 0 || dst >= d->num_blocks || src == dst)
+            return fail(SWAN_ERR_INVALID_ARG, "copy %d = (%d, %d): ids outside [0, %d) or equal", i, src, dst,
+                        d->num_blocks);
+        if (skip < -1 || skip >= d->block_size)
+            return fail(SWAN_ERR_INVALID_ARG, "copy %d: skip row %d outside [-1, %d)", i, skip, d->block_size);
+    }
+    if (n_entries > swan::kFusedEntries || n_copies > swan::kFusedCopies) {
+        // more than one launch carries: the table update first, then the step's
+        // projection and append (same results, one more launch)
+        std::vector<int32_t> pairs((size_t)2 * n_copies);
+        for (int32_t i = 0; i < n_copies; ++i) {
+            pairs[2 * i] = copies[3 * i];
+            pairs[2 * i + 1] = copies[3 * i + 1];
+        }
+        if ((st = swan_paged_update(d, c, block_table, entries, n_entries, pairs.data(), n_copies, stream))) return st;
+        return swan_project_append(d, c, q, k, v_hat, pos, max_pos, P_qk, rope_base, q_hat, k_hat, stream);
+    }
+    if (!q || !k || !v_hat || !pos || !P_qk || !q_hat || !k_hat) return fail(SWAN_ERR_INVALID_ARG, "NULL array argument");
+    if (!(rope_base > 1.0f)) return fail(SWAN_ERR_INVALID_ARG, "rope_base must be > 1");
+    const int64_t row = d->R > 0 ? (int64_t)max_pos - d->R : (int64_t)max_pos;
+    if (row >= row_cap(d))
+        return fail(SWAN_ERR_CAPACITY, "max_pos = %d writes sparse row %lld, capacity is %lld", max_pos,
+                    (long long)row, (long long)row_cap(d));
+    swan::ProjectArgs p{d->B, d->N_h, d->H_kv, q, k, pos, P_qk, rope_base, q_hat, k_hat};
+    swan::AppendArgs a;
+    a.B = d->B;
+    a.H = d->H_kv;
+    a.R = d->R;
+    a.k = d->k;
+    a.k_v = kept_v(d);
+    a.geom = geom(d, c);
+    a.kidx = c->k_idx;
+    a.vidx = c->v_idx;
+    a.kval = (uint8_t *)c->k_val;
+    a.vval = (uint8_t *)c->v_val;
+    a.kbuf = c->k_buf;
+    a.vbuf = c->v_buf;
+    a.pos = pos;
+    a.k_hat = k_hat;
+    a.v_hat = v_hat;
+    swan::StepUpdateArgs u;
+    u.n_entries = n_entries;
+    u.n_copies = n_copies;
+    u.table = block_table;
+    for (int32_t i = 0; i < n_entries; ++i) {
+        u.entry[i][0] = entries[2 * i];
+        u.entry[i][1] = entries[2 * i + 1];
+    }
+    for (int32_t i = 0; i < n_copies; ++i)
+        for (int t = 0; t < 3; ++t) u.copy[i][t] = copies[3 * i + t];
+    return hip_status(swan::launch_project_append_paged(p, a, u, (hipStream_t)stream),
+                      "swan_project_append_paged launch");
 }
 
 size_t swan_decode_workspace_bytes(const swan_dims *d, int32_t max_pos)

@@ -30,10 +30,12 @@ constexpr int kProjRows = kD / (kProjThreads / kD); // rows of P per thread grou
 // oldest key while the rotation angles are computed; only the new key's
 // placement waits for the projection.  Every load that depends on no other
 // (raw vectors, rows of P_QK, the old buffer entries) is issued at the start.
+// (blk: the block of the unit's appended row when the launch carries it,
+// kTableBlock to read the block table)
 template <int G, bool APPEND>
-__global__ __launch_bounds__(kProjThreads) void k_project(ProjectArgs a, AppendArgs ap)
+__device__ __forceinline__ void project_unit(const ProjectArgs &a, const AppendArgs &ap, int h, int b, int blk)
 {
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int tid = threadIdx.x;
     const int j = tid % kD, quarter = tid / kD, wave = tid / kWave, lane = tid % kWave;
     constexpr int kWaves = kProjThreads / kWave;
     __shared__ double xs[G + 1][kD];
@@ -65,9 +67,9 @@ __global__ __launch_bounds__(kProjThreads) void k_project(ProjectArgs a, AppendA
     if constexpr (APPEND) {
         if (wave == kWaves - 1) {
             const int64_t u = (int64_t)b * ap.H + h;
-            append_token(ap, b, h, 1, lane, f2h(ap.v_hat[u * kD + lane]), f2h(ap.v_hat[u * kD + lane + 64]));
+            append_token(ap, b, h, 1, lane, f2h(ap.v_hat[u * kD + lane]), f2h(ap.v_hat[u * kD + lane + 64]), blk);
         } else if (wave == kWaves - 2) {
-            evict_token(ap, b, h, 0, lane);
+            evict_token(ap, b, h, 0, lane, blk);
         }
     }
     if (tid < kD / 2) {
@@ -118,7 +120,73 @@ __global__ __launch_bounds__(kProjThreads) void k_project(ProjectArgs a, AppendA
     }
     if constexpr (APPEND) {
         __syncthreads();
-        if (wave == 0) place_token(ap, b, h, 0, lane, khs[lane], khs[lane + 64]);
+        if (wave == 0) place_token(ap, b, h, 0, lane, khs[lane], khs[lane + 64], blk);
+    }
+}
+
+template <int G, bool APPEND>
+__global__ __launch_bounds__(kProjThreads) void k_project(ProjectArgs a, AppendArgs ap)
+{
+    project_unit<G, APPEND>(a, ap, blockIdx.x, blockIdx.y, kTableBlock);
+}
+
+// ---------------------------------------------------------------------------
+// a paged step's projection, append and block-table update in one launch
+// ---------------------------------------------------------------------------
+
+// Block that sequence b's append writes this step, from the launch's table
+// entries (the last entry for the row's table slot), or kTableBlock when the
+// entries do not touch that slot (the table then holds it and this launch
+// does not write it).  Every thread of the workgroup gets the same answer.
+__device__ int step_append_block(const StepUpdateArgs &u, const AppendArgs &ap, int b, int *shared_hit)
+{
+    const int p = ap.pos[b];
+    const int r = ap.R > 0 ? p - ap.R : p; // sparse row written this step
+    const int64_t slot = r >= 0 && r / ap.geom.bs < ap.geom.max_blocks
+                             ? (int64_t)b * ap.geom.max_blocks + r / ap.geom.bs
+                             : -1;
+    if (threadIdx.x == 0) *shared_hit = -1;
+    __syncthreads();
+    if (p >= 0 && slot >= 0 && (int)threadIdx.x < u.n_entries && u.entry[threadIdx.x][0] == slot)
+        atomicMax(shared_hit, (int)threadIdx.x);
+    __syncthreads();
+    const int hit = *shared_hit;
+    return hit >= 0 ? u.entry[hit][1] : kTableBlock;
+}
+
+// plane 0 / 1: key / value indices, 2 / 3: key / value values.  Blocks are
+// [H][bs][row] per plane; row `skip` of every head is left alone (-1: none).
+__device__ void copy_plane_skip(const AppendArgs &ap, int plane, int src, int dst, int skip)
+{
+    const SparseGeom &g = ap.geom;
+    uint8_t *const base[4] = {ap.kidx, ap.vidx, ap.kval, ap.vval};
+    const int entries = (plane & 1) ? g.ks_v : g.ks;
+    const int64_t row_bytes = (int64_t)entries * (plane < 2 ? 1 : g.vbytes); // a power of two >= 8
+    const int64_t bytes = (int64_t)g.H * g.bs * row_bytes;
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 *s = (const u32x2 *)(base[plane] + (int64_t)src * bytes);
+    u32x2 *d = (u32x2 *)(base[plane] + (int64_t)dst * bytes);
+    for (int64_t j = threadIdx.x; j < bytes / 8; j += kProjThreads)
+        if ((int)((j * 8 / row_bytes) % g.bs) != skip) d[j] = s[j];
+}
+
+// Workgroups 0 .. H B - 1: unit (h, b) = (i % H, i / H), projected and
+// appended; workgroup H B writes the table entries; H B + 1 + 4 c + p copies
+// plane p of copy c.
+template <int G>
+__global__ __launch_bounds__(kProjThreads) void k_project_paged(ProjectArgs a, AppendArgs ap, StepUpdateArgs u)
+{
+    __shared__ int hit;
+    const int units = a.H * a.B, i = blockIdx.x;
+    if (i < units) {
+        const int h = i % a.H, b = i / a.H;
+        const int blk = step_append_block(u, ap, b, &hit);
+        project_unit<G, true>(a, ap, h, b, blk);
+    } else if (i == units) {
+        for (int t = threadIdx.x; t < u.n_entries; t += kProjThreads) u.table[u.entry[t][0]] = u.entry[t][1];
+    } else {
+        const int c = (i - units - 1) / 4, plane = (i - units - 1) % 4;
+        copy_plane_skip(ap, plane, u.copy[c][0], u.copy[c][1], u.copy[c][2]);
     }
 }
 
@@ -141,6 +209,20 @@ hipError_t launch_project(const ProjectArgs &a, hipStream_t s) { return launch_g
 hipError_t launch_project_append(const ProjectArgs &p, const AppendArgs &a, hipStream_t s)
 {
     return launch_g<true>(p, a, s);
+}
+
+hipError_t launch_project_append_paged(const ProjectArgs &p, const AppendArgs &a, const StepUpdateArgs &u,
+                                       hipStream_t s)
+{
+    const dim3 grid(p.H * p.B + 1 + 4 * u.n_copies), block(kProjThreads);
+    switch (p.N_h / p.H) {
+    case 1: hipLaunchKernelGGL(k_project_paged<1>, grid, block, 0, s, p, a, u); break;
+    case 2: hipLaunchKernelGGL(k_project_paged<2>, grid, block, 0, s, p, a, u); break;
+    case 4: hipLaunchKernelGGL(k_project_paged<4>, grid, block, 0, s, p, a, u); break;
+    case 8: hipLaunchKernelGGL(k_project_paged<8>, grid, block, 0, s, p, a, u); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 } // namespace swan

@@ -119,6 +119,17 @@ __device__ __forceinline__ int64_t row_slot_rt(const SparseGeom &g, int b, int h
     return g.bs > 0 ? row_slot<true>(g, b, h, r) : row_slot<false>(g, b, h, r);
 }
 
+// Block of an appended row when the caller already knows it (a paged step
+// whose table entries travel in the same launch): kTableBlock means "read the
+// block table".
+constexpr int kTableBlock = -0x7fffffff;
+__device__ __forceinline__ int64_t append_row_slot(const SparseGeom &g, int b, int h, int r, int blk)
+{
+    if (blk == kTableBlock) return row_slot_rt(g, b, h, r);
+    if (blk < 0 || blk >= g.num_blocks) return -1;
+    return ((int64_t)blk * g.H + h) * g.bs + (r % g.bs);
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (lane == 0) ? 0ull : ((~0ull) >> (64 - lane)); }
 
 // Magnitude top-k of one 128-vector held by a full wave, two fp16 per lane
@@ -206,7 +217,7 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 // prunes the new token straight into row pos.  Inactive sequences (pos < 0)
 // append nothing.  The two parts must run in this order (the slot is read
 // before it is overwritten).
-__device__ inline void evict_token(const AppendArgs &a, int b, int h, int wave, int lane)
+__device__ inline void evict_token(const AppendArgs &a, int b, int h, int wave, int lane, int blk = kTableBlock)
 {
     const int p = a.pos[b];
     if (p < a.R || a.R == 0) return; // also p < 0
@@ -215,21 +226,22 @@ __device__ inline void evict_token(const AppendArgs &a, int b, int h, int wave, 
     const uint16_t olo = buf[lane], ohi = buf[lane + 64];
     const int r = p - a.R;
     const int row_cap = a.geom.bs > 0 ? a.geom.max_blocks * a.geom.bs : a.geom.n_cap;
-    const int64_t slot = r < row_cap ? row_slot_rt(a.geom, b, h, r) : -1;
+    const int64_t slot = r < row_cap ? append_row_slot(a.geom, b, h, r, blk) : -1;
     if (slot < 0) return;
     const int vb = a.geom.vbytes, kk = wave == 0 ? a.k : a.k_v, ks = wave == 0 ? a.geom.ks : a.geom.ks_v;
     wave_prune_row(lane, olo, ohi, kk, ks, (wave == 0 ? a.kidx : a.vidx) + slot * ks,
                    (wave == 0 ? a.kval : a.vval) + slot * ks * vb, vb);
 }
 
-__device__ inline void place_token(const AppendArgs &a, int b, int h, int wave, int lane, uint16_t lo, uint16_t hi)
+__device__ inline void place_token(const AppendArgs &a, int b, int h, int wave, int lane, uint16_t lo, uint16_t hi,
+                                   int blk = kTableBlock)
 {
     const int p = a.pos[b];
     if (p < 0) return;
     const int64_t u = (int64_t)b * a.H + h;
     if (a.R == 0) {
         const int row_cap = a.geom.bs > 0 ? a.geom.max_blocks * a.geom.bs : a.geom.n_cap;
-        const int64_t slot = p < row_cap ? row_slot_rt(a.geom, b, h, p) : -1;
+        const int64_t slot = p < row_cap ? append_row_slot(a.geom, b, h, p, blk) : -1;
         if (slot < 0) return;
         const int vb = a.geom.vbytes, kk = wave == 0 ? a.k : a.k_v, ks = wave == 0 ? a.geom.ks : a.geom.ks_v;
         wave_prune_row(lane, lo, hi, kk, ks, (wave == 0 ? a.kidx : a.vidx) + slot * ks,
@@ -241,15 +253,32 @@ __device__ inline void place_token(const AppendArgs &a, int b, int h, int wave, 
     buf[lane + 64] = hi;
 }
 
-__device__ inline void append_token(const AppendArgs &a, int b, int h, int wave, int lane, uint16_t lo, uint16_t hi)
+__device__ inline void append_token(const AppendArgs &a, int b, int h, int wave, int lane, uint16_t lo, uint16_t hi,
+                                    int blk = kTableBlock)
 {
-    evict_token(a, b, h, wave, lane);
-    place_token(a, b, h, wave, lane, lo, hi);
+    evict_token(a, b, h, wave, lane, blk);
+    place_token(a, b, h, wave, lane, lo, hi, blk);
 }
 
 // projection and append of a step in one launch (the append waits for the
 // unit's new key inside the workgroup, not for the whole grid)
 hipError_t launch_project_append(const ProjectArgs &p, const AppendArgs &a, hipStream_t s);
+
+// A paged step's block-table writes and copy-on-write copies carried by value
+// into the projection/append launch.  The appends take their rows' blocks
+// from these entries (so they never read a table entry the same launch
+// writes), and copy i skips row skip of every head of its destination: the
+// row this launch's append writes there.  No two workgroups then touch the
+// same bytes, so the launch needs no ordering inside it.
+constexpr int kFusedEntries = 192, kFusedCopies = 32;
+struct StepUpdateArgs {
+    int n_entries, n_copies;
+    int32_t *table;
+    int32_t entry[kFusedEntries][2]; // (b * max_blocks + j, block id); slots distinct
+    int32_t copy[kFusedCopies][3];   // (src, dst, skip row or -1)
+};
+hipError_t launch_project_append_paged(const ProjectArgs &p, const AppendArgs &a, const StepUpdateArgs &u,
+                                       hipStream_t s);
 
 // Shape of the sparse stream in the split kernel for GQA group G, stored key
 // rows of KS entries and value rows of KSV entries (KSmax the wider).  TPI

@@ -19,7 +19,7 @@ SWAN_OK, SWAN_ERR_INVALID_ARG, SWAN_ERR_UNSUPPORTED, SWAN_ERR_CAPACITY, SWAN_ERR
 EXPORTS = ("swan_status_str", "swan_last_error", "swan_row_stride", "swan_cache_bytes", "swan_project_qk",
            "swan_append_evict", "swan_decode_workspace_bytes", "swan_decode_num_splits", "swan_decode_attn",
            "swan_decode_split", "swan_decode_reduce", "swan_prefill_convert", "swan_copy_blocks",
-           "swan_project_append", "swan_paged_update")
+           "swan_project_append", "swan_paged_update", "swan_project_append_paged")
 
 
 class SwanError(RuntimeError):
@@ -69,6 +69,7 @@ def lib():
             "swan_prefill_convert": ([D, Cc, V, I32, I64, V, V, V, F, V], C.c_int),
             "swan_copy_blocks": ([D, Cc, V, V, I32, V], C.c_int),
             "swan_paged_update": ([D, Cc, V, V, I32, V, I32, V], C.c_int),
+            "swan_project_append_paged": ([D, Cc, V, V, V, V, I32, V, F, V, V, V, V, I32, V, I32, V], C.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -196,11 +197,12 @@ def swan_copy_blocks(dims, cache, src, dst, stream=None):
                                   _ptr(dst, torch.int32, "dst"), int(src.numel()), _stream(stream)))
 
 
-def _host_pairs(a, what):
+def _host_pairs(a, what, width=2):
     import numpy as np
-    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1, 2)) if a is not None else np.zeros((0, 2), np.int32)
-    if a.ndim != 2 or a.shape[1] != 2:
-        raise ValueError(f"{what} must be pairs")
+    a = (np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1, width)) if a is not None
+         else np.zeros((0, width), np.int32))
+    if a.ndim != 2 or a.shape[1] != width:
+        raise ValueError(f"{what} must be rows of {width}")
     return a
 
 
@@ -213,3 +215,20 @@ def swan_paged_update(dims, cache, block_table, entries=None, copies=None, strea
     _check(lib().swan_paged_update(C.byref(dims), C.byref(cache), _ptr(block_table, torch.int32, "block_table"),
                                    e.ctypes.data_as(C.c_void_p), int(e.shape[0]), c.ctypes.data_as(C.c_void_p),
                                    int(c.shape[0]), _stream(stream)))
+
+
+def swan_project_append_paged(dims, cache, q, k, v_hat, pos, max_pos, P_qk, rope_base, q_hat, k_hat, block_table,
+                              entries=None, copies=None, stream=None):
+    """Projection, append and the paged table update of a step in one launch:
+    entries are host pairs (b * max_blocks + j, id), copies host triples
+    (src, dst, skip row)."""
+    import torch
+    e, c = _host_pairs(entries, "entries"), _host_pairs(copies, "copies", 3)
+    _check(lib().swan_project_append_paged(C.byref(dims), C.byref(cache), _ptr(q, torch.float32, "q"),
+                                           _ptr(k, torch.float32, "k"), _ptr(v_hat, torch.float32, "v_hat"),
+                                           _ptr(pos, torch.int32, "pos"), int(max_pos),
+                                           _ptr(P_qk, torch.float32, "P_qk"), float(rope_base),
+                                           _ptr(q_hat, torch.float32, "q_hat"), _ptr(k_hat, torch.float16, "k_hat"),
+                                           _ptr(block_table, torch.int32, "block_table"),
+                                           e.ctypes.data_as(C.c_void_p), int(e.shape[0]), c.ctypes.data_as(C.c_void_p),
+                                           int(c.shape[0]), _stream(stream)))

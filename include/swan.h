@@ -290,6 +290,36 @@ swan_status swan_paged_update(const swan_dims *dims, const swan_cache *cache, in
                               const int32_t *entries, int32_t n_entries, const int32_t *copies, int32_t n_copies,
                               void *stream);
 
+/*
+ * A paged step's steps 1 and 2 and its table update in one launch (the
+ * projection and append of swan_project_append with the entries and copies
+ * of swan_paged_update; "Reuse, Evict, or Limit Earlier Context" sections
+ * 1.2-1.4 for the table, reference counts and copy-on-write).
+ *   block_table  int32 [B][max_blocks] (device): must be cache->block_table
+ *   entries      int32 [n_entries][2] (host): (b * max_blocks + j, id) sets
+ *                block_table[b][j] = id, id in -1..num_blocks-1; slots distinct
+ *   copies       int32 [n_copies][3] (host): (src, dst, skip) copies block src
+ *                to dst in all four sparse planes except row `skip` of every
+ *                head (0..block_size-1, or -1 for none), which is the row this
+ *                call's append writes into dst
+ * Each sequence's append takes the block of its sparse row from `entries`
+ * when they set that slot, else from the table, so the appends, the table
+ * writes and the copies run side by side in one launch.  The results are
+ * those of swan_paged_update (with full copies) followed by
+ * swan_project_append, provided no copy's source block is one an append of
+ * this call writes into (a caller precondition, as the exclusive ownership of
+ * appended blocks is: a block is copied only when it is shared, and shared
+ * blocks are not written).  Up to 192 entries and 32 copies travel in the one
+ * launch; more are handed to swan_paged_update first (one launch more, same
+ * results).  Errors: those of the two calls, INVALID_ARG for repeated slots
+ * or a skip row outside [-1, block_size).
+ */
+swan_status swan_project_append_paged(const swan_dims *dims, const swan_cache *cache, const float *q, const float *k,
+                                      const float *v_hat, const int32_t *pos, int32_t max_pos, const float *P_qk,
+                                      float rope_base, float *q_hat, uint16_t *k_hat, int32_t *block_table,
+                                      const int32_t *entries, int32_t n_entries, const int32_t *copies,
+                                      int32_t n_copies, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -192,6 +192,11 @@ def pairs(*xs):
     return (C.c_int32 * max(1, len(xs)))(*xs)
 def upd(d, c=pcache, table=0x2000, entries=pairs(0, 3), ne=1, copies=pairs(1, 2), nc=1):
     return L.swan_paged_update(C.byref(d), C.byref(c), C.c_void_p(table) if table else None, entries, ne, copies, nc, st)
+def pap(d, c=pcache, table=0x2000, entries=pairs(0, 3), ne=1, copies=pairs(1, 2, 0), nc=1, max_pos=50, **kw):
+    a = dict(q=F, k=F, vh=F, pos=F, P=F, base=10000.0, qh=F, kh=F); a.update(kw)
+    return L.swan_project_append_paged(C.byref(d), C.byref(c), a['q'], a['k'], a['vh'], a['pos'], max_pos, a['P'],
+                                       a['base'], a['qh'], a['kh'], C.c_void_p(table) if table else None, entries, ne,
+                                       copies, nc, st)
 def pre(d, c=cache, max_len=40, T=64, **kw):
     a = dict(len=F, kr=F, vh=F, P=F); a.update(kw)
     return L.swan_prefill_convert(C.byref(d), C.byref(c), a['len'], max_len, T, a['kr'], a['vh'], a['P'], 10000.0, st)
@@ -262,6 +267,18 @@ cases += [
     ("paged update null entries", upd(pdims(), entries=None, ne=2), E),
     ("paged update null copies", upd(pdims(), copies=None, nc=1), E),
     ("paged update odd block bytes", upd(dims(H_kv=1, N_h=1, k=8, block_size=1, max_blocks=4, num_blocks=8)), U),
+    ("paged step contiguous", pap(dims(), c=cache), E),
+    ("paged step other table", pap(pdims(), table=0x3000), E),
+    ("paged step repeated slot", pap(pdims(), entries=pairs(0, 3, 0, 4), ne=2), E),
+    ("paged step slot past the table", pap(pdims(), entries=pairs(8, 3)), E),
+    ("paged step skip row past the block", pap(pdims(), copies=pairs(1, 2, 16)), E),
+    ("paged step skip row -2", pap(pdims(), copies=pairs(1, 2, -2)), E),
+    ("paged step copy onto itself", pap(pdims(), copies=pairs(2, 2, 0)), E),
+    ("paged step negative count", pap(pdims(), nc=-1), E),
+    ("paged step null copies", pap(pdims(), copies=None, nc=1), E),
+    ("paged step null v_hat", pap(pdims(), vh=N), E),
+    ("paged step capacity", pap(pdims(), max_pos=16 * 4 + 16), CAP),
+    ("paged step g = 3", pap(dims(N_h=6, H_kv=2, block_size=16, max_blocks=4, num_blocks=8)), U),
 ]
 bad = [(n, got, want) for n, got, want in cases if got != want]
 for n, got, want in bad: print("MISMATCH", n, got, want)

@@ -101,8 +101,11 @@ def build_pool(w, prefix_blocks, slack=8):
                               lambda n: wl.pool_order(w, n), slack)
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("k,vf", [(64, 0), (40, 0), (64, 1)])
-def test_paged_pool_steps_with_copy_on_write(k, vf):
+def test_paged_pool_steps_with_copy_on_write(k, vf, fused):
+    # fused: the step's table writes and copies travel in the projection/append
+    # launch (swan_project_append_paged), copies skipping the appended row
     # prefix 96 tokens = 6 blocks of 16 rows; R = 16.  Sequence 1 (83 rows)
     # and 2 (95 rows) append into the shared block 5 (copy-on-write), 3 opens
     # block 6, 5 crosses into block 7 at its second step.
@@ -134,8 +137,12 @@ def test_paged_pool_steps_with_copy_on_write(k, vf):
         shared_before = np.flatnonzero(pool.ref > 1)
         snap = [p[torch.from_numpy(shared_before).long().cuda()].cpu().numpy().copy()
                 for p in dec.cache.sparse_views()]
-        copies.append(dec.prepare_step(pos))
-        out = dec.step(cuda(q), cuda(kr), cuda(vn), cuda(pos), int(pos.max())).cpu().numpy()
+        if fused:
+            copies.append(dec.project_append_paged(cuda(q), cuda(kr), cuda(vn), cuda(pos), pos))
+            out = dec.decode(cuda(pos), int(pos.max())).cpu().numpy()
+        else:
+            copies.append(dec.prepare_step(pos))
+            out = dec.step(cuda(q), cuda(kr), cuda(vn), cuda(pos), int(pos.max())).cpu().numpy()
         _, _, want = oc.step(q, kr, vn, pos.astype(np.int64), P.astype(np.float64), w.rope_base)
         err = rel_l2_max(out, want)
         print(f"[paged k={k}] step {s} cow={copies[-1]} rel_l2={err:.2e}")
@@ -150,6 +157,11 @@ def test_paged_pool_steps_with_copy_on_write(k, vf):
             np.testing.assert_array_equal(rows[0][b, :, r, :k], oc.kidx[b, :, r])
             np.testing.assert_array_equal(rows[2][b, :, r, :k], oc.vidx[b, :, r])
             assert_values_bits(rows[3][b, :, r, :k], oc.vval[b, :, r], vf)
+            # every row of the sequence, copied blocks included
+            np.testing.assert_array_equal(rows[0][b, :, :r + 1, :k], oc.kidx[b, :, :r + 1])
+            np.testing.assert_array_equal(rows[2][b, :, :r + 1, :k], oc.vidx[b, :, :r + 1])
+            assert_values_bits(rows[1][b, :, :r + 1, :k], oc.kval[b, :, :r + 1], vf)
+            assert_values_bits(rows[3][b, :, :r + 1, :k], oc.vval[b, :, :r + 1], vf)
     # copy-on-write happened exactly for sequences 1 and 2 at their first step
     assert copies == [2, 0, 0]
     assert (pool.ref[pool.table[0, :5]] == w.B).all() and pool.ref[pool.table[0, 5]] == w.B - 2
