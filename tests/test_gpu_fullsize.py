@@ -107,10 +107,11 @@ def test_full_size_steps(cfg):
     P64 = wl.projection_qk(w).astype(np.float64)
     for s in range(STEPS):
         q, kr, vn, pos = wl.step_inputs(w, s)
-        if w.block_size > 0:
-            dec.prepare_step(pos)
         cu = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (q, kr, vn, pos)]
-        out = dec.step(*cu, int(pos.max()))
+        if w.block_size > 0:  # the benchmark's paged step: table update, projection and append in one launch
+            out = dec.step_paged(*cu, pos)
+        else:
+            out = dec.step(*cu, int(pos.max()))
         _, _, want = oc.step(q[seqs], kr[seqs], vn[seqs], pos[seqs].astype(np.int64), P64, w.rope_base,
                              oracle.default_threads())
         got = out[seqs].cpu().numpy()
