@@ -51,13 +51,15 @@ def stats_table(path: str, top: int = 12) -> str:
     return "\n".join(out)
 
 
-def last_dispatches(trace_csv: str, kernel: str, last: int):
-    """(mean, min, max) duration in us of the last `last` dispatches of a
-    kernel in a rocprofv3 kernel_trace.csv (in start order)."""
+def last_dispatches(trace_csv: str, kernel: str, last: int, skip: int = 0):
+    """(mean, min, max) duration in us of `last` dispatches of a kernel in a
+    rocprofv3 kernel_trace.csv (in start order), ending `skip` dispatches
+    before the run's last one."""
     rows = [r for r in csv.DictReader(open(trace_csv)) if kernel in r["Kernel_Name"]]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    rows = rows[:len(rows) - skip] if skip else rows
     d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows[-last:]]
-    return statistics.mean(d), min(d), max(d), len(rows)
+    return statistics.mean(d), min(d), max(d), len(rows) + skip
 
 
 def _counter_values(path: str, counter: str):
@@ -110,6 +112,8 @@ def main(argv=None):
     l.add_argument("csv", help="kernel_trace.csv")
     l.add_argument("--kernel", default="k_split")
     l.add_argument("--n", type=int, default=36, help="dispatches at the end of the run (timed + back-to-back)")
+    l.add_argument("--skip", type=int, default=0,
+                   help="leave out this many dispatches at the very end (bench.py's single-launch timings)")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -121,8 +125,9 @@ def main(argv=None):
     if args.cmd == "stats":
         print(stats_table(args.csv, args.top))
     elif args.cmd == "last":
-        mean, lo, hi, total = last_dispatches(args.csv, args.kernel, args.n)
-        print(f"{args.kernel}: last {args.n} of {total} dispatches: mean {mean:.2f} us, min {lo:.2f}, max {hi:.2f}")
+        mean, lo, hi, total = last_dispatches(args.csv, args.kernel, args.n, args.skip)
+        where = f"last {args.n}" + (f" before the final {args.skip}" if args.skip else "")
+        print(f"{args.kernel}: {where} of {total} dispatches: mean {mean:.2f} us, min {lo:.2f}, max {hi:.2f}")
     else:
         res = traffic(args.fetch, args.write, args.kernel, args.copy_mib, args.workload)
         txt = json.dumps(res, indent=1)
