@@ -129,3 +129,55 @@ def test_changed_entries_are_recorded():
     changed = np.flatnonzero(before.reshape(-1) != pool.table.reshape(-1))
     assert set(changed) <= set(e[:, 0].tolist())
     assert len(pool.take_dirty()) == 0
+
+
+def _recording_paged_decoder(monkeypatch):
+    """A PagedSwanDecoder on host tensors whose binding calls are recorded
+    instead of launched: two sequences sharing block 0 of the pool's order,
+    R = 4, 16-row blocks."""
+    import torch
+    from decode_attention_compressed_02_amd import swan as S
+    from decode_attention_compressed_02_amd.cache import PagedSwanDecoder
+    calls = []
+    monkeypatch.setattr(S, "swan_project_append_paged",
+                        lambda *a, **k: calls.append(("one launch", np.asarray(a[12]), np.asarray(a[13]))))
+    monkeypatch.setattr(S, "swan_paged_update",
+                        lambda dims, cache, table, entries, copies, stream=None: calls.append(
+                            ("table update", np.asarray(entries), np.asarray(copies))))
+    monkeypatch.setattr(S, "swan_project_append", lambda *a, **k: calls.append(("project+append",)))
+    pool = PagedPool(num_blocks=8, B=2, max_blocks=4, block_size=16, order=np.arange(8))
+    shared = pool.map_new(0, 0)
+    pool.share(0, 1, 1)
+    dims = S.make_dims(2, 2, 1, 4, 8, block_size=16, max_blocks=4, num_blocks=8)
+    dec = PagedSwanDecoder(dims, torch.zeros((1, 128, 128)), pool, device="cpu")
+    x = torch.zeros(1)
+    return dec, pool, shared, calls, x
+
+
+def test_paged_step_one_launch_host_side(monkeypatch):
+    # sequence 0 appends row 5 into the shared block (copy-on-write, skip row 5),
+    # sequence 1 appends row 20 into its unmapped logical block 1 (new block):
+    # one launch carrying both table entries and the copy
+    dec, pool, shared, calls, x = _recording_paged_decoder(monkeypatch)
+    n = dec.project_append_paged(x, x, x, x, np.array([5 + 4, 20 + 4]))
+    assert n == 1 and [c[0] for c in calls] == ["one launch"]
+    _, entries, copies = calls[0]
+    new0, new1 = pool.table[0, 0], pool.table[1, 1]
+    assert new0 != shared and pool.table[1, 0] == shared
+    assert sorted(map(tuple, entries.tolist())) == [(0, new0), (5, new1)]
+    assert copies.tolist() == [[shared, new0, 5]]
+    assert dec._bt_version == pool.version and not pool._dirty
+
+
+def test_paged_step_two_launches_when_a_copy_source_is_appended_into(monkeypatch):
+    # both sequences append into the block they share, at different rows: the
+    # first copies it away (copy-on-write), then the second holds it alone and
+    # writes row 3 in place.  The copy's source is appended into in the same
+    # step, so the table update runs in its own launch before the append.
+    dec, pool, shared, calls, x = _recording_paged_decoder(monkeypatch)
+    n = dec.project_append_paged(x, x, x, x, np.array([5 + 4, 3 + 4]))
+    assert n == 1 and [c[0] for c in calls] == ["table update", "project+append"]
+    _, entries, copies = calls[0]
+    assert pool.table[1, 0] == shared and pool.ref[shared] == 1
+    assert copies.tolist() == [[shared, pool.table[0, 0]]]
+    assert entries.tolist() == [[0, pool.table[0, 0]]]
