@@ -30,10 +30,29 @@ constexpr int kProjRows = kD / (kProjThreads / kD); // rows of P per thread grou
 // oldest key while the rotation angles are computed; only the new key's
 // placement waits for the projection.  Every load that depends on no other
 // (raw vectors, rows of P_QK, the old buffer entries) is issued at the start.
-// (blk: the block of the unit's appended row when the launch carries it,
-// kTableBlock to read the block table)
+// Block that sequence b's append writes this step, from the launch's table
+// entries (slots are distinct, so at most one matches), or kTableBlock when
+// the entries do not set that slot (the table then holds it and this launch
+// does not write it).  Run by a whole wave; every lane gets the answer.
+__device__ int wave_append_block(const StepUpdateArgs &u, const AppendArgs &ap, int b, int lane)
+{
+    const int p = ap.pos[b];
+    const int r = ap.R > 0 ? p - ap.R : p; // sparse row written this step
+    if (p < 0 || r < 0 || r / ap.geom.bs >= ap.geom.max_blocks) return kTableBlock;
+    const int slot = b * ap.geom.max_blocks + r / ap.geom.bs;
+    int hit = -1;
+    for (int t = lane; t < u.n_entries; t += kWave)
+        if (u.entry[t][0] == slot) hit = t;
+    const uint64_t m = __ballot(hit >= 0);
+    if (!m) return kTableBlock;
+    return u.entry[__builtin_amdgcn_readlane(hit, __builtin_ctzll(m))][1];
+}
+
+// (u: the launch's table update on a paged step, whose entries give the
+// appended rows' blocks; nullptr to read the block table)
 template <int G, bool APPEND>
-__device__ __forceinline__ void project_unit(const ProjectArgs &a, const AppendArgs &ap, int h, int b, int blk)
+__device__ __forceinline__ void project_unit(const ProjectArgs &a, const AppendArgs &ap, int h, int b,
+                                             const StepUpdateArgs *u)
 {
     const int tid = threadIdx.x;
     const int j = tid % kD, quarter = tid / kD, wave = tid / kWave, lane = tid % kWave;
@@ -66,10 +85,11 @@ __device__ __forceinline__ void project_unit(const ProjectArgs &a, const AppendA
     }
     if constexpr (APPEND) {
         if (wave == kWaves - 1) {
-            const int64_t u = (int64_t)b * ap.H + h;
-            append_token(ap, b, h, 1, lane, f2h(ap.v_hat[u * kD + lane]), f2h(ap.v_hat[u * kD + lane + 64]), blk);
+            const int64_t un = (int64_t)b * ap.H + h;
+            const int blk = u ? wave_append_block(*u, ap, b, lane) : kTableBlock;
+            append_token(ap, b, h, 1, lane, f2h(ap.v_hat[un * kD + lane]), f2h(ap.v_hat[un * kD + lane + 64]), blk);
         } else if (wave == kWaves - 2) {
-            evict_token(ap, b, h, 0, lane, blk);
+            evict_token(ap, b, h, 0, lane, u ? wave_append_block(*u, ap, b, lane) : kTableBlock);
         }
     }
     if (tid < kD / 2) {
@@ -120,39 +140,21 @@ __device__ __forceinline__ void project_unit(const ProjectArgs &a, const AppendA
     }
     if constexpr (APPEND) {
         __syncthreads();
-        if (wave == 0) place_token(ap, b, h, 0, lane, khs[lane], khs[lane + 64], blk);
+        if (wave == 0)
+            place_token(ap, b, h, 0, lane, khs[lane], khs[lane + 64],
+                        u && ap.R == 0 ? wave_append_block(*u, ap, b, lane) : kTableBlock);
     }
 }
 
 template <int G, bool APPEND>
 __global__ __launch_bounds__(kProjThreads) void k_project(ProjectArgs a, AppendArgs ap)
 {
-    project_unit<G, APPEND>(a, ap, blockIdx.x, blockIdx.y, kTableBlock);
+    project_unit<G, APPEND>(a, ap, blockIdx.x, blockIdx.y, nullptr);
 }
 
 // ---------------------------------------------------------------------------
 // a paged step's projection, append and block-table update in one launch
 // ---------------------------------------------------------------------------
-
-// Block that sequence b's append writes this step, from the launch's table
-// entries (the last entry for the row's table slot), or kTableBlock when the
-// entries do not touch that slot (the table then holds it and this launch
-// does not write it).  Every thread of the workgroup gets the same answer.
-__device__ int step_append_block(const StepUpdateArgs &u, const AppendArgs &ap, int b, int *shared_hit)
-{
-    const int p = ap.pos[b];
-    const int r = ap.R > 0 ? p - ap.R : p; // sparse row written this step
-    const int64_t slot = r >= 0 && r / ap.geom.bs < ap.geom.max_blocks
-                             ? (int64_t)b * ap.geom.max_blocks + r / ap.geom.bs
-                             : -1;
-    if (threadIdx.x == 0) *shared_hit = -1;
-    __syncthreads();
-    if (p >= 0 && slot >= 0 && (int)threadIdx.x < u.n_entries && u.entry[threadIdx.x][0] == slot)
-        atomicMax(shared_hit, (int)threadIdx.x);
-    __syncthreads();
-    const int hit = *shared_hit;
-    return hit >= 0 ? u.entry[hit][1] : kTableBlock;
-}
 
 // plane 0 / 1: key / value indices, 2 / 3: key / value values.  Blocks are
 // [H][bs][row] per plane; row `skip` of every head is left alone (-1: none).
@@ -176,12 +178,9 @@ __device__ void copy_plane_skip(const AppendArgs &ap, int plane, int src, int ds
 template <int G>
 __global__ __launch_bounds__(kProjThreads) void k_project_paged(ProjectArgs a, AppendArgs ap, StepUpdateArgs u)
 {
-    __shared__ int hit;
     const int units = a.H * a.B, i = blockIdx.x;
     if (i < units) {
-        const int h = i % a.H, b = i / a.H;
-        const int blk = step_append_block(u, ap, b, &hit);
-        project_unit<G, true>(a, ap, h, b, blk);
+        project_unit<G, true>(a, ap, i % a.H, i / a.H, &u);
     } else if (i == units) {
         for (int t = threadIdx.x; t < u.n_entries; t += kProjThreads) u.table[u.entry[t][0]] = u.entry[t][1];
     } else {
