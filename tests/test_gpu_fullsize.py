@@ -78,10 +78,11 @@ def _check_rows(dec, oc, seqs, w, lo, ns):
         if n <= lo:
             continue
         ki, kv, vi, vv = _seq_rows(dec, b, n)
+        k_v = w.k_v or w.k  # kept value coordinates
         np.testing.assert_array_equal(ki[:, lo:n, :w.k], oc.kidx[i, :, lo:n])
-        np.testing.assert_array_equal(vi[:, lo:n, :w.k], oc.vidx[i, :, lo:n])
+        np.testing.assert_array_equal(vi[:, lo:n, :k_v], oc.vidx[i, :, lo:n])
         assert_values_bits(kv[:, lo:n, :w.k], oc.kval[i, :, lo:n], w.value_format)
-        assert_values_bits(vv[:, lo:n, :w.k], oc.vval[i, :, lo:n], w.value_format)
+        assert_values_bits(vv[:, lo:n, :k_v], oc.vval[i, :, lo:n], w.value_format)
     if w.R > 0:
         kb, vb = dec.cache.buffer_views()
         for i, b in enumerate(seqs):
@@ -89,11 +90,13 @@ def _check_rows(dec, oc, seqs, w, lo, ns):
             np.testing.assert_array_equal(vb[b].cpu().numpy().astype(np.float64), oc.ringv[i])
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5, "3-fp8", "5-fp8"])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5, "3-fp8", "5-fp8", "2-kv"])
 def test_full_size_steps(cfg):
     w = wl.config(int(str(cfg)[0]))
     if str(cfg).endswith("fp8"):  # the same workload with 8-bit sparse values
         w = w.scaled(value_format=1)
+    if str(cfg).endswith("kv"):  # its 2k budget split 60/40 between keys and values (77 / 51)
+        w = w.scaled(k=77, k_v=51)
     seqs = _samples(w)
     print(f"\n[fullsize] config {cfg}: {w.name} B={w.B} samples={seqs}", flush=True)
     dec = build_decoder(w, extra_steps=STEPS)
