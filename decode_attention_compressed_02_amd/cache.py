@@ -248,6 +248,11 @@ class PagedPool:
                 self._dirty.append(b * self.max_blocks + lb)
         self.version += 1
 
+    def dirty_count(self) -> int:
+        """Table slot changes recorded since the last take_dirty() (a slot
+        changed twice counts twice)."""
+        return len(self._dirty)
+
     def take_dirty(self):
         """(slot, block id) pairs of the table entries changed since the last
         call, slot = b * max_blocks + logical block; clears the record."""
@@ -346,7 +351,7 @@ class PagedSwanDecoder(SwanDecoder):
         w = np.flatnonzero(rows >= 0)
         lb = np.minimum(rows[w] // pool.block_size, pool.max_blocks - 1)
         appended = set(pool.table[w, lb].tolist())
-        if (self._bt_version < 0 or len(pool._dirty) > self.FULL_UPLOAD_ENTRIES
+        if (self._bt_version < 0 or pool.dirty_count() > self.FULL_UPLOAD_ENTRIES
                 or any(c[0] in appended for c in copies)):
             self.sync_table([c[:2] for c in copies], stream)
             self.project_append(q, k, v_hat, pos, max_pos, stream)

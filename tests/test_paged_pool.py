@@ -166,7 +166,7 @@ def test_paged_step_one_launch_host_side(monkeypatch):
     assert new0 != shared and pool.table[1, 0] == shared
     assert sorted(map(tuple, entries.tolist())) == [(0, new0), (5, new1)]
     assert copies.tolist() == [[shared, new0, 5]]
-    assert dec._bt_version == pool.version and not pool._dirty
+    assert dec._bt_version == pool.version and pool.dirty_count() == 0
 
 
 def test_paged_step_two_launches_when_a_copy_source_is_appended_into(monkeypatch):
