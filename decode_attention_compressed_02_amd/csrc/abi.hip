@@ -293,8 +293,12 @@ swan_status swan_project_append_paged(const swan_dims *d, const swan_cache *c, c
         if (at < 0 || at >= n_slots || id < -1 || id >= d->num_blocks)
             return fail(SWAN_ERR_INVALID_ARG, "entry %d = (%d, %d): slot outside [0, %lld) or block outside [-1, %d)", i,
                         at, id, (long long)n_slots, d->num_blocks);
-        for (int32_t j = 0; j < i; ++j)
-            if (entries[2 * j] == at) return fail(SWAN_ERR_INVALID_ARG, "entries %d and %d write the same slot %d", j, i, at);
+        // the one-launch path reads each append's block from these entries: at
+        // most one may set a slot (checked where that path is taken)
+        if (n_entries <= swan::kFusedEntries)
+            for (int32_t j = 0; j < i; ++j)
+                if (entries[2 * j] == at)
+                    return fail(SWAN_ERR_INVALID_ARG, "entries %d and %d write the same slot %d", j, i, at);
     }
     for (int32_t i = 0; i < n_copies; ++i) {
         const int32_t src = copies[3 * i], dst = copies[3 * i + 1], skip = copies[3 * i + 2];

@@ -311,8 +311,9 @@ swan_status swan_paged_update(const swan_dims *dims, const swan_cache *cache, in
  * appended blocks is: a block is copied only when it is shared, and shared
  * blocks are not written).  Up to 192 entries and 32 copies travel in the one
  * launch; more are handed to swan_paged_update first (one launch more, same
- * results).  Errors: those of the two calls, INVALID_ARG for repeated slots
- * or a skip row outside [-1, block_size).
+ * results).  Errors: those of the two calls, INVALID_ARG for a skip row
+ * outside [-1, block_size) or, when the entries travel in the one launch
+ * (at most 192), a slot set twice.
  */
 swan_status swan_project_append_paged(const swan_dims *dims, const swan_cache *cache, const float *q, const float *k,
                                       const float *v_hat, const int32_t *pos, int32_t max_pos, const float *P_qk,
