@@ -165,3 +165,58 @@ def test_paged_pool_steps_with_copy_on_write(k, vf, fused):
     # copy-on-write happened exactly for sequences 1 and 2 at their first step
     assert copies == [2, 0, 0]
     assert (pool.ref[pool.table[0, :5]] == w.B).all() and pool.ref[pool.table[0, 5]] == w.B - 2
+
+
+@pytest.mark.parametrize("R,k,kv,vf,bs", [(0, 32, 0, 0, 16), (16, 64, 0, 1, 16), (16, 40, 20, 0, 32),
+                                          (0, 64, 32, 1, 32)])
+def test_one_launch_paged_step_equals_two_launches(R, k, kv, vf, bs, monkeypatch):
+    # two decoders from the same state: one issues each step's table writes and
+    # copy-on-write copies with its projection/append (swan_project_append_paged),
+    # the other through swan_paged_update first; every output, plane, table entry
+    # and buffer stays bit-identical.  Sequences 1 and 2 append into the last
+    # shared prefix block at the first step (copy-on-write); R = 0 prunes the new
+    # token straight into its row through the launch's entries.
+    import copy
+    ctx = tuple(c - 16 + R for c in (300, 100, 112, 113, 250, 128))
+    w = wl.Workload("paged one launch", len(ctx), 8, 2, R, k, ctx, steps=4, seed=77, block_size=bs,
+                    shared_prefix=96, value_format=vf, k_v=kv)
+    P = wl.projection_qk(w)
+    oc = oracle.OracleCache.for_workload(w, ncap=max(w.history_len(b) for b in range(w.B)) + w.steps)
+    T = [w.history_len(b) for b in range(w.B)]
+    K = np.zeros((w.B, w.H_kv, max(T), D), np.float32)
+    V = np.zeros_like(K)
+    for b in range(w.B):
+        K[b, :, :T[b]], V[b, :, :T[b]] = wl.history(w, b)
+    oc.prefill(K, V, np.array(T, np.int64), P.astype(np.float64), w.rope_base)
+    pool = build_pool(w, prefix_blocks=96 // bs)
+    rows = [T[b] - w.R for b in range(w.B)]
+    decs = []
+    for p in (pool, copy.deepcopy(pool)):
+        dims = S.make_dims(w.B, w.N_h, w.H_kv, w.R, w.k, block_size=bs, max_blocks=p.max_blocks,
+                           num_blocks=p.num_blocks, value_format=vf, k_v=kv)
+        d = PagedSwanDecoder(dims, cuda(P), p, w.rope_base)
+        upload(d.cache, oc, p.table, rows=rows)
+        decs.append(d)
+    one, two = decs
+    updates = []
+    real_update = S.swan_paged_update
+    monkeypatch.setattr(S, "swan_paged_update", lambda *a, **kw: (updates.append(1), real_update(*a, **kw)))
+    copies = []
+    for s in range(w.steps):
+        q, kr, vn, pos = wl.step_inputs(w, s)
+        args = [cuda(a) for a in (q, kr, vn, pos)]
+        n_before = len(updates)
+        copies.append(one.project_append_paged(*args, pos))
+        assert len(updates) == n_before, "the one-launch path fell back to a separate table update"
+        out1 = one.decode(args[3], int(pos.max())).clone()
+        two.prepare_step(pos)
+        two.project_append(*args, int(pos.max()))
+        out2 = two.decode(args[3], int(pos.max()))
+        torch.testing.assert_close(out1, out2, rtol=0, atol=0)
+    assert copies[0] == 2, copies
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(one.cache.block_table.cpu().numpy(), two.cache.block_table.cpu().numpy())
+    np.testing.assert_array_equal(one.pool.table, two.pool.table)
+    for a, b in zip([*one.cache.sparse_views(), *one.cache.buffer_views()],
+                    [*two.cache.sparse_views(), *two.cache.buffer_views()]):
+        np.testing.assert_array_equal(a.cpu().numpy().view(np.uint8), b.cpu().numpy().view(np.uint8))
