@@ -336,6 +336,44 @@ def test_decode_inactive_and_ragged():
     assert rel_l2_max(out[keep], want[keep]) < TOL
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_decode_batch_over_two_waves_of_sequences(paged):
+    # 130 sequences: the split pass's work-plan scan keeps 64 sequences per
+    # pass of a wave, so this batch takes three passes; ragged contexts from 1
+    # to 400 tokens, a few sequences inactive, a fixed plan of 64 rows a wave
+    # (pieces straddle units) and the automatic one
+    B = 130
+    ctx = tuple(int(x) for x in rng(130).integers(1, 400, B))
+    w = wl.Workload("big batch", B, 8, 2, 16, 32, ctx, seed=31)
+    oc, *_ = oracle_state(w)
+    P = wl.projection_qk(w)
+    q, kr, vn, pos = wl.step_inputs(w, 0)
+    qhat, khat = oc.project(q, kr, pos.astype(np.int64), P.astype(np.float64))
+    oc.append(khat, vn.astype(np.float64), pos.astype(np.int64))
+    want = oc.decode(qhat.astype(np.float32).astype(np.float64), pos.astype(np.int64))
+    inactive = [3, 64, 65, 129]
+    pos_gpu = pos.copy()
+    pos_gpu[inactive] = -1
+    keep = [b for b in range(B) if b not in inactive]
+    for split in (64, 0):
+        bt, kw = None, {}
+        if paged:
+            bs = 16
+            mb = (oc.ncap + bs - 1) // bs
+            nb = B * mb + 3
+            bt = rng(9).permutation(nb)[:B * mb].reshape(B, mb).astype(np.int32)
+            kw = dict(block_size=bs, max_blocks=mb, num_blocks=nb, block_table=bt)
+        dec = make_decoder(oc, P, split_tokens=split, **kw)
+        upload(dec.cache, oc, bt)
+        dec.q_hat.copy_(cuda(qhat.astype(np.float32)))
+        out = dec.decode(cuda(pos_gpu), int(pos.max())).cpu().numpy()
+        err = rel_l2_max(out[keep], want[keep])
+        print(f"[B={B} paged={paged} split={split}] splits={S.swan_decode_num_splits(dec.dims, int(pos.max()))} "
+              f"rel_l2={err:.2e}")
+        assert not out[inactive].any()
+        assert err < TOL
+
+
 # ---------------------------------------------------------------------------
 # whole steps chained on the GPU vs oracle steps
 # ---------------------------------------------------------------------------
