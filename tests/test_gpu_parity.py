@@ -336,6 +336,57 @@ def test_decode_inactive_and_ragged():
     assert rel_l2_max(out[keep], want[keep]) < TOL
 
 
+def _random_case(seed):
+    """A valid decode configuration drawn from a seeded generator: GQA group,
+    kv heads, batch, ragged contexts, kept key and value coordinates (row
+    widths equal or a factor of two apart), buffer size, value format, layout
+    and work plan."""
+    r = rng(5000 + seed)
+    g = int(r.choice([1, 2, 4, 8]))
+    H = int(r.choice([1, 2]))
+    B = int(r.integers(1, 6))
+    k = int(r.integers(1, 129))
+    k_v = 0
+    if r.random() < 0.4:
+        ks = S.swan_row_stride(k)
+        lo, hi = max(1, ks // 4 + 1), min(128, 2 * ks)
+        k_v = int(r.integers(lo, hi + 1))
+    R = int(r.choice([0, 8, 16, 64]))
+    ctx = tuple(int(x) for x in r.integers(1, 700, B))
+    vf = int(r.random() < 0.3)
+    bs = int(r.choice([0, 0, 8, 16, 32, 48]))
+    split = int(r.choice([0, 64, 128]))
+    return dict(g=g, H=H, B=B, k=k, k_v=k_v, R=R, ctx=ctx, vf=vf, bs=bs, split=split)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_decode_random_configurations(seed):
+    c = _random_case(seed)
+    print(f"[random {seed}] {c}", flush=True)
+    extra = dict(value_format=c["vf"]) | (dict(k_v=c["k_v"]) if c["k_v"] else {})
+    w = wl.Workload(f"random {seed}", c["B"], c["g"] * c["H"], c["H"], c["R"], c["k"], c["ctx"], seed=seed, **extra)
+    oc, *_ = oracle_state(w, ncap=max(w.n_cap(), 1))
+    P = wl.projection_qk(w)
+    q, kr, vn, pos = wl.step_inputs(w, 0)
+    qhat, khat = oc.project(q, kr, pos.astype(np.int64), P.astype(np.float64))
+    oc.append(khat, vn.astype(np.float64), pos.astype(np.int64))
+    want = oc.decode(qhat.astype(np.float32).astype(np.float64), pos.astype(np.int64))
+    bt, kw = None, {}
+    if c["bs"]:
+        bs = c["bs"]
+        mb = (oc.ncap + bs - 1) // bs
+        nb = c["B"] * mb + 2
+        bt = rng(seed).permutation(nb)[:c["B"] * mb].reshape(c["B"], mb).astype(np.int32)
+        kw = dict(block_size=bs, max_blocks=mb, num_blocks=nb, block_table=bt)
+    dec = make_decoder(oc, P, split_tokens=c["split"], **kw)
+    upload(dec.cache, oc, bt)
+    dec.q_hat.copy_(cuda(qhat.astype(np.float32)))
+    out = dec.decode(cuda(pos), int(pos.max())).cpu().numpy()
+    err = rel_l2_max(out, want)
+    print(f"[random {seed}] rel_l2={err:.2e}", flush=True)
+    assert err < TOL
+
+
 @pytest.mark.parametrize("paged", [False, True])
 def test_decode_batch_over_two_waves_of_sequences(paged):
     # 130 sequences: the split pass's work-plan scan keeps 64 sequences per
