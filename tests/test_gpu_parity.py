@@ -459,6 +459,40 @@ def test_step_chain(cfg):
                 assert_values_bits(rows[3][b, :, r, :w.k_v or w.k], oc.vval[b, :, r], w.value_format)
 
 
+@pytest.mark.parametrize("seed", range(100, 112))
+def test_step_chain_random_configurations(seed):
+    # the GPU builds the hybrid cache from the seeded history itself
+    # (swan_prefill_convert), then runs three whole steps; the oracle does the
+    # same in float64: k_hat and every stored row bit-exact, q_hat and the
+    # outputs within their bars
+    c = _random_case(seed)
+    print(f"[random step {seed}] {c}", flush=True)
+    extra = dict(value_format=c["vf"]) | (dict(k_v=c["k_v"]) if c["k_v"] else {})
+    w = wl.Workload(f"random step {seed}", c["B"], c["g"] * c["H"], c["H"], c["R"], c["k"], c["ctx"], seed=seed,
+                    steps=3, **extra)
+    k_v = w.k_v or w.k
+    oc, K, V, Ts = oracle_state(w)
+    P = wl.projection_qk(w)
+    dec = make_decoder(oc, P, split_tokens=c["split"])
+    dec.prefill(cuda(Ts.astype(np.int32)), max(int(Ts.max()), 1), cuda(K), cuda(V))
+    for s in range(w.steps):
+        q, kr, vn, pos = wl.step_inputs(w, s)
+        out = dec.step(cuda(q), cuda(kr), cuda(vn), cuda(pos), int(pos.max())).cpu().numpy()
+        qh, kh, want = oc.step(q, kr, vn, pos.astype(np.int64), P.astype(np.float64), w.rope_base)
+        assert rel_l2_max(dec.q_hat.cpu().numpy(), qh) < 1e-6
+        np.testing.assert_array_equal(dec.k_hat.cpu().numpy().astype(np.float64), kh)
+        err = rel_l2_max(out, want)
+        print(f"[random step {seed}] step {s} rel_l2={err:.2e}", flush=True)
+        assert err < TOL
+    rows = download_rows(dec.cache, w.B, w.H_kv, oc.ncap)
+    for b in range(w.B):
+        n = max(0, int(pos[b]) + 1 - w.R)
+        np.testing.assert_array_equal(rows[0][b, :, :n, :w.k], oc.kidx[b, :, :n])
+        np.testing.assert_array_equal(rows[2][b, :, :n, :k_v], oc.vidx[b, :, :n])
+        assert_values_bits(rows[1][b, :, :n, :w.k], oc.kval[b, :, :n], w.value_format)
+        assert_values_bits(rows[3][b, :, :n, :k_v], oc.vval[b, :, :n], w.value_format)
+
+
 # ---------------------------------------------------------------------------
 # prefill -> hybrid cache
 # ---------------------------------------------------------------------------
