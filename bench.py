@@ -285,7 +285,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded N(0,1) raw keys/queries, stored-basis values, random orthogonal P_QK)",
-        "config": {"workload": f"config {args.config}: {w.name}" + (", fp8 values" if w.value_format else "")
+        "config": {"workload": f"workload {args.config}: {w.name}" + (", fp8 values" if w.value_format else "")
                    + (f", k_K {w.k} / k_V {w.k_v}" if w.k_v else ""),
                    "B": w.B, "N_h": w.N_h, "H_kv": w.H_kv,
                    "d_h": w.d_h, "ctx_first_step": int(w.ctx[0]), "R": w.R, "k": w.k, "k_v": w.k_v or w.k,

@@ -98,7 +98,7 @@ def test_full_size_steps(cfg):
     if str(cfg).endswith("kv"):  # its 2k budget split 60/40 between keys and values (77 / 51)
         w = w.scaled(k=77, k_v=51)
     seqs = _samples(w)
-    print(f"\n[fullsize] config {cfg}: {w.name} B={w.B} samples={seqs}", flush=True)
+    print(f"\n[fullsize] workload {cfg}: {w.name} B={w.B} samples={seqs}", flush=True)
     dec = build_decoder(w, extra_steps=STEPS)
     print(f"[fullsize] GPU state built; split waves "
           f"{S.swan_decode_num_splits(dec.dims, int(max(w.ctx)) + STEPS)}", flush=True)
@@ -126,7 +126,7 @@ def test_full_size_steps(cfg):
         else:
             vmax = max(vmax, float(dec.cache.v_val.abs().max()))
         bound = float(out.abs().max())
-        print(f"[fullsize] config {cfg} step {s}: sampled rel_l2={err:.2e}; max|o|={bound:.3f} <= {vmax:.3f}",
+        print(f"[fullsize] workload {cfg} step {s}: sampled rel_l2={err:.2e}; max|o|={bound:.3f} <= {vmax:.3f}",
               flush=True)
         assert torch.isfinite(out).all()
         assert bound <= vmax * (1 + 1e-5)
