@@ -62,6 +62,18 @@ def last_dispatches(trace_csv: str, kernel: str, last: int, skip: int = 0):
     return statistics.mean(d), min(d), max(d), len(rows) + skip
 
 
+def counter_means(counter_csv: str, kernel: str, last: int) -> dict:
+    """{counter: mean value per dispatch} over the last `last` dispatches of a
+    kernel in a rocprofv3 counter_collection.csv."""
+    per = {}
+    for r in csv.DictReader(open(counter_csv)):
+        if kernel in r["Kernel_Name"]:
+            per.setdefault(int(r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    ids = sorted(per)[-last:]
+    names = sorted({n for i in ids for n in per[i]})
+    return {n: statistics.mean(per[i][n] for i in ids if n in per[i]) for n in names}
+
+
 def _counter_values(path: str, counter: str):
     """{kernel name: [value per dispatch]} for one counter."""
     vals = {}
@@ -114,6 +126,10 @@ def main(argv=None):
     l.add_argument("--n", type=int, default=36, help="dispatches at the end of the run (timed + back-to-back)")
     l.add_argument("--skip", type=int, default=0,
                    help="leave out this many dispatches at the very end (bench.py's single-launch timings)")
+    c = sub.add_parser("counters")
+    c.add_argument("csv", help="counter_collection.csv")
+    c.add_argument("--kernel", default="k_split")
+    c.add_argument("--n", type=int, default=8, help="dispatches at the end of the run")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -124,6 +140,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         print(stats_table(args.csv, args.top))
+    elif args.cmd == "counters":
+        for n, v in counter_means(args.csv, args.kernel, args.n).items():
+            print(f"{n}: {v:.6g}")
     elif args.cmd == "last":
         mean, lo, hi, total = last_dispatches(args.csv, args.kernel, args.n, args.skip)
         where = f"last {args.n}" + (f" before the final {args.skip}" if args.skip else "")
