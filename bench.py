@@ -73,13 +73,34 @@ def cpu_baseline(w, seqs: list[int], seconds: float, max_steps: int = 4096, thre
     return tokens / secs, used, secs, desc
 
 
+def host_cpu():
+    """(CPU model, hardware threads this process may run on) of the host."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count() or 1
+    return model, threads
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=16)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first (replaying the step sequence); the GPU's power "
-                         "management needs ~20 ms of sustained load to settle")
+    ap.add_argument("--warmup", type=int, default=16,
+                    help="untimed steps right before the timed ones (replaying the step sequence)")
+    ap.add_argument("--settle-steps", type=int, default=400,
+                    help="steps run back to back, timed in chunks and reported, before the warm-up of the "
+                         "timed steps: the GPU's power management needs some tens of ms of sustained load "
+                         "before kernels run at their steady speed (0 = no settle phase)")
     ap.add_argument("--config", type=int, default=3, help="workload number (1-5); 3 is the headline")
     ap.add_argument("--split-tokens", type=int, default=0, help="work rows per wave (0 = automatic)")
     ap.add_argument("--values", choices=("fp16", "fp8"), default="fp16",
@@ -94,6 +115,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle stepping time of the sample")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="split launches timed one at a time after a 1 GiB cache-evicting fill (median); 0 = skip")
+    ap.add_argument("--no-stream-ceiling", action="store_true",
+                    help="skip the streaming-read measurement of the GPU's attainable HBM read rate")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run plain device copies of this size (for calibrating HBM byte counters)")
     args = ap.parse_args()
@@ -114,6 +137,7 @@ def main():
         sys.exit(1)
     S.lib()
     w = wl.config(args.config)
+    base_name = w.name.replace(f" {w.steps} steps", "")
     if args.values == "fp8":
         w = w.scaled(value_format=1)
     if args.kv_share > 0:
@@ -165,32 +189,95 @@ def main():
             dec._bt_version = -1
             dec.sync_table()
 
-    # warm-up: replay the step sequence from the initial state, cyclically
-    for s in range(args.warmup):
-        if s % args.steps == 0:
-            restore()
-        run_step(inputs[s % args.steps], ph=pos_host[s % args.steps])
-    torch.cuda.synchronize()
-    restore()
-    torch.cuda.synchronize()
+    def split_launch():
+        q, kr, vn, pos, mp = inputs[args.steps - 1]
+        S.swan_decode_split(dec.dims, dec.cache.struct(), pos, mp, dec.q_hat, dec.workspace)
+
+    def back_to_back(launch, reps=20):
+        """Per-launch time (ms) of `reps` launches enqueued back to back between two events."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
 
     graphs = None
+
+    def timed_steps(warmup):
+        """`warmup` untimed steps replaying the step sequence from the initial
+        state, then the args.steps timed steps from it: wall seconds."""
+        for s in range(warmup):
+            if s % args.steps == 0:
+                restore()
+            run_step(inputs[s % args.steps], ph=pos_host[s % args.steps])
+        torch.cuda.synchronize()
+        restore()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            if graphs is None:
+                run_step(inputs[s], ph=pos_host[s])
+            else:
+                if paged:  # host bookkeeping stays eager; its table writes travel by value
+                    dec.prepare_step(pos_host[s])
+                graphs[s].replay()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    tokens = sum(int(inputs[s][3].sum().item()) + w.B for s in range(args.steps))  # sum_b (pos_b + 1)
+    # algorithmic bytes of the split kernel per launch, per timed step
+    split_bytes, dec_bytes, flops = [], [], []
+    for s in range(args.steps):
+        pos = inputs[s][3].cpu().numpy()
+        n = [max(0, int(p) + 1 - w.R) for p in pos]
+        f = [min(int(p) + 1, w.R) for p in pos]
+        split_bytes.append(acc.split_kernel_bytes(n, w.H_kv, w.N_h, f, w.k, value_bytes=vbytes, k_v=w.k_v))
+        dec_bytes.append(acc.decode_bytes(n, w.H_kv, w.N_h, f, w.k, value_bytes=vbytes, k_v=w.k_v))
+        flops.append(acc.decode_flops(n, w.H_kv, w.N_h, f, w.k, k_v=w.k_v))
+    last_bytes = float(split_bytes[-1])
+
+    # 1. the timed steps without a settle phase (only the warm-up before them)
+    wall_u = timed_steps(args.warmup)
+    split_b2b_u = back_to_back(split_launch)
+    unsettled = {"warmup": args.warmup, "ms_per_step": wall_u * 1e3 / args.steps, "value": tokens / wall_u,
+                 "step_frac_of_peak": float(np.mean(dec_bytes)) / wall_u * args.steps / 1e9 / HBM_PEAK_GBS,
+                 "split_kernel_ms_back_to_back": split_b2b_u,
+                 "roofline_frac": last_bytes / (split_b2b_u * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    log(f"without a settle phase: {unsettled['ms_per_step'] * 1e3:.1f} us a step, split pass "
+        f"{split_b2b_u * 1e3:.1f} us back to back")
+
+    # 2. the settle phase: whole steps back to back, in chunks of the step
+    # sequence (restored before each), each chunk timed between two events
+    settle = None
+    if args.settle_steps > 0:
+        chunks, done = [], 0
+        while done < args.settle_steps:
+            restore()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for s in range(args.steps):
+                run_step(inputs[s], ph=pos_host[s])
+            e1.record(stream)
+            chunks.append((e0, e1))
+            done += args.steps
+        torch.cuda.synchronize()
+        per_step = [a.elapsed_time(b) * 1e3 / args.steps for a, b in chunks]
+        settle = {"steps": done, "chunk_steps": args.steps, "ms": sum(per_step) * args.steps / 1e3,
+                  "per_step_us_by_chunk": [round(x, 1) for x in per_step]}
+        log(f"settle phase: {done} steps, {per_step[0]:.1f} -> {per_step[-1]:.1f} us a step")
+
     if args.graph:  # capturing records the launches and runs nothing: the state is unchanged
         from decode_attention_compressed_02_amd.cache import StepGraph
+        restore()
         graphs = [StepGraph(dec, *inputs[s][:4], max_pos=max_pos_all) for s in range(args.steps)]
         torch.cuda.synchronize()
 
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        if graphs is None:
-            run_step(inputs[s], ph=pos_host[s])
-        else:
-            if paged:  # host bookkeeping stays eager; its table writes travel by value
-                dec.prepare_step(pos_host[s])
-            graphs[s].replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    # 3. the timed steps (the reported value): warm-up, then the steps
+    wall = timed_steps(args.warmup)
     ms_step = wall * 1e3 / args.steps
+    value = tokens / wall
 
     # the split pass's duration inside a step, from a replay of the same steps
     # with events around it (event markers add a few microseconds of launch
@@ -202,34 +289,22 @@ def main():
         run_step(inputs[s], evs[s], ph=pos_host[s])
     torch.cuda.synchronize()
     split_ms = [a.elapsed_time(b) for a, b in evs]
+    split_avg_ms = float(np.mean(split_ms))
 
     # the split kernel alone, launched back to back on the same stream over
     # the state the last step left (decode does not modify the cache): its
     # per-launch time is the kernel's duration plus the launch gap, without
     # the wait for the preceding kernels of a step
-    q, kr, vn, pos, mp = inputs[args.steps - 1]
-    reps = 20
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
+    split_b2b_ms = back_to_back(split_launch)
+    achieved = last_bytes / (split_b2b_ms * 1e-3) / 1e9
+
+    # the whole decode (split + reduce) back to back: t_decode
+    def decode_launch():
+        q, kr, vn, pos, mp = inputs[args.steps - 1]
         S.swan_decode_split(dec.dims, dec.cache.struct(), pos, mp, dec.q_hat, dec.workspace)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    split_b2b_ms = e0.elapsed_time(e1) / reps
-    tokens = sum(int(inputs[s][3].sum().item()) + w.B for s in range(args.steps))  # sum_b (pos_b + 1)
-    value = tokens / wall
-    # algorithmic bytes of the split kernel per launch, averaged over the timed steps
-    split_bytes, dec_bytes, flops = [], [], []
-    for s in range(args.steps):
-        pos = inputs[s][3].cpu().numpy()
-        n = [max(0, int(p) + 1 - w.R) for p in pos]
-        f = [min(int(p) + 1, w.R) for p in pos]
-        split_bytes.append(acc.split_kernel_bytes(n, w.H_kv, w.N_h, f, w.k, value_bytes=vbytes, k_v=w.k_v))
-        dec_bytes.append(acc.decode_bytes(n, w.H_kv, w.N_h, f, w.k, value_bytes=vbytes, k_v=w.k_v))
-        flops.append(acc.decode_flops(n, w.H_kv, w.N_h, f, w.k, k_v=w.k_v))
-    split_avg_ms = float(np.mean(split_ms))
-    # bytes of the last step's launch over the back-to-back duration
-    achieved = float(split_bytes[-1]) / (split_b2b_ms * 1e-3) / 1e9
+        S.swan_decode_reduce(dec.dims, pos, mp, dec.workspace, dec.o_hat)
+    decode_ms = back_to_back(decode_launch)
+    last_tokens = int(inputs[args.steps - 1][3].sum().item()) + w.B
 
     # the split kernel from a cold last-level cache: before every other one of
     # these launches a 1 GiB fill evicts the L2s and the 256 MB MALL, so a
@@ -238,7 +313,6 @@ def main():
     # warm figure of the same protocol
     split_cold_ms = split_single_ms = None
     if args.cold_reps > 0:
-        pos, mp = inputs[args.steps - 1][3:5]
         flush = torch.empty(2 ** 30, dtype=torch.uint8, device="cuda")
         times = {True: [], False: []}
         for i in range(2 * args.cold_reps):
@@ -247,12 +321,31 @@ def main():
                 flush.fill_(1)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            S.swan_decode_split(dec.dims, dec.cache.struct(), pos, mp, dec.q_hat, dec.workspace)
+            split_launch()
             b.record(stream)
             torch.cuda.synchronize()
             times[evict].append(a.elapsed_time(b))
         del flush
         split_cold_ms, split_single_ms = float(np.median(times[True])), float(np.median(times[False]))
+
+    # the attainable HBM read rate on this GPU: a plain streaming read of the
+    # split kernel's byte count, at a few grid sizes (the best is the ceiling)
+    stream_read = None
+    if not args.no_stream_ceiling:
+        nb = int(last_bytes) // 16 * 16
+        buf = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
+        sink = torch.empty(4096 * 64, dtype=torch.int32, device="cuda")
+        best = None
+        for waves in (1024, 2048, 4096):
+            launch = lambda: S.swan_measure_stream_read(buf, waves, sink)
+            back_to_back(launch, 3)
+            ms = back_to_back(launch)
+            gbs = nb / (ms * 1e-3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, waves, ms)
+        del buf, sink
+        stream_read = {"GBps": best[0], "waves": best[1], "ms": best[2], "bytes": nb,
+                       "frac_of_peak": best[0] / HBM_PEAK_GBS}
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -272,6 +365,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                "kernel": "k_split", "algorithmic_bytes_per_launch": last_bytes}
+    if stream_read:
+        roofline["measured_ceiling_GBps"] = stream_read["GBps"]
+        roofline["frac_of_measured_ceiling"] = achieved / stream_read["GBps"]
     result = {
         "metric": "decode-attn KV tokens/sec and achieved HBM GB/s (% of peak) per step",
         "value": value,
@@ -285,37 +384,43 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded N(0,1) raw keys/queries, stored-basis values, random orthogonal P_QK)",
-        "config": {"workload": f"workload {args.config}: {w.name}" + (", fp8 values" if w.value_format else "")
-                   + (f", k_K {w.k} / k_V {w.k_v}" if w.k_v else ""),
+        "config": {"workload": f"workload {args.config}: {base_name}" + (", fp8 values" if w.value_format else "")
+                   + (f", k_K {w.k} / k_V {w.k_v}" if w.k_v else "")
+                   + f", {args.steps} consecutive decode steps timed",
                    "B": w.B, "N_h": w.N_h, "H_kv": w.H_kv,
                    "d_h": w.d_h, "ctx_first_step": int(w.ctx[0]), "R": w.R, "k": w.k, "k_v": w.k_v or w.k,
                    "storage": f"{'fp8 E4M3' if w.value_format else 'fp16'} values, uint8 indices, fp16 dense buffer",
                    "split_waves": nsplit,
                    "split_tokens": dec.dims.split_tokens or "auto",
                    "launch": "HIP graph per step" if args.graph else "eager"},
+        "settle": settle,
+        "unsettled": unsettled,
         "step_hbm_GBps": float(np.mean(dec_bytes)) / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": float(np.mean(dec_bytes)) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "head_tokens_per_s": value * w.H_kv,
+        "decode_ms_back_to_back": decode_ms,
+        "decode_kv_tokens_per_s": last_tokens / (decode_ms * 1e-3),
+        "decode_frac_of_peak": float(dec_bytes[-1]) / (decode_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "split_kernel_ms_in_step": split_avg_ms,
         "split_kernel_ms_back_to_back": split_b2b_ms,
         "split_kernel_ms_single_launch": split_single_ms,
         "split_kernel_ms_cold_cache": split_cold_ms,
-        "split_cold_cache_GBps": (float(split_bytes[-1]) / (split_cold_ms * 1e-3) / 1e9) if split_cold_ms else None,
+        "split_cold_cache_GBps": (last_bytes / (split_cold_ms * 1e-3) / 1e9) if split_cold_ms else None,
+        "stream_read": stream_read,
         "decode_gflops_per_step": float(np.mean(flops)) / 1e9,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "k_split", "algorithmic_bytes_per_launch": float(split_bytes[-1])},
+        "roofline": roofline,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
+        model, threads = host_cpu()
         seqs = list(range(min(args.cpu_seqs, w.B)))
         v, cores, secs, desc = cpu_baseline(w, seqs, args.cpu_seconds)
         result["cpu_baseline"] = {"value": v, "unit": "KV tokens/s", "cores": cores, "kind": "oracle",
-                                  "sample": desc, "seconds": secs}
+                                  "sample": desc, "seconds": secs, "host_cpu": model, "host_threads": threads}
         # the same oracle on one thread, over one sequence (all kv heads)
         v1, _, secs1, desc1 = cpu_baseline(w, seqs[:1], args.cpu_seconds / 4, threads=1)
         result["cpu_baseline_1_thread"] = {"value": v1, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
-                                           "sample": desc1, "seconds": secs1}
+                                           "sample": desc1, "seconds": secs1, "host_cpu": model}
     print(json.dumps(result), flush=True)
 
 

@@ -12,7 +12,7 @@ import math
 
 def sparse_vector_bytes(k: int, value_bytes: int = 2, index_bytes: int = 1, offset_bytes: int = 2) -> int:
     """Bytes of one pruned vector: k (index, value) pairs plus the constant
-    2-byte CSR offset (SWAN memory section): 3k + 2 with fp16 values and
+    2-byte CSR offset (SWAN page, memory-savings paragraphs): 3k + 2 with fp16 values and
     8-bit indices, 2k + 2 with 8-bit float values."""
     return k * (value_bytes + index_bytes) + offset_bytes
 

@@ -50,6 +50,14 @@ swan_status check_dims(const swan_dims *d)
     if (d->block_size > 0) {
         if (d->max_blocks < 1 || d->num_blocks < 1)
             return fail(SWAN_ERR_INVALID_ARG, "paged layout needs max_blocks >= 1 and num_blocks >= 1");
+        // table slots (b * max_blocks + j) travel as int32 and a sequence's
+        // sparse rows are counted in int32 (positions are int32)
+        if ((int64_t)d->B * d->max_blocks > INT32_MAX)
+            return fail(SWAN_ERR_UNSUPPORTED, "B * max_blocks = %lld block-table slots, at most %d are supported",
+                        (long long)d->B * d->max_blocks, INT32_MAX);
+        if ((int64_t)d->max_blocks * d->block_size > INT32_MAX)
+            return fail(SWAN_ERR_UNSUPPORTED, "max_blocks * block_size = %lld sparse rows a sequence, at most %d are "
+                                              "supported", (long long)d->max_blocks * d->block_size, INT32_MAX);
     } else if (d->n_cap < 0) {
         return fail(SWAN_ERR_INVALID_ARG, "n_cap < 0");
     }
@@ -63,6 +71,16 @@ swan_status check_dims(const swan_dims *d)
         if (ksv != ks && ksv != 2 * ks && 2 * ksv != ks)
             return fail(SWAN_ERR_UNSUPPORTED, "k = %d and k_v = %d: stored row widths %d and %d, supported when equal "
                                               "or one twice the other", d->k, d->k_v, ks, ksv);
+    }
+    if (d->block_size == 0) {
+        // the decode reads a unit's rows of each plane through one buffer
+        // resource, whose byte range is 32-bit
+        const int ks = row_stride(d->k), ksv = row_stride(d->k_v > 0 ? d->k_v : d->k);
+        const int64_t unit_plane = (int64_t)d->n_cap * (ks > ksv ? ks : ksv) *
+                                   (d->value_format == SWAN_VALUES_FP8_E4M3 ? 1 : 2);
+        if (unit_plane >= ((int64_t)1 << 32))
+            return fail(SWAN_ERR_UNSUPPORTED, "n_cap = %d: %lld bytes of one (sequence, kv head) value plane, below "
+                                              "2^32 are supported", d->n_cap, (long long)unit_plane);
     }
     return SWAN_OK;
 }
@@ -308,9 +326,18 @@ swan_status swan_project_append_paged(const swan_dims *d, const swan_cache *c, c
         if (skip < -1 || skip >= d->block_size)
             return fail(SWAN_ERR_INVALID_ARG, "copy %d: skip row %d outside [-1, %d)", i, skip, d->block_size);
     }
+    if (!q || !k || !v_hat || !pos || !P_qk || !q_hat || !k_hat) return fail(SWAN_ERR_INVALID_ARG, "NULL array argument");
+    if (!(rope_base > 1.0f)) return fail(SWAN_ERR_INVALID_ARG, "rope_base must be > 1");
+    const int64_t row = d->R > 0 ? (int64_t)max_pos - d->R : (int64_t)max_pos;
+    if (row >= row_cap(d))
+        return fail(SWAN_ERR_CAPACITY, "max_pos = %d writes sparse row %lld, capacity is %lld", max_pos,
+                    (long long)row, (long long)row_cap(d));
     if (n_entries > swan::kFusedEntries || n_copies > swan::kFusedCopies) {
         // more than one launch carries: the table update first, then the step's
-        // projection and append (same results, one more launch)
+        // projection and append (same results, one more launch).  Every check
+        // of swan_project_append has passed above, so once the update (which
+        // validates before it enqueues) has launched, the append cannot fail
+        // validation.
         std::vector<int32_t> pairs((size_t)2 * n_copies);
         for (int32_t i = 0; i < n_copies; ++i) {
             pairs[2 * i] = copies[3 * i];
@@ -319,12 +346,6 @@ swan_status swan_project_append_paged(const swan_dims *d, const swan_cache *c, c
         if ((st = swan_paged_update(d, c, block_table, entries, n_entries, pairs.data(), n_copies, stream))) return st;
         return swan_project_append(d, c, q, k, v_hat, pos, max_pos, P_qk, rope_base, q_hat, k_hat, stream);
     }
-    if (!q || !k || !v_hat || !pos || !P_qk || !q_hat || !k_hat) return fail(SWAN_ERR_INVALID_ARG, "NULL array argument");
-    if (!(rope_base > 1.0f)) return fail(SWAN_ERR_INVALID_ARG, "rope_base must be > 1");
-    const int64_t row = d->R > 0 ? (int64_t)max_pos - d->R : (int64_t)max_pos;
-    if (row >= row_cap(d))
-        return fail(SWAN_ERR_CAPACITY, "max_pos = %d writes sparse row %lld, capacity is %lld", max_pos,
-                    (long long)row, (long long)row_cap(d));
     swan::ProjectArgs p{d->B, d->N_h, d->H_kv, q, k, pos, P_qk, rope_base, q_hat, k_hat};
     swan::AppendArgs a;
     a.B = d->B;
@@ -566,6 +587,18 @@ swan_status swan_paged_update(const swan_dims *d, const swan_cache *c, int32_t *
         k += a.n_copies;
     }
     return SWAN_OK;
+}
+
+swan_status swan_measure_stream_read(const void *buf, size_t bytes, int32_t waves, uint32_t *sink, void *stream)
+{
+    if (!buf || !sink) return fail(SWAN_ERR_INVALID_ARG, "NULL buffer or sink");
+    if ((uintptr_t)buf % 16) return fail(SWAN_ERR_INVALID_ARG, "buffer is not 16-byte aligned");
+    if (bytes == 0 || bytes % 16 || bytes > ((size_t)1 << 40))
+        return fail(SWAN_ERR_INVALID_ARG, "bytes = %zu: must be a positive multiple of 16, at most 2^40", bytes);
+    if (waves < 1 || waves > swan::kMaxWaves)
+        return fail(SWAN_ERR_INVALID_ARG, "waves = %d outside 1..%d", waves, swan::kMaxWaves);
+    return hip_status(swan::launch_stream_read(buf, (int64_t)bytes, waves, sink, (hipStream_t)stream),
+                      "swan_measure_stream_read launch");
 }
 
 } // extern "C"

@@ -1,6 +1,6 @@
 // append.hip -- put the new token in the dense buffer; the token leaving the
 // buffer is pruned to its k largest-magnitude coordinates and appended to
-// the sparse history (SWAN section 4.2, hybrid cache and pruning).  The
+// the sparse history (SWAN page, hybrid-cache and pruning paragraphs).  The
 // buffer is circular with slot = position mod R ("Reuse, Evict, or Limit
 // Earlier Context", section 3.2), so the evicted token is exactly the one
 // in the new token's slot.

@@ -1,5 +1,5 @@
 // prefill.hip -- convert a prefilled history into the hybrid cache (the step
-// before decoding starts: SWAN section 4.2 keeps the newest R tokens dense
+// before decoding starts: the SWAN page's hybrid cache keeps the newest R tokens dense
 // and every older one as its pruned sparse row).
 //
 // One workgroup of 256 threads per (32-token tile, kv head, sequence):

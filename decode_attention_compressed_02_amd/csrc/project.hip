@@ -1,6 +1,6 @@
-// project.hip -- runtime projection of the new query and key (SWAN section
-// 4.1: RoPE is position dependent, so RoPE(x) P_QK cannot be folded into the
-// weights and runs every decode step).
+// project.hip -- runtime projection of the new query and key (SWAN page,
+// projection-absorption paragraphs: RoPE is position dependent, so RoPE(x)
+// P_QK cannot be folded into the weights and runs every decode step).
 //
 // One workgroup of 512 threads per (kv head, sequence).  The g query vectors
 // of the GQA group and the new key are rotated by RoPE into LDS; thread

@@ -1,5 +1,5 @@
-// split_kernel.h -- hybrid decode attention (SWAN section 4.2 and appendix A.2,
-// steps 2-4): scores of the rotated query against the sparse history (an
+// split_kernel.h -- hybrid decode attention (SWAN page, hybrid-cache
+// paragraphs and Appendix A.2, steps 2-4): scores of the rotated query against the sparse history (an
 // indexed gather of q_hat) and the dense buffer, one softmax over both, and
 // the output accumulated from sparse values (scatter-add at the stored
 // indices) and dense values.
@@ -602,16 +602,16 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(G, KS > KSV ? KS : KSV))
                 // row slot of row r0 + tl (rows past t1 re-read the last row and
                 // are masked); paged rows whose block-table entry is not a block of
                 // the pool read block 0 and are dropped
-                auto slice = [&](int r0, bool &ok) -> uint32_t {
+                auto slice = [&](int r0, bool &ok) -> int64_t {
                     const int r = min(r0 + tl, t1 - 1);
                     if constexpr (PAGED) {
                         const int blk = a.geom.bt[(int64_t)b * a.geom.max_blocks + r / a.geom.bs];
                         ok = blk >= 0 && blk < a.geom.num_blocks;
-                        const int bb = ok ? blk : 0;
-                        return (uint32_t)((bb * a.H + h) * a.geom.bs + r % a.geom.bs);
+                        const int64_t bb = ok ? blk : 0;
+                        return (bb * a.H + h) * a.geom.bs + r % a.geom.bs;
                     } else {
                         ok = true;
-                        return (uint32_t)r;
+                        return r;
                     }
                 };
                 KSlot<E, VB> rk[D];

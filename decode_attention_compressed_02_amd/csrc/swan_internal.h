@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "swan.h"
+#include "swan_measure.h"
 
 namespace swan {
 
@@ -453,5 +454,9 @@ struct PagedUpdateArgs {
     int32_t copy[kUpdateCopies][2];   // (src, dst)
 };
 hipError_t launch_paged_update(const PagedUpdateArgs &a, hipStream_t s);
+
+// streaming read of a buffer (swan_measure.h): waves one-wave workgroups,
+// bytes a multiple of 16, sink of waves * 64 words
+hipError_t launch_stream_read(const void *buf, int64_t bytes, int waves, uint32_t *sink, hipStream_t s);
 
 } // namespace swan

@@ -62,6 +62,20 @@ def last_dispatches(trace_csv: str, kernel: str, last: int, skip: int = 0):
     return statistics.mean(d), min(d), max(d), len(rows) + skip
 
 
+def dispatch_series(trace_csv: str, kernel: str, first: int, per_bin: int):
+    """Durations (us) of the first `first` dispatches of a kernel in a
+    rocprofv3 kernel_trace.csv, in start order, as (first index, last index,
+    mean, min, max) per bin of `per_bin` dispatches."""
+    rows = [r for r in csv.DictReader(open(trace_csv)) if kernel in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows[:first]]
+    out = []
+    for i in range(0, len(d), per_bin):
+        c = d[i:i + per_bin]
+        out.append((i, i + len(c) - 1, statistics.mean(c), min(c), max(c)))
+    return out, len(rows)
+
+
 def counter_means(counter_csv: str, kernel: str, last: int) -> dict:
     """{counter: mean value per dispatch} over the last `last` dispatches of a
     kernel in a rocprofv3 counter_collection.csv."""
@@ -126,6 +140,11 @@ def main(argv=None):
     l.add_argument("--n", type=int, default=36, help="dispatches at the end of the run (timed + back-to-back)")
     l.add_argument("--skip", type=int, default=0,
                    help="leave out this many dispatches at the very end (bench.py's single-launch timings)")
+    se = sub.add_parser("series")
+    se.add_argument("csv", help="kernel_trace.csv")
+    se.add_argument("--kernel", default="k_split")
+    se.add_argument("--first", type=int, default=300, help="dispatches from the start of the run")
+    se.add_argument("--bin", type=int, default=10, help="dispatches per row")
     c = sub.add_parser("counters")
     c.add_argument("csv", help="counter_collection.csv")
     c.add_argument("--kernel", default="k_split")
@@ -140,6 +159,13 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         print(stats_table(args.csv, args.top))
+    elif args.cmd == "series":
+        bins, total = dispatch_series(args.csv, args.kernel, args.first, args.bin)
+        print(f"{args.kernel}: first {min(args.first, total)} of {total} dispatches, in start order")
+        print("| dispatches | mean us | min us | max us |")
+        print("|---|---|---|---|")
+        for i0, i1, m, lo, hi in bins:
+            print(f"| {i0}-{i1} | {m:.1f} | {lo:.1f} | {hi:.1f} |")
     elif args.cmd == "counters":
         for n, v in counter_means(args.csv, args.kernel, args.n).items():
             print(f"{n}: {v:.6g}")

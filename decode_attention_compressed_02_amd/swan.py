@@ -19,7 +19,8 @@ SWAN_OK, SWAN_ERR_INVALID_ARG, SWAN_ERR_UNSUPPORTED, SWAN_ERR_CAPACITY, SWAN_ERR
 EXPORTS = ("swan_status_str", "swan_last_error", "swan_row_stride", "swan_cache_bytes", "swan_project_qk",
            "swan_append_evict", "swan_decode_workspace_bytes", "swan_decode_num_splits", "swan_decode_attn",
            "swan_decode_split", "swan_decode_reduce", "swan_prefill_convert", "swan_copy_blocks",
-           "swan_project_append", "swan_paged_update", "swan_project_append_paged")
+           "swan_project_append", "swan_paged_update", "swan_project_append_paged",
+           "swan_measure_stream_read")
 
 
 class SwanError(RuntimeError):
@@ -70,6 +71,7 @@ def lib():
             "swan_copy_blocks": ([D, Cc, V, V, I32, V], C.c_int),
             "swan_paged_update": ([D, Cc, V, V, I32, V, I32, V], C.c_int),
             "swan_project_append_paged": ([D, Cc, V, V, V, V, I32, V, F, V, V, V, V, I32, V, I32, V], C.c_int),
+            "swan_measure_stream_read": ([V, SZ, I32, V, V], C.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -232,3 +234,14 @@ def swan_project_append_paged(dims, cache, q, k, v_hat, pos, max_pos, P_qk, rope
                                            _ptr(block_table, torch.int32, "block_table"),
                                            e.ctypes.data_as(C.c_void_p), int(e.shape[0]), c.ctypes.data_as(C.c_void_p),
                                            int(c.shape[0]), _stream(stream)))
+
+
+def swan_measure_stream_read(buf, waves, sink, stream=None):
+    """Streaming read of the whole of `buf` (a contiguous device tensor whose
+    byte size is a multiple of 16) by `waves` one-wave workgroups; sink is a
+    uint32-sized device tensor of at least waves * 64 elements."""
+    nbytes = buf.numel() * buf.element_size()
+    if sink.numel() * sink.element_size() < waves * 64 * 4:
+        raise ValueError("sink must hold waves * 64 uint32 words")
+    _check(lib().swan_measure_stream_read(_ptr(buf, None, "buf"), nbytes, int(waves), _ptr(sink, None, "sink"),
+                                          _stream(stream)))

@@ -5,7 +5,8 @@
  * Compression", arXiv 2511.18936) keeps a small dense buffer of the R most
  * recent rotated keys/values and a large sparse history in which every older
  * rotated key and value keeps only its k largest-magnitude coordinates as
- * (8-bit index, fp16 value) pairs.  One decode step (SWAN section 4.2):
+ * (8-bit index, fp16 value) pairs.  One decode step (SWAN page, hybrid-cache
+ * paragraphs):
  *
  *   1. swan_project_qk    q_hat = RoPE(q) P_QK, k_hat = RoPE(k) P_QK
  *   2. swan_append_evict  put (k_hat, v_hat) in the dense buffer; the token
@@ -28,8 +29,9 @@
  *   nothing and returns a status != SWAN_OK; swan_last_error() (host,
  *   thread-local) describes the failure.  A failed launch returns
  *   SWAN_ERR_HIP.
- * - d_h must be 128 (indices fit in 8 bits, SWAN memory section).  The GQA
- *   group g = N_h / H_kv must be 1, 2, 4 or 8.  1 <= k <= d_h.
+ * - d_h must be 128 (indices fit in 8 bits: SWAN page, memory-savings
+ *   paragraphs).  The GQA group g = N_h / H_kv must be 1, 2, 4 or 8.
+ *   1 <= k <= d_h.
  * - fp16 arrays hold IEEE binary16 bit patterns (uint16_t).
  * - pos[b] (int32, device) is the position (0-based) of the token appended
  *   by this step for sequence b.  After swan_append_evict the cache holds
@@ -107,9 +109,10 @@ typedef struct swan_dims {
 } swan_dims;
 
 /* Storage of the values of sparse rows (the dense buffer is always fp16).
- * FP8_E4M3 is the 8-bit float storage the SWAN page's memory section allows
- * (2k + 2 bytes a vector) in the OCP E4M3 encoding (exponent bias 7, 3
- * fraction bits, largest finite value 448, no infinities), with no scale:
+ * FP8_E4M3 is the 8-bit float storage the SWAN page's memory-savings
+ * paragraphs allow (2k + 2 bytes a vector) in the OCP E4M3 encoding
+ * (exponent bias 7, 3 fraction bits, largest finite value 448, no
+ * infinities), with no scale:
  * a pruned row keeps the same coordinates as with fp16 values (chosen on the
  * fp16 magnitudes) and each kept value is rounded from fp16 to nearest even,
  * saturating at +-448. */
@@ -142,8 +145,9 @@ int32_t swan_row_stride(int32_t k);
 swan_status swan_cache_bytes(const swan_dims *dims, size_t out[5]);
 
 /*
- * Step 1 -- runtime projection (SWAN section 4.1: RoPE cannot be absorbed
- * into W_Q / W_K, so q -> RoPE(q) -> RoPE(q) P_QK runs every step).
+ * Step 1 -- runtime projection (SWAN page, projection-absorption paragraphs:
+ * RoPE cannot be absorbed into W_Q / W_K, so q -> RoPE(q) -> RoPE(q) P_QK
+ * runs every step).
  *   q      float32 [B][N_h][128]   raw queries (before RoPE)
  *   k      float32 [B][H_kv][128]  raw new keys (before RoPE)
  *   pos    int32   [B]             rotation position of each sequence
@@ -160,12 +164,14 @@ swan_status swan_project_qk(const swan_dims *dims, const float *q, const float *
                             const float *P_qk, float rope_base, float *q_hat, uint16_t *k_hat, void *stream);
 
 /*
- * Step 2 -- append the new token, evict and prune (SWAN section 4.2: when the
- * buffer exceeds its capacity the oldest vectors are evicted, pruned to their
- * top-k magnitude coordinates and appended to the sparse cache).
+ * Step 2 -- append the new token, evict and prune (SWAN page, hybrid-cache
+ * and pruning paragraphs: when the buffer exceeds its capacity the oldest
+ * vectors are evicted, pruned to their top-k magnitude coordinates and
+ * appended to the sparse cache).
  *   k_hat  fp16    [B][H_kv][128]  rotated new keys (from swan_project_qk)
  *   v_hat  float32 [B][H_kv][128]  new values, already in the rotated basis
- *                                  (P_VO absorbed into W_V, SWAN section 4.1);
+ *                                  (P_VO absorbed into W_V: SWAN page,
+ *                                  projection-absorption paragraphs);
  *                                  rounded to fp16 (nearest even) on store
  * For R > 0 the token at pos - R (if pos >= R) is read from slot pos mod R,
  * pruned into sparse row pos - R, and the new token takes the slot.  For
@@ -206,8 +212,8 @@ size_t swan_decode_workspace_bytes(const swan_dims *dims, int32_t max_pos);
 int32_t swan_decode_num_splits(const swan_dims *dims, int32_t max_pos);
 
 /*
- * Step 3 -- hybrid decode attention (SWAN section 4.2 and appendix A.2,
- * steps 2-4).  For every query head of sequence b, over the n_b sparse and
+ * Step 3 -- hybrid decode attention (SWAN page, hybrid-cache paragraphs and
+ * Appendix A.2, steps 2-4).  For every query head of sequence b, over the n_b sparse and
  * min(pos[b] + 1, R) buffered tokens of its kv head:
  *   s_t = (sum_i q_hat[idx_t,i] val_t,i) / sqrt(128)  for sparse tokens
  *   s_t = (q_hat . k_t) / sqrt(128)                    for buffered tokens

@@ -14,10 +14,10 @@
  *
  * Arithmetic is IEEE double throughout.  The only places a value is rounded
  * to binary16 are where the method stores it in the cache: the rotated key and
- * the value when they enter the dense buffer ([SWAN] section 4.2: values are
- * stored as float16, section 5.1).  Stored values are kept as doubles that are
+ * the value when they enter the dense buffer ([SWAN] hybrid-cache paragraphs;
+ * values are stored as float16 per its memory-savings paragraphs).  Stored values are kept as doubles that are
  * exactly representable in binary16, so widening them back is exact.  With
- * 8-bit sparse values (section 5.1) the values a pruned row keeps are rounded
+ * 8-bit sparse values (memory-savings paragraphs) the values a pruned row keeps are rounded
  * once more, to E4M3, when they enter the sparse cache.
  *
  * Readings where the pages are silent (each also listed in the design notes):
@@ -50,8 +50,8 @@
 /* Round a double to the nearest binary16 value, ties to even (IEEE 754
  * roundTiesToEven), returned as a double.  binary16 has 10 fraction bits,
  * normal exponents -14..15 and subnormal spacing 2^-24; magnitudes that round
- * past the largest finite value 65504 become infinity.  Used where [SWAN]
- * section 5.1 stores values as float16. */
+ * past the largest finite value 65504 become infinity.  Used where the
+ * memory-savings paragraphs of [SWAN] store values as float16. */
 double so_round_f16(double x)
 {
     if (isnan(x) || isinf(x) || x == 0.0)
@@ -77,8 +77,9 @@ void so_round_f16_array(long n, const double *x, double *y)
 }
 
 /* ------------------------------------------------------------------------ */
-/* 8-bit float sparse values ([SWAN] section 5.1: the values kept in a      */
-/* sparse vector may be stored as 8-bit floats, 2k + 2 bytes a vector)      */
+/* 8-bit float sparse values ([SWAN] memory-savings paragraphs: the values */
+/* kept in a
+/* sparse vector may be stored as 8-bit floats, 2k + 2 bytes a vector)    */
 /* ------------------------------------------------------------------------ */
 
 /* Round a double to the nearest E4M3 value, ties to even.  The pages name
@@ -113,10 +114,11 @@ void so_round_e4m3_array(long n, const double *x, double *y)
 }
 
 /* ------------------------------------------------------------------------ */
-/* Runtime projection: q -> RoPE(q) -> RoPE(q) P_QK   ([SWAN] section 4.1) */
+/* Runtime projection: q -> RoPE(q) -> RoPE(q) P_QK                        */
+/* ([SWAN] projection-absorption paragraphs)                                */
 /* ------------------------------------------------------------------------ */
 
-/* Rotary position embedding (Su et al., as cited in [SWAN] section 4.1):
+/* Rotary position embedding (Su et al., as cited in the [SWAN] projection-absorption paragraphs):
  * each pair (x_i, x_{i+d/2}) is rotated by the angle pos * base^(-2i/d). */
 void so_rope(int d, const double *x, double pos, double base, double *y)
 {
@@ -141,7 +143,7 @@ void so_rowvec_mat(int d, const double *x, const double *P, double *y)
     }
 }
 
-/* x_hat = RoPE(x, pos) P  ([SWAN] section 4.1: the projection follows RoPE). */
+/* x_hat = RoPE(x, pos) P  ([SWAN] projection-absorption paragraphs: the projection follows RoPE). */
 void so_project(int d, const double *x, double pos, double base, const double *P, double *y)
 {
     double tmp[512];
@@ -150,7 +152,7 @@ void so_project(int d, const double *x, double pos, double base, const double *P
 }
 
 /* ------------------------------------------------------------------------ */
-/* Magnitude top-k pruning  ([SWAN] section 4.2, pruning paragraph)          */
+/* Magnitude top-k pruning  ([SWAN] pruning paragraph)                      */
 /* ------------------------------------------------------------------------ */
 
 typedef struct { double mag; int idx; } so_key;
@@ -190,7 +192,8 @@ void so_prune(int d, int k, const double *x, uint8_t *idx, double *val)
 
 /* ------------------------------------------------------------------------ */
 /* Hybrid attention of one (sequence, kv-head) unit                          */
-/* ([SWAN] section 4.2 and appendix A.2 steps 2-4; decode formula sec. 3)    */
+/* ([SWAN] hybrid-cache paragraphs and Appendix A.2 steps 2-4; the decode  */
+/* formula of its background on autoregressive generation)                  */
 /* ------------------------------------------------------------------------ */
 
 /* For each of the g query heads sharing this kv-head:
@@ -261,8 +264,8 @@ static size_t unit_off(int b, int h, int H, size_t per) { return ((size_t)b * H 
 
 /* Move one token's stored (rounded) key/value into the cache at position
  * pos, evicting and pruning the token that leaves the buffer ([SWAN]
- * section 4.2: the oldest buffered vectors are evicted, pruned and appended
- * to the sparse cache). */
+ * hybrid-cache paragraphs: the oldest buffered vectors are evicted, pruned
+ * and appended to the sparse cache). */
 /* Prune x into a sparse row and store its kept values in the sparse value
  * format: binary16 as they are (vfmt 0) or rounded to E4M3 (vfmt 1). */
 static void so_prune_store(int d, int k, int vfmt, const double *x, uint8_t *idx, double *val)
@@ -396,7 +399,7 @@ void so_decode_batch(int B, int N, int H, int d, int R, int k, int kv, long ncap
         }
 }
 
-/* One whole decode step ([SWAN] section 4.2, in its order): project the new
+/* One whole decode step ([SWAN] hybrid-cache paragraphs, in their order): project the new
  * query and key, append the rounded key and value (evicting and pruning the
  * oldest buffered token), then attend.  Outputs qhat (double, unrounded),
  * khat (binary16-rounded) and out.  Returns nonzero on sparse overflow. */

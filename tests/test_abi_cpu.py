@@ -16,9 +16,14 @@ from decode_attention_compressed_02_amd import swan as S  # noqa: E402
 
 
 def declared_functions():
-    txt = open(os.path.join(ROOT, "include", "swan.h")).read()
-    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(swan_[a-z0-9_]+)\s*\(", txt)))
+    """Every function the headers under include/ declare."""
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", h)).read()
+            txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+            names |= set(re.findall(r"\b(swan_[a-z0-9_]+)\s*\(", txt))
+    return sorted(names)
 
 
 def test_header_and_binding_agree():
@@ -50,6 +55,14 @@ def test_row_stride_and_sizes():
     da = S.make_dims(2, 8, 2, 16, 77, n_cap=100, k_v=51)
     rows = 2 * 2 * 100
     assert S.swan_cache_bytes(da) == (rows * 128, rows * 256, rows * 64, rows * 128, 2 * 2 * 16 * 128 * 2)
+
+
+def test_size_limits():
+    # the largest contiguous unit a 32-bit buffer range covers: 2^24 - 1 rows of 128 fp16 entries
+    assert S.swan_cache_bytes(S.make_dims(1, 4, 1, 0, 128, n_cap=(1 << 24) - 1))[1] == ((1 << 24) - 1) * 256
+    # paged row slots are 64-bit: a pool of more than 2^31 rows (of 8-entry rows) is accepted
+    d = S.make_dims(4, 8, 8, 64, 8, block_size=16, max_blocks=1 << 20, num_blocks=1 << 24)
+    assert S.swan_cache_bytes(d)[0] == (1 << 24) * 8 * 16 * 8
 
 
 def test_split_plan():
@@ -279,6 +292,29 @@ cases += [
     ("paged step null v_hat", pap(pdims(), vh=N), E),
     ("paged step capacity", pap(pdims(), max_pos=16 * 4 + 16), CAP),
     ("paged step g = 3", pap(dims(N_h=6, H_kv=2, block_size=16, max_blocks=4, num_blocks=8)), U),
+    # more than 32 copies or 192 entries take two launches; every argument is
+    # still checked before the first of them is enqueued
+    ("paged step 33 copies, null v_hat", pap(pdims(), copies=pairs(*([1, 2, 0] * 33)), nc=33, vh=N), E),
+    ("paged step 33 copies, rope base", pap(pdims(), copies=pairs(*([1, 2, 0] * 33)), nc=33, base=1.0), E),
+    ("paged step 200 entries, capacity", pap(pdims(), entries=pairs(*([0, 3] * 200)), ne=200, max_pos=16 * 4 + 16), CAP),
+    ("paged step 200 entries, null q", pap(pdims(), entries=pairs(*([0, 3] * 200)), ne=200, q=N), E),
+    # sizes the kernels' 32-bit quantities cannot address
+    ("paged table slots past int32", proj(dims(B=65535, block_size=1, max_blocks=40000, num_blocks=8)), U),
+    ("paged rows a sequence past int32", proj(dims(block_size=1 << 16, max_blocks=1 << 16, num_blocks=8)), U),
+    ("contiguous unit plane of 2^32 bytes", dec(dims(k=128, n_cap=1 << 24)), U),
+    ("contiguous unit value plane of 2^32 bytes (k_v wider)", proj(dims(k=8, k_v=16, n_cap=1 << 27)), U),
+]
+def sread(buf=0x1000, nbytes=1 << 20, waves=64, sink=0x2000):
+    return L.swan_measure_stream_read(C.c_void_p(buf) if buf else None, nbytes, waves,
+                                      C.c_void_p(sink) if sink else None, st)
+cases += [
+    ("stream read null buffer", sread(buf=0), E),
+    ("stream read null sink", sread(sink=0), E),
+    ("stream read misaligned", sread(buf=0x1008), E),
+    ("stream read 0 bytes", sread(nbytes=0), E),
+    ("stream read odd bytes", sread(nbytes=1000), E),
+    ("stream read 0 waves", sread(waves=0), E),
+    ("stream read too many waves", sread(waves=(1 << 20) + 1), E),
 ]
 bad = [(n, got, want) for n, got, want in cases if got != want]
 for n, got, want in bad: print("MISMATCH", n, got, want)

@@ -35,11 +35,46 @@ def _gpu():
     S.lib()
 
 
-def _samples(w):
+def _straddling(w, dims, pos):
+    """Sequences whose units share split-pass waves with the units before and
+    after them: unit (b, 0) starts and unit (b, H_kv - 1) ends strictly inside a
+    wave's range of work rows.  The plan is the one include/swan.h describes
+    (work rows of a unit: its sparse rows plus its buffered tokens weighted by
+    their bytes; V waves over equal shares of the batch)."""
+    ks, ksv = S.swan_row_stride(w.k), S.swan_row_stride(w.k_v or w.k)
+    row_bytes = (1 + (1 if w.value_format else 2)) * (ks + ksv)
+    lens = []
+    for p in pos:
+        ctx = int(p) + 1
+        n, f = max(ctx - w.R, 0), (0 if ctx <= 0 else min(ctx, w.R))
+        lens.append(n + -(-f * 512 // row_bytes))
+    H = w.H_kv
+    T = H * sum(lens)
+    V = min(S.swan_decode_num_splits(dims, int(max(pos))), T // 64) if dims.split_tokens == 0 else None
+    assert V is not None and V >= 1
+    inside = lambda x: (x * V) % T != 0  # x is not a wave boundary w T / V
+    out, start = [], 0
+    for b, L in enumerate(lens):
+        if L and inside(start) and inside(start + H * L):
+            out.append(b)
+        start += H * L
+    return out
+
+
+def _samples(w, dims):
+    """Sequences the oracle runs: the ends of the batch, a middle sequence,
+    and for ragged batches the shortest, the longest and the two sequences
+    nearest the middle whose units straddle waves shared with their
+    neighbours (where the work plan and the merge index pieces hardest)."""
     ctx = np.asarray(w.ctx)
     if w.B <= 4:
-        return [w.B - 1]
-    return sorted({int(np.argmax(ctx)), int(np.argmin(ctx)), w.B - 1} if len(set(w.ctx)) > 1 else {0, w.B - 1})
+        return sorted({1 % w.B, w.B - 1})
+    if len(set(w.ctx)) == 1:
+        return sorted({0, w.B // 2 - 1, w.B - 1})
+    pos = wl.step_inputs(w, 0)[3]
+    mid = sorted(_straddling(w, dims, pos), key=lambda b: abs(b - w.B // 2))[:2]
+    assert len(mid) == 2, "a ragged batch with no straddling middle units"
+    return sorted({int(np.argmax(ctx)), int(np.argmin(ctx)), w.B - 1, *mid})
 
 
 def _oracle_for(w, seqs):
@@ -97,9 +132,10 @@ def test_full_size_steps(cfg):
         w = w.scaled(value_format=1)
     if str(cfg).endswith("kv"):  # its 2k budget split 60/40 between keys and values (77 / 51)
         w = w.scaled(k=77, k_v=51)
-    seqs = _samples(w)
-    print(f"\n[fullsize] workload {cfg}: {w.name} B={w.B} samples={seqs}", flush=True)
+    print(f"\n[fullsize] workload {cfg}: {w.name} B={w.B}", flush=True)
     dec = build_decoder(w, extra_steps=STEPS)
+    seqs = _samples(w, dec.dims)
+    print(f"[fullsize] samples {seqs}", flush=True)
     print(f"[fullsize] GPU state built; split waves "
           f"{S.swan_decode_num_splits(dec.dims, int(max(w.ctx)) + STEPS)}", flush=True)
     oc = _oracle_for(w, seqs)
