@@ -5,6 +5,7 @@
 
 #include "swan_internal.h"
 
+#include <mutex>
 #include <vector>
 
 namespace {
@@ -159,8 +160,8 @@ size_t workspace_bytes(const swan_dims *d, const Plan &p)
     return partial_count(d, p) * (swan::kD + 2) * sizeof(float);
 }
 
-swan_status check_decode(const swan_dims *d, const swan_cache *c, const int32_t *pos, int32_t max_pos,
-                         const void *ws, size_t ws_bytes, Plan *out)
+// the checks of a decode call other than its workspace's, and its plan
+swan_status check_decode_plan(const swan_dims *d, const swan_cache *c, const int32_t *pos, int32_t max_pos, Plan *out)
 {
     swan_status st = check_dims(d);
     if (st) return st;
@@ -174,9 +175,57 @@ swan_status check_decode(const swan_dims *d, const swan_cache *c, const int32_t 
     if (out->W > swan::kMaxWaves)
         return fail(SWAN_ERR_INVALID_ARG, "split_tokens = %d gives %d waves, at most %d are supported", d->split_tokens,
                     out->W, swan::kMaxWaves);
+    return SWAN_OK;
+}
+
+swan_status check_decode(const swan_dims *d, const swan_cache *c, const int32_t *pos, int32_t max_pos,
+                         const void *ws, size_t ws_bytes, Plan *out)
+{
+    swan_status st = check_decode_plan(d, c, pos, max_pos, out);
+    if (st) return st;
     if (!ws) return fail(SWAN_ERR_INVALID_ARG, "workspace is NULL");
     if (ws_bytes < workspace_bytes(d, *out))
         return fail(SWAN_ERR_INVALID_ARG, "workspace of %zu bytes, need %zu", ws_bytes, workspace_bytes(d, *out));
+    return SWAN_OK;
+}
+
+// The partials of swan_decode_attn_noalloc: a file-scope device array, one
+// copy on every GPU the library runs on, held until the process ends.  Host
+// code never uses its name as an address (on the host the name stands for a
+// host-side shadow): the address on each device comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+constexpr size_t kScratchBytes = SWAN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices]; // address of `scratch` per device, null until looked up
+
+// the scratch array of the device `stream` runs on, which must be the
+// current device (the symbol's address is looked up on the current device)
+swan_status scratch_for(hipStream_t stream, void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if ((e = hipStreamGetDevice(stream, &sdev)) != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+        if ((int)sdev != dev)
+            return fail(SWAN_ERR_INVALID_ARG, "stream belongs to device %d, the current device is %d", (int)sdev, dev);
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SWAN_ERR_UNSUPPORTED, "device %d: the no-allocation scratch serves devices 0..%d", dev,
+                    kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess)
+            return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(SWAN_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return SWAN_OK;
 }
 
@@ -461,6 +510,27 @@ swan_status swan_decode_attn(const swan_dims *d, const swan_cache *c, const int3
     if (!q_hat || !o_hat) return fail(SWAN_ERR_INVALID_ARG, "NULL array argument");
     if ((st = swan_decode_split(d, c, pos, max_pos, q_hat, ws, ws_bytes, stream))) return st;
     return swan_decode_reduce(d, pos, max_pos, ws, ws_bytes, o_hat, stream);
+}
+
+swan_status swan_decode_attn_noalloc(const swan_dims *d, const swan_cache *c, const int32_t *pos, int32_t max_pos,
+                                     const float *q_hat, float *o_hat, void *stream)
+{
+    Plan p;
+    swan_status st = check_decode_plan(d, c, pos, max_pos, &p);
+    if (st) return st;
+    if (!c) return fail(SWAN_ERR_INVALID_ARG, "cache is NULL");
+    if (!q_hat || !o_hat) return fail(SWAN_ERR_INVALID_ARG, "NULL array argument");
+    const size_t need = workspace_bytes(d, p);
+    if (need > kScratchBytes)
+        return fail(SWAN_ERR_CAPACITY, "the split pass needs %zu bytes of partials, the no-allocation scratch holds "
+                                       "%zu (swan_decode_attn takes a workspace of any size)", need, kScratchBytes);
+    void *ws = nullptr;
+    if ((st = scratch_for((hipStream_t)stream, &ws))) return st;
+    // the same two launches as swan_decode_attn, over the scratch array; the
+    // split pass writes every partial the reduce pass reads, so nothing is
+    // cleared between calls
+    if ((st = swan_decode_split(d, c, pos, max_pos, q_hat, ws, kScratchBytes, stream))) return st;
+    return swan_decode_reduce(d, pos, max_pos, ws, kScratchBytes, o_hat, stream);
 }
 
 swan_status swan_prefill_convert(const swan_dims *d, const swan_cache *c, const int32_t *len, int32_t max_len,

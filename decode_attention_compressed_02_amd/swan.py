@@ -20,7 +20,7 @@ EXPORTS = ("swan_status_str", "swan_last_error", "swan_row_stride", "swan_cache_
            "swan_append_evict", "swan_decode_workspace_bytes", "swan_decode_num_splits", "swan_decode_attn",
            "swan_decode_split", "swan_decode_reduce", "swan_prefill_convert", "swan_copy_blocks",
            "swan_project_append", "swan_paged_update", "swan_project_append_paged",
-           "swan_measure_stream_read")
+           "swan_measure_stream_read", "swan_decode_attn_noalloc")
 
 
 class SwanError(RuntimeError):
@@ -72,6 +72,7 @@ def lib():
             "swan_paged_update": ([D, Cc, V, V, I32, V, I32, V], C.c_int),
             "swan_project_append_paged": ([D, Cc, V, V, V, V, I32, V, F, V, V, V, V, I32, V, I32, V], C.c_int),
             "swan_measure_stream_read": ([V, SZ, I32, V, V], C.c_int),
+            "swan_decode_attn_noalloc": ([D, Cc, V, I32, V, V, V], C.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -163,6 +164,14 @@ def swan_decode_attn(dims, cache, pos, max_pos, q_hat, o_hat, workspace, stream=
                                   _ptr(q_hat, torch.float32, "q_hat"), _ptr(o_hat, torch.float32, "o_hat"),
                                   _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
                                   _stream(stream)))
+
+
+def swan_decode_attn_noalloc(dims, cache, pos, max_pos, q_hat, o_hat, stream=None):
+    """swan_decode_attn over the library's per-GPU scratch array: no workspace argument."""
+    import torch
+    _check(lib().swan_decode_attn_noalloc(C.byref(dims), C.byref(cache), _ptr(pos, torch.int32, "pos"), int(max_pos),
+                                          _ptr(q_hat, torch.float32, "q_hat"), _ptr(o_hat, torch.float32, "o_hat"),
+                                          _stream(stream)))
 
 
 def swan_decode_split(dims, cache, pos, max_pos, q_hat, workspace, stream=None):

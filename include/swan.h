@@ -231,6 +231,32 @@ swan_status swan_decode_attn(const swan_dims *dims, const swan_cache *cache, con
                              const float *q_hat, float *o_hat, void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/*
+ * swan_decode_attn without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops that must not
+ * call hipMalloc, harnesses that forbid allocation).  Same arguments, checks
+ * and results as swan_decode_attn, and the same two kernels; the split
+ * pass's partials go to a scratch array the library holds on every GPU it
+ * runs on: SWAN_NOALLOC_SCRATCH_BYTES (16 MiB) of device memory reserved
+ * when the library's code is loaded on that GPU and kept until the process
+ * ends.  The call allocates nothing.
+ *   - SWAN_ERR_CAPACITY when the plan's partials (swan_decode_workspace_bytes
+ *     for these dims and max_pos) exceed the scratch size: about 8000 pieces
+ *     of work at g = 4 (the automatic plan of a batch with up to ~6000
+ *     (sequence, kv head) units), half that at g = 8.
+ *   - `stream` must belong to the current device (SWAN_ERR_INVALID_ARG
+ *     otherwise); the scratch address of a device is looked up on the first
+ *     call on it.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap
+ *     (on different streams, or enqueued from several host threads without
+ *     ordering) race and give wrong results.  Calls ordered on one stream are
+ *     safe; each writes every partial it reads, so nothing carries over from
+ *     the previous call.
+ */
+#define SWAN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+swan_status swan_decode_attn_noalloc(const swan_dims *dims, const swan_cache *cache, const int32_t *pos,
+                                     int32_t max_pos, const float *q_hat, float *o_hat, void *stream);
+
 /* The two halves of swan_decode_attn, for callers that time or schedule them
  * separately: the split pass writes per-piece partials to the workspace, the
  * reduce pass merges them into o_hat.  Same arguments and checks; the two

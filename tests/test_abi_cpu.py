@@ -316,6 +316,16 @@ cases += [
     ("stream read 0 waves", sread(waves=0), E),
     ("stream read too many waves", sread(waves=(1 << 20) + 1), E),
 ]
+def noalloc(d, c=cache, max_pos=50, **kw):
+    a = dict(pos=F, qh=F, oh=F); a.update(kw)
+    return L.swan_decode_attn_noalloc(C.byref(d), C.byref(c), a['pos'], max_pos, a['qh'], a['oh'], st)
+cases += [
+    ("noalloc null q_hat", noalloc(dims(), qh=N), E),
+    ("noalloc null cache plane", noalloc(dims(), c=nocache), E),
+    ("noalloc capacity", noalloc(dims(), max_pos=100 + 16), CAP),
+    # partials of 300k-row units at 64 work rows a wave: ~39 MB, beyond the 16 MiB scratch
+    ("noalloc plan beyond the scratch", noalloc(dims(split_tokens=64, n_cap=300000), max_pos=300000), CAP),
+]
 bad = [(n, got, want) for n, got, want in cases if got != want]
 for n, got, want in bad: print("MISMATCH", n, got, want)
 print("OK" if not bad else "FAIL", len(cases))
