@@ -103,6 +103,9 @@ def main():
                          "before kernels run at their steady speed (0 = no settle phase)")
     ap.add_argument("--config", type=int, default=3, help="workload number (1-5); 3 is the headline")
     ap.add_argument("--split-tokens", type=int, default=0, help="work rows per wave (0 = automatic)")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="layers stacked along the batch (each the workload's batch, drawn from its own seed): "
+                         "one launch of each kernel serves all of them")
     ap.add_argument("--values", choices=("fp16", "fp8"), default="fp16",
                     help="storage of the sparse values (fp8: E4M3, one byte each)")
     ap.add_argument("--kv-share", type=float, default=0.0,
@@ -130,7 +133,7 @@ def main():
     from decode_attention_compressed_02_amd import accounting as acc
     from decode_attention_compressed_02_amd import swan as S
     from decode_attention_compressed_02_amd import workloads as wl
-    from decode_attention_compressed_02_amd.state import build_decoder
+    from decode_attention_compressed_02_amd.state import build_decoder, step_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -146,13 +149,16 @@ def main():
     vbytes = 1 if w.value_format else 2
     if args.steps > w.steps:
         w = w.scaled(steps=args.steps)
+    if args.layers > 1:
+        w = w.scaled(layers=args.layers)
+    L = max(1, w.layers)
     dec = build_decoder(w, args.split_tokens)
     log(f"device {torch.cuda.get_device_name(0)}; dims {dec.dims}")
 
     # step inputs for every step, resident in HBM before timing
     inputs, pos_host = [], []
     for s in range(args.steps):
-        q, kr, vn, pos = wl.step_inputs(w, s)
+        q, kr, vn, pos = step_inputs(w, s)
         inputs.append(tuple(torch.from_numpy(a).cuda() for a in (q, kr, vn, pos)) + (int(pos.max()),))
         pos_host.append(pos)
     paged = w.block_size > 0
@@ -226,7 +232,7 @@ def main():
         torch.cuda.synchronize()
         return time.perf_counter() - t0
 
-    tokens = sum(int(inputs[s][3].sum().item()) + w.B for s in range(args.steps))  # sum_b (pos_b + 1)
+    tokens = sum(int(inputs[s][3].sum().item()) + inputs[s][3].numel() for s in range(args.steps))  # sum (pos + 1)
     # algorithmic bytes of the split kernel per launch, per timed step
     split_bytes, dec_bytes, flops = [], [], []
     for s in range(args.steps):
@@ -304,7 +310,7 @@ def main():
         S.swan_decode_split(dec.dims, dec.cache.struct(), pos, mp, dec.q_hat, dec.workspace)
         S.swan_decode_reduce(dec.dims, pos, mp, dec.workspace, dec.o_hat)
     decode_ms = back_to_back(decode_launch)
-    last_tokens = int(inputs[args.steps - 1][3].sum().item()) + w.B
+    last_tokens = int(inputs[args.steps - 1][3].sum().item()) + inputs[args.steps - 1][3].numel()
 
     # the split kernel from a cold last-level cache: before every other one of
     # these launches a 1 GiB fill evicts the L2s and the 256 MB MALL, so a
@@ -386,9 +392,11 @@ def main():
         "data": "synthetic (seeded N(0,1) raw keys/queries, stored-basis values, random orthogonal P_QK)",
         "config": {"workload": f"workload {args.config}: {base_name}" + (", fp8 values" if w.value_format else "")
                    + (f", k_K {w.k} / k_V {w.k_v}" if w.k_v else "")
+                   + (f", {L} layers stacked in one batch" if L > 1 else "")
                    + f", {args.steps} consecutive decode steps timed",
                    "B": w.B, "N_h": w.N_h, "H_kv": w.H_kv,
                    "d_h": w.d_h, "ctx_first_step": int(w.ctx[0]), "R": w.R, "k": w.k, "k_v": w.k_v or w.k,
+                   "layers": L,
                    "storage": f"{'fp8 E4M3' if w.value_format else 'fp16'} values, uint8 indices, fp16 dense buffer",
                    "split_waves": nsplit,
                    "split_tokens": dec.dims.split_tokens or "auto",
@@ -398,6 +406,7 @@ def main():
         "step_hbm_GBps": float(np.mean(dec_bytes)) / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": float(np.mean(dec_bytes)) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "head_tokens_per_s": value * w.H_kv,
+        "ms_per_step_per_layer": ms_step / L,
         "decode_ms_back_to_back": decode_ms,
         "decode_kv_tokens_per_s": last_tokens / (decode_ms * 1e-3),
         "decode_frac_of_peak": float(dec_bytes[-1]) / (decode_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,

@@ -52,6 +52,22 @@ class HybridCache:
                                         p(self.k_buf), p(self.v_buf), p(self.block_table))
         return self._struct
 
+    def sub_struct(self, b0: int) -> S.swan_cache:
+        """The planes as seen by a batch starting at sequence b0 (the layers of
+        a multi-layer batch one at a time): contiguous planes and the dense
+        buffers offset to sequence b0; a paged pool is shared by all
+        sequences, so only its block table is offset (to row b0)."""
+        d, base = self.dims, self.struct()
+        ring = b0 * d.H_kv * d.R * 128 * 2
+        if d.block_size > 0:
+            return S.swan_cache(base.k_idx, base.k_val, base.v_idx, base.v_val, base.k_buf + ring,
+                                base.v_buf + ring, base.block_table + b0 * d.max_blocks * 4)
+        vb = 1 if d.value_format == S.SWAN_VALUES_FP8_E4M3 else 2
+        rows = b0 * d.H_kv * d.n_cap
+        return S.swan_cache(base.k_idx + rows * self.k_stride, base.k_val + rows * self.k_stride * vb,
+                            base.v_idx + rows * self.v_stride, base.v_val + rows * self.v_stride * vb,
+                            base.k_buf + ring, base.v_buf + ring, None)
+
     # shaped views for inspection: (k_idx, k_val, v_idx, v_val), rows of the
     # key and the value stride
     def sparse_views(self):
@@ -368,25 +384,31 @@ class PagedSwanDecoder(SwanDecoder):
         return self.decode(pos, int(max(pos_host)), stream)
 
 
-def shared_prefix_pool(B: int, rows, steps: int, block_size: int, prefix_rows: int, order_fn, slack: int = 0):
-    """A pool for B sequences holding rows[b] sparse rows each, whose first
-    prefix_rows rows are the same tokens in every sequence: sequence 0 owns
-    the prefix blocks and every other sequence maps them too (reference count
-    B); all other blocks are private.  Blocks come from the permutation
-    order_fn(num_blocks) of the pool.  The pool has room for `steps` more rows
-    per sequence (plus copy-on-write of one prefix block each) and `slack`
-    spare blocks."""
+def shared_prefix_pool(B: int, rows, steps: int, block_size: int, prefix_rows: int, order_fn, slack: int = 0,
+                       groups: int = 1):
+    """A pool for B sequences holding rows[b] sparse rows each, in `groups`
+    consecutive groups of B / groups sequences (the layers of a multi-layer
+    batch) whose first prefix_rows rows are the same tokens in every sequence
+    of the group: the group's first sequence owns the prefix blocks and the
+    others map them too (reference count B / groups); all other blocks are
+    private.  Blocks come from the permutation order_fn(num_blocks) of the
+    pool.  The pool has room for `steps` more rows per sequence (plus
+    copy-on-write of one prefix block each) and `slack` spare blocks."""
     bs = block_size
+    if groups < 1 or B % groups:
+        raise ValueError("groups must divide B")
+    gB = B // groups
     prefix_blocks = -(-prefix_rows // bs) if prefix_rows > 0 else 0
     have = [-(-int(r) // bs) for r in rows]
     need = [-(-(int(r) + steps) // bs) for r in rows]
     max_blocks = max(1, max(need))
-    num_blocks = prefix_blocks + sum(max(0, n - prefix_blocks) for n in need) + B + slack
+    num_blocks = groups * prefix_blocks + sum(max(0, n - prefix_blocks) for n in need) + B + slack
     pool = PagedPool(num_blocks, B, max_blocks, bs, order=order_fn(num_blocks))
-    for lb in range(max(have[0], min(prefix_blocks, max_blocks))):
-        pool.map_new(0, lb)
-    for b in range(1, B):
-        pool.share(0, b, min(prefix_blocks, have[b], have[0]))
-        for lb in range(min(prefix_blocks, have[b], have[0]), have[b]):
-            pool.map_new(b, lb)
+    for g0 in range(0, B, gB):
+        for lb in range(max(have[g0], min(prefix_blocks, max_blocks))):
+            pool.map_new(g0, lb)
+        for b in range(g0 + 1, g0 + gB):
+            pool.share(g0, b, min(prefix_blocks, have[b], have[g0]))
+            for lb in range(min(prefix_blocks, have[b], have[g0]), have[b]):
+                pool.map_new(b, lb)
     return pool

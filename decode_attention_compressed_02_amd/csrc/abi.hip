@@ -73,6 +73,8 @@ swan_status check_dims(const swan_dims *d)
             return fail(SWAN_ERR_UNSUPPORTED, "k = %d and k_v = %d: stored row widths %d and %d, supported when equal "
                                               "or one twice the other", d->k, d->k_v, ks, ksv);
     }
+    if (d->layers < 0 || (d->layers > 1 && d->B % d->layers))
+        return fail(SWAN_ERR_INVALID_ARG, "layers = %d: must be 0 or 1 (one layer) or divide B = %d", d->layers, d->B);
     if (d->block_size == 0) {
         // the decode reads a unit's rows of each plane through one buffer
         // resource, whose byte range is 32-bit
@@ -87,6 +89,8 @@ swan_status check_dims(const swan_dims *d)
 }
 
 int value_bytes(const swan_dims *d) { return d->value_format == SWAN_VALUES_FP8_E4M3 ? 1 : 2; }
+// sequences of one layer: the batch holds `layers` layers' sequences, layer-major
+int layer_seqs(const swan_dims *d) { return d->layers > 1 ? d->B / d->layers : d->B; }
 // kept value coordinates (k unless keys and values keep different counts)
 int kept_v(const swan_dims *d) { return d->k_v > 0 ? d->k_v : d->k; }
 int row_bytes(const swan_dims *d)
@@ -272,7 +276,7 @@ swan_status swan_project_qk(const swan_dims *d, const float *q, const float *k, 
     if (st) return st;
     if (!q || !k || !pos || !P_qk || !q_hat || !k_hat) return fail(SWAN_ERR_INVALID_ARG, "NULL array argument");
     if (!(rope_base > 1.0f)) return fail(SWAN_ERR_INVALID_ARG, "rope_base must be > 1");
-    swan::ProjectArgs a{d->B, d->N_h, d->H_kv, q, k, pos, P_qk, rope_base, q_hat, k_hat};
+    swan::ProjectArgs a{d->B, d->N_h, d->H_kv, q, k, pos, P_qk, rope_base, q_hat, k_hat, layer_seqs(d)};
     return hip_status(swan::launch_project(a, (hipStream_t)stream), "swan_project_qk launch");
 }
 
@@ -319,7 +323,7 @@ swan_status swan_project_append(const swan_dims *d, const swan_cache *c, const f
     if (row >= row_cap(d))
         return fail(SWAN_ERR_CAPACITY, "max_pos = %d writes sparse row %lld, capacity is %lld", max_pos,
                     (long long)row, (long long)row_cap(d));
-    swan::ProjectArgs p{d->B, d->N_h, d->H_kv, q, k, pos, P_qk, rope_base, q_hat, k_hat};
+    swan::ProjectArgs p{d->B, d->N_h, d->H_kv, q, k, pos, P_qk, rope_base, q_hat, k_hat, layer_seqs(d)};
     swan::AppendArgs a;
     a.B = d->B;
     a.H = d->H_kv;
@@ -395,7 +399,7 @@ swan_status swan_project_append_paged(const swan_dims *d, const swan_cache *c, c
         if ((st = swan_paged_update(d, c, block_table, entries, n_entries, pairs.data(), n_copies, stream))) return st;
         return swan_project_append(d, c, q, k, v_hat, pos, max_pos, P_qk, rope_base, q_hat, k_hat, stream);
     }
-    swan::ProjectArgs p{d->B, d->N_h, d->H_kv, q, k, pos, P_qk, rope_base, q_hat, k_hat};
+    swan::ProjectArgs p{d->B, d->N_h, d->H_kv, q, k, pos, P_qk, rope_base, q_hat, k_hat, layer_seqs(d)};
     swan::AppendArgs a;
     a.B = d->B;
     a.H = d->H_kv;
@@ -567,6 +571,7 @@ swan_status swan_prefill_convert(const swan_dims *d, const swan_cache *c, const 
     a.k_raw = k_raw;
     a.v_hat = v_hat;
     a.P = P_qk;
+    a.Bl = layer_seqs(d);
     a.base = rope_base;
     return hip_status(swan::launch_prefill(a, (hipStream_t)stream), "swan_prefill_convert launch");
 }

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a)
         double acc[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[q] = 0.0;
-        const float *P = a.P + (int64_t)h * kD * kD + j;
+        const float *P = a.P + ((int64_t)(b / a.Bl) * a.H + h) * kD * kD + j;
         for (int c = 0; c < kD; ++c) {
             const double pc = P[c * kD];
             const double *xr = &xs[c][half * 16];

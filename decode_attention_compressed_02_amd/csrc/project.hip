@@ -79,7 +79,7 @@ __device__ __forceinline__ void project_unit(const ProjectArgs &a, const AppendA
     const int c0 = quarter * kProjRows;
     float pr[kProjRows];
     {
-        const float *P = a.P + (int64_t)h * kD * kD + (int64_t)c0 * kD + j;
+        const float *P = a.P + ((int64_t)(b / a.Bl) * a.H + h) * kD * kD + (int64_t)c0 * kD + j;
 #pragma unroll
         for (int u = 0; u < kProjRows; ++u) pr[u] = P[u * kD];
     }

@@ -190,10 +190,11 @@ struct ProjectArgs {
     int B, N_h, H;
     const float *q, *k;
     const int32_t *pos;
-    const float *P;
+    const float *P; // [layers][H][128][128]; sequence b uses layer b / Bl
     float base;
     float *q_hat;
     uint16_t *k_hat;
+    int Bl; // sequences per layer (B when the batch is one layer)
 };
 hipError_t launch_project(const ProjectArgs &a, hipStream_t s);
 
@@ -424,8 +425,9 @@ struct PrefillArgs {
     uint8_t *kval, *vval; // value planes, geom.vbytes bytes per entry
     uint16_t *kbuf, *vbuf;
     const int32_t *len;
-    const float *k_raw, *v_hat, *P;
+    const float *k_raw, *v_hat, *P; // P: [layers][H][128][128]; sequence b uses layer b / Bl
     float base;
+    int Bl; // sequences per layer
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 

@@ -31,7 +31,7 @@ class SwanError(RuntimeError):
 
 class swan_dims(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("B", "N_h", "H_kv", "d_h", "R", "k", "n_cap", "block_size", "max_blocks",
-                                         "num_blocks", "split_tokens", "value_format", "k_v")]
+                                         "num_blocks", "split_tokens", "value_format", "k_v", "layers")]
 
     def __repr__(self):
         return "swan_dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -109,9 +109,9 @@ SWAN_VALUES_FP16, SWAN_VALUES_FP8_E4M3 = 0, 1
 
 
 def make_dims(B, N_h, H_kv, R, k, n_cap=0, d_h=128, block_size=0, max_blocks=0, num_blocks=0, split_tokens=0,
-              value_format=SWAN_VALUES_FP16, k_v=0):
+              value_format=SWAN_VALUES_FP16, k_v=0, layers=0):
     return swan_dims(B, N_h, H_kv, d_h, R, k, n_cap, block_size, max_blocks, num_blocks, split_tokens, value_format,
-                     k_v)
+                     k_v, layers)
 
 
 def swan_row_stride(k: int) -> int:

@@ -64,6 +64,7 @@ class Workload:
     pool_slack: int = 0  # extra free blocks in the paged pool
     value_format: int = 0  # sparse values: 0 fp16, 1 fp8 E4M3 (storage only; the inputs are the same)
     k_v: int = 0  # value coordinates kept, 0 = k (keys and values keeping different shares)
+    layers: int = 1  # layers stacked along the batch (each B sequences; see layer())
 
     @property
     def g(self) -> int:
@@ -219,6 +220,32 @@ def step_inputs(w: Workload, step: int):
         _shape_values(w, vb)
         v[b] = vb[:, 0, :]
     return q, k, v, pos
+
+
+# ---------------------------------------------------------------------------
+# Several layers in one batch: the library stacks the sequences of all layers
+# layer-major along its batch.  Layer l of a workload has the same shapes and
+# context lengths and its own inputs, drawn from seed + _LAYER_SEED_STRIDE l.
+# ---------------------------------------------------------------------------
+
+_LAYER_SEED_STRIDE = 7919
+
+
+def layer(w: Workload, l: int) -> Workload:
+    """Layer ``l`` (0-based) of a multi-layer workload, as a one-layer workload."""
+    return w.scaled(seed=w.seed + _LAYER_SEED_STRIDE * l, layers=1)
+
+
+def projection_qk_stacked(w: Workload) -> np.ndarray:
+    """P_QK of every layer, float32 [layers][H_kv][d_h][d_h] (a layer is
+    [H_kv][d_h][d_h], as projection_qk gives it)."""
+    return np.stack([projection_qk(layer(w, l)) for l in range(max(1, w.layers))])
+
+
+def step_inputs_stacked(w: Workload, step: int):
+    """step_inputs of every layer, concatenated layer-major along the batch."""
+    parts = [step_inputs(layer(w, l), step) for l in range(max(1, w.layers))]
+    return tuple(np.concatenate([p[i] for p in parts]) for i in range(4))
 
 
 def pool_order(w: Workload, num_blocks: int) -> np.ndarray:

@@ -40,6 +40,11 @@
  *   buffer, "Reuse, Evict, or Limit Earlier Context" section 3.2).  A
  *   sequence with pos[b] < 0 is inactive: nothing is appended and its output
  *   rows are zero.
+ * - Several layers can share one batch (dims->layers): their sequences are
+ *   stacked layer-major along B in the same cache planes (contiguous) or the
+ *   same pool and block table (paged), so one launch of each kernel serves
+ *   every layer, e.g. the layers of micro-batches pipelined through a model.
+ *   Only the projection and the prefill tell layers apart (their P_QK).
  * - max_pos (host) must be >= every pos[b]; it sizes grids and is checked
  *   against the sparse capacity.  A device pos[b] above max_pos gives
  *   undefined results for that sequence but no out-of-bounds access.
@@ -106,6 +111,11 @@ typedef struct swan_dims {
                              (SWAN Appendix A.5, Table 2: keys and values may keep
                              different shares of d_h); swan_row_stride(k_v) must equal
                              swan_row_stride(k), twice it or half of it */
+    int32_t layers;       /* layers whose sequences share the batch, 0 or 1 = one:
+                             B counts the sequences of all layers, layer-major, so
+                             sequence b belongs to layer b / (B / layers) and is
+                             projected with that layer's P_QK; every decode call
+                             covers all layers in one split and one reduce launch */
 } swan_dims;
 
 /* Storage of the values of sparse rows (the dense buffer is always fp16).
@@ -151,9 +161,9 @@ swan_status swan_cache_bytes(const swan_dims *dims, size_t out[5]);
  *   q      float32 [B][N_h][128]   raw queries (before RoPE)
  *   k      float32 [B][H_kv][128]  raw new keys (before RoPE)
  *   pos    int32   [B]             rotation position of each sequence
- *   P_qk   float32 [H_kv][128][128] row-vector convention: x_hat = x P,
- *                                  element [h][c][j]; query head j uses
- *                                  P_qk[j / g]
+ *   P_qk   float32 [layers][H_kv][128][128] row-vector convention: x_hat =
+ *                                  x P, element [l][h][c][j]; query head j
+ *                                  of a sequence of layer l uses P_qk[l][j / g]
  *   rope_base                      RoPE base (10000 for Llama-3)
  *   q_hat  float32 [B][N_h][128]   out: rotated queries
  *   k_hat  fp16    [B][H_kv][128]  out: rotated keys, rounded to nearest even
@@ -268,7 +278,8 @@ swan_status swan_decode_reduce(const swan_dims *dims, const int32_t *pos, int32_
 
 /*
  * Prefill -> hybrid cache.  Sequence b has len[b] prefilled tokens at
- * positions 0..len[b]-1 (max_len host bound, 0 <= len[b] <= max_len):
+ * positions 0..len[b]-1 (max_len host bound, 0 <= len[b] <= max_len); its
+ * keys are projected with the P_QK of its layer ([layers][H_kv][128][128]):
  *   k_raw  float32 [B][H_kv][T_stride][128]  raw keys (before RoPE)
  *   v_hat  float32 [B][H_kv][T_stride][128]  values in the rotated basis
  * Each key gets RoPE at its own position and P_qk; keys and values are

@@ -230,6 +230,8 @@ cases = [
     ("k_v stride 4x k's", dec(dims(k=8, k_v=32)), U),
     ("k_v stride 8x k's", app(dims(k=128, k_v=16)), U),
     ("value format -1", dec(dims(value_format=-1)), U),
+    ("layers not dividing B", proj(dims(layers=3)), E),
+    ("layers < 0", dec(dims(layers=-1)), E),
     ("null q", proj(dims(), q=N), E),
     ("null k_hat out", proj(dims(), kh=N), E),
     ("rope base 1", proj(dims(), base=1.0), E),

@@ -1,0 +1,97 @@
+"""GPU parity of a batch that stacks several layers (swan_dims.layers): every
+layer's sequences live in the same cache planes (contiguous) or the same pool
+and block table (paged), are converted from their own seeded history with
+their own P_QK, and are stepped by one projection/append launch and one
+decode (one split and one reduce launch) for all layers.  Each layer is
+checked against the float64 oracle run on that layer alone: stored rows and
+k_hat bit-exact, q_hat and outputs within their bars."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_compressed_02_amd import swan as S
+from decode_attention_compressed_02_amd import workloads as wl
+from decode_attention_compressed_02_amd.state import build_decoder, step_inputs
+
+from gpu_helpers import assert_values_bits, rel_l2_max
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    S.lib()
+
+
+def _oracle_layer(w):
+    oc = oracle.OracleCache.for_workload(w)
+    T = [w.history_len(b) for b in range(w.B)]
+    K = np.zeros((w.B, w.H_kv, max(T), 128), np.float32)
+    V = np.zeros_like(K)
+    for b in range(w.B):
+        K[b, :, :T[b]], V[b, :, :T[b]] = wl.history(w, b)
+    oc.prefill(K, V, np.array(T, np.int64), wl.projection_qk(w).astype(np.float64), w.rope_base)
+    return oc
+
+
+def _rows(dec, b, n):
+    """Stacked-batch sequence b's sparse rows [0, n): 4 arrays [H][n][stride]."""
+    d, planes = dec.dims, dec.cache.sparse_views()
+    if d.block_size == 0:
+        return [p[b, :, :n].cpu().numpy() for p in planes]
+    blk = torch.from_numpy(dec.pool.table[b, :-(-n // d.block_size)].astype(np.int64)).cuda()
+    return [p.index_select(0, blk).permute(1, 0, 2, 3).reshape(d.H_kv, -1, p.shape[-1])[:, :n].cpu().numpy()
+            for p in planes]
+
+
+def _check_rows(dec, ocs, w, Bl, n_of):
+    kb, vb = dec.cache.buffer_views()
+    for l, oc in enumerate(ocs):
+        for i in range(Bl):
+            b, n = l * Bl + i, n_of(i)
+            ki, kv, vi, vv = _rows(dec, b, n)
+            np.testing.assert_array_equal(ki[:, :, :w.k], oc.kidx[i, :, :n])
+            np.testing.assert_array_equal(vi[:, :, :w.k], oc.vidx[i, :, :n])
+            assert_values_bits(kv[:, :, :w.k], oc.kval[i, :, :n], w.value_format)
+            assert_values_bits(vv[:, :, :w.k], oc.vval[i, :, :n], w.value_format)
+            np.testing.assert_array_equal(kb[b].cpu().numpy().astype(np.float64), oc.ringk[i])
+            np.testing.assert_array_equal(vb[b].cpu().numpy().astype(np.float64), oc.ringv[i])
+
+
+@pytest.mark.parametrize("paged,L", [(False, 3), (True, 3), (False, 1)])
+def test_layers_stacked_along_the_batch(paged, L):
+    base = wl.Workload("stacked layers", 3, 8, 2, 32, 32, (420, 333, 700), steps=3, seed=91,
+                       block_size=16 if paged else 0, shared_prefix=160 if paged else 0, pool_slack=4)
+    w = base.scaled(layers=L)
+    dec = build_decoder(w)
+    assert dec.dims.B == 3 * L and dec.dims.layers == (L if L > 1 else 0)
+    layers = [wl.layer(w, l) for l in range(L)]
+    # the layers differ: their projections are not the same matrices
+    if L > 1:
+        assert not np.array_equal(wl.projection_qk(layers[0]), wl.projection_qk(layers[1]))
+    ocs = [_oracle_layer(x) for x in layers]
+    _check_rows(dec, ocs, w, w.B, lambda i: max(0, w.history_len(i) - w.R))
+    P64 = [wl.projection_qk(x).astype(np.float64) for x in layers]
+    for s in range(w.steps):
+        q, kr, vn, pos = step_inputs(w, s)
+        cu = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (q, kr, vn, pos)]
+        if paged:
+            out = dec.step_paged(*cu, pos)
+        else:
+            out = dec.step(*cu, int(pos.max()))
+        out = out.cpu().numpy()
+        qh_gpu, kh_gpu = dec.q_hat.cpu().numpy(), dec.k_hat.cpu().numpy().astype(np.float64)
+        for l, oc in enumerate(ocs):
+            sl = slice(l * w.B, (l + 1) * w.B)
+            qh, kh, want = oc.step(q[sl], kr[sl], vn[sl], pos[sl].astype(np.int64), P64[l], w.rope_base)
+            assert rel_l2_max(qh_gpu[sl], qh) < 1e-6
+            np.testing.assert_array_equal(kh_gpu[sl], kh)
+            err = rel_l2_max(out[sl], want)
+            print(f"[layers paged={paged}] step {s} layer {l}: rel_l2={err:.2e}", flush=True)
+            assert err < TOL
+    _check_rows(dec, ocs, w, w.B, lambda i: w.n_after(i, w.steps - 1))
