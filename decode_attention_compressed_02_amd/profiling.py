@@ -76,6 +76,31 @@ def dispatch_series(trace_csv: str, kernel: str, first: int, per_bin: int):
     return out, len(rows)
 
 
+def clock_series(trace_csv: str, counter_csv: str, kernel: str, per_bin: int, xcds: int = 8):
+    """Shader clock of each dispatch of a kernel, from a run that collected
+    GRBM_GUI_ACTIVE (GPU-busy cycles, summed over the XCDs) together with the
+    kernel trace: cycles per XCD / duration.  Returns (first index, last
+    index, mean duration us, mean clock GHz) per bin of `per_bin` dispatches
+    in start order."""
+    cyc = {}
+    for r in csv.DictReader(open(counter_csv)):
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+            cyc[int(r["Dispatch_Id"])] = float(r["Counter_Value"])
+    rows = [r for r in csv.DictReader(open(trace_csv)) if kernel in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    pts = []
+    for r in rows:
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        c = cyc.get(int(r["Dispatch_Id"]))
+        if c:
+            pts.append((dur, c / xcds / dur / 1e3))
+    out = []
+    for i in range(0, len(pts), per_bin):
+        c = pts[i:i + per_bin]
+        out.append((i, i + len(c) - 1, statistics.mean(x[0] for x in c), statistics.mean(x[1] for x in c)))
+    return out
+
+
 def counter_means(counter_csv: str, kernel: str, last: int) -> dict:
     """{counter: mean value per dispatch} over the last `last` dispatches of a
     kernel in a rocprofv3 counter_collection.csv."""
@@ -103,6 +128,30 @@ def _pick(vals, needle):
     if not hits:
         raise SystemExit(f"no kernel matching {needle!r} in counter file")
     return [x for v in hits for x in v]
+
+
+EA_COUNTERS = ("TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_RDREQ_128B_sum", "TCC_EA0_RDREQ_64B_sum",
+               "TCC_EA0_RDREQ_32B_sum")
+
+
+def ea_reads(ea_csv: str, kernel: str, copy_mib: float) -> dict:
+    """A second path to the read traffic: DRAM read requests counted in
+    32-byte units (a 64-byte request counts 2, a 128-byte one 4), and the
+    requests by size, per dispatch of the kernel and of the calibration
+    copies.  Bytes = 32 x the DRAM count, with no scale factor; the copy shows
+    whether that reading is exact."""
+    vals = {c: _counter_values(ea_csv, c) for c in EA_COUNTERS}
+    copy_bytes = copy_mib * 2 ** 20
+    dram_k = statistics.mean(_pick(vals[EA_COUNTERS[0]], kernel)) * 32.0
+    copies = [v * 32.0 for v in _pick(vals[EA_COUNTERS[0]], COPY_KERNEL_HINT)
+              if copy_bytes / 4 <= v * 32.0 <= copy_bytes * 4]
+    if not copies:
+        raise SystemExit("no calibration copy found in the EA counter file")
+    by_size = {c: statistics.mean(_pick(vals[c], kernel)) for c in EA_COUNTERS[1:]}
+    sized = 128 * by_size[EA_COUNTERS[1]] + 64 * by_size[EA_COUNTERS[2]] + 32 * by_size[EA_COUNTERS[3]]
+    return {"ea_read_bytes_per_launch": dram_k, "ea_copy_read_bytes": statistics.mean(copies),
+            "ea_copy_scale": copy_bytes / statistics.mean(copies), "ea_requests_by_size": by_size,
+            "ea_sized_read_bytes_per_launch": sized}
 
 
 def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_mib: float, workload: str) -> dict:
@@ -145,6 +194,11 @@ def main(argv=None):
     se.add_argument("--kernel", default="k_split")
     se.add_argument("--first", type=int, default=300, help="dispatches from the start of the run")
     se.add_argument("--bin", type=int, default=10, help="dispatches per row")
+    ck = sub.add_parser("clock")
+    ck.add_argument("trace", help="kernel_trace.csv of a run that also collected GRBM_GUI_ACTIVE")
+    ck.add_argument("counters", help="counter_collection.csv of the same run")
+    ck.add_argument("--kernel", default="k_split")
+    ck.add_argument("--bin", type=int, default=20)
     c = sub.add_parser("counters")
     c.add_argument("csv", help="counter_collection.csv")
     c.add_argument("--kernel", default="k_split")
@@ -155,6 +209,7 @@ def main(argv=None):
     t.add_argument("--kernel", default="k_split")
     t.add_argument("--copy-mib", type=float, required=True)
     t.add_argument("--workload", required=True)
+    t.add_argument("--ea", help="counter_collection.csv of the TCC_EA read-request counters (cross-check)")
     t.add_argument("--out")
     args = ap.parse_args(argv)
     if args.cmd == "stats":
@@ -166,6 +221,11 @@ def main(argv=None):
         print("|---|---|---|---|")
         for i0, i1, m, lo, hi in bins:
             print(f"| {i0}-{i1} | {m:.1f} | {lo:.1f} | {hi:.1f} |")
+    elif args.cmd == "clock":
+        print("| dispatches | mean us | clock GHz |")
+        print("|---|---|---|")
+        for i0, i1, d, g in clock_series(args.trace, args.counters, args.kernel, args.bin):
+            print(f"| {i0}-{i1} | {d:.1f} | {g:.2f} |")
     elif args.cmd == "counters":
         for n, v in counter_means(args.csv, args.kernel, args.n).items():
             print(f"{n}: {v:.6g}")
@@ -175,6 +235,8 @@ def main(argv=None):
         print(f"{args.kernel}: {where} of {total} dispatches: mean {mean:.2f} us, min {lo:.2f}, max {hi:.2f}")
     else:
         res = traffic(args.fetch, args.write, args.kernel, args.copy_mib, args.workload)
+        if args.ea:
+            res["cross_check"] = ea_reads(args.ea, args.kernel, args.copy_mib)
         txt = json.dumps(res, indent=1)
         if args.out:
             with open(args.out, "w") as f:
