@@ -50,24 +50,30 @@ def _rows(dec, b, n):
 
 
 def _check_rows(dec, ocs, w, Bl, n_of):
-    kb, vb = dec.cache.buffer_views()
+    kb, vb = dec.cache.buffer_views() if w.R > 0 else (None, None)
     for l, oc in enumerate(ocs):
         for i in range(Bl):
             b, n = l * Bl + i, n_of(i)
             ki, kv, vi, vv = _rows(dec, b, n)
+            k_v = w.k_v or w.k
             np.testing.assert_array_equal(ki[:, :, :w.k], oc.kidx[i, :, :n])
-            np.testing.assert_array_equal(vi[:, :, :w.k], oc.vidx[i, :, :n])
+            np.testing.assert_array_equal(vi[:, :, :k_v], oc.vidx[i, :, :n])
             assert_values_bits(kv[:, :, :w.k], oc.kval[i, :, :n], w.value_format)
-            assert_values_bits(vv[:, :, :w.k], oc.vval[i, :, :n], w.value_format)
-            np.testing.assert_array_equal(kb[b].cpu().numpy().astype(np.float64), oc.ringk[i])
-            np.testing.assert_array_equal(vb[b].cpu().numpy().astype(np.float64), oc.ringv[i])
+            assert_values_bits(vv[:, :, :k_v], oc.vval[i, :, :n], w.value_format)
+            if w.R > 0:
+                np.testing.assert_array_equal(kb[b].cpu().numpy().astype(np.float64), oc.ringk[i])
+                np.testing.assert_array_equal(vb[b].cpu().numpy().astype(np.float64), oc.ringv[i])
 
 
-@pytest.mark.parametrize("paged,L", [(False, 3), (True, 3), (False, 1)])
-def test_layers_stacked_along_the_batch(paged, L):
+@pytest.mark.parametrize("paged,L,extra", [(False, 3, {}), (True, 3, {}), (False, 1, {}),
+                                           (False, 2, {"value_format": 1}),
+                                           (True, 2, {"value_format": 1, "k": 48, "k_v": 20}),
+                                           (True, 4, {"R": 0})])
+def test_layers_stacked_along_the_batch(paged, L, extra):
     base = wl.Workload("stacked layers", 3, 8, 2, 32, 32, (420, 333, 700), steps=3, seed=91,
                        block_size=16 if paged else 0, shared_prefix=160 if paged else 0, pool_slack=4)
-    w = base.scaled(layers=L)
+    w = base.scaled(layers=L, **extra)
+    print(f"\n[layers] paged={paged} L={L} {extra}", flush=True)
     dec = build_decoder(w)
     assert dec.dims.B == 3 * L and dec.dims.layers == (L if L > 1 else 0)
     layers = [wl.layer(w, l) for l in range(L)]
