@@ -353,14 +353,17 @@ def main():
         stream_read = {"GBps": best[0], "waves": best[1], "ms": best[2], "bytes": nb,
                        "frac_of_peak": best[0] / HBM_PEAK_GBS}
 
-    traffic = None
+    traffic = traffic_ea = None
     if os.path.exists(TRAFFIC_FILE):
         from decode_attention_compressed_02_amd.profiling import kernel_source_hash
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if (tr.get("kernel_source_sha") == kernel_source_hash() and tr.get("workload") == w.name
-                and tr.get("value_format", 0) == w.value_format and not w.k_v):
+                and tr.get("value_format", 0) == w.value_format and not w.k_v and L == 1):
             traffic = tr.get("hbm_bytes_per_launch")
+            cc = tr.get("cross_check")
+            if cc:  # DRAM read requests in 32-byte units, plus the same writes
+                traffic_ea = cc["ea_read_bytes_per_launch"] + tr["write_bytes_per_launch"]
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * 2 ** 20
@@ -374,6 +377,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "kernel": "k_split", "algorithmic_bytes_per_launch": last_bytes}
+    if traffic_ea is not None:
+        roofline["traffic_dram_request_count"] = traffic_ea
     if stream_read:
         roofline["measured_ceiling_GBps"] = stream_read["GBps"]
         roofline["frac_of_measured_ceiling"] = achieved / stream_read["GBps"]
