@@ -12,6 +12,9 @@ A timed step is the whole hot path: swan_project_append (projection and
 append/evict in one launch; on a paged pool swan_project_append_paged, which
 also carries the step's block-table writes and copy-on-write copies) ->
 swan_decode_split -> swan_decode_reduce, all inputs already resident in HBM.
+After the decode measurements the prefill conversion of the same history
+(swan_prefill_convert, the step before decoding) is timed too, against the
+fp64 matrix-core roofline of its double-precision key projection.
 Prints one JSON line (rank 0).
 """
 from __future__ import annotations
@@ -28,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_F64_PEAK_TFLOPS = 78.6  # MI355X dense fp64 matrix, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_traffic.json")
 
 
@@ -120,6 +124,9 @@ def main():
                     help="split launches timed one at a time after a 1 GiB cache-evicting fill (median); 0 = skip")
     ap.add_argument("--no-stream-ceiling", action="store_true",
                     help="skip the streaming-read measurement of the GPU's attainable HBM read rate")
+    ap.add_argument("--prefill-reps", type=int, default=5,
+                    help="swan_prefill_convert launches over the workload's history timed back to back "
+                         "after the decode measurements (one layer only; 0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run plain device copies of this size (for calibrating HBM byte counters)")
     args = ap.parse_args()
@@ -152,7 +159,7 @@ def main():
     if args.layers > 1:
         w = w.scaled(layers=args.layers)
     L = max(1, w.layers)
-    dec = build_decoder(w, args.split_tokens)
+    dec = build_decoder(w, args.split_tokens, keep_history=args.prefill_reps > 0)
     log(f"device {torch.cuda.get_device_name(0)}; dims {dec.dims}")
 
     # step inputs for every step, resident in HBM before timing
@@ -365,6 +372,44 @@ def main():
             if cc:  # DRAM read requests in 32-byte units, plus the same writes
                 traffic_ea = cc["ea_read_bytes_per_launch"] + tr["write_bytes_per_launch"]
 
+    # the prefill conversion of the workload's own history (the step before
+    # decoding; it rebuilds the cache the decode steps started from): its
+    # double-precision key projection runs on the fp64 matrix cores, so its
+    # roofline is their rate, published and measured with the same grid of
+    # independent products (swan_measure_mfma_f64)
+    prefill = None
+    if args.prefill_reps > 0 and getattr(dec, "history", None) is not None:
+        lens, Tm, K, V = dec.history
+        T = [int(x) for x in lens.cpu()]
+        th = sum(T) * w.H_kv
+        pf_flops = 2.0 * 128 * 128 * th
+        kv_v = w.k_v or w.k
+        n_rows = sum(max(0, t - w.R) for t in T) * w.H_kv
+        pf_bytes = (th * 2 * 128 * 4 + n_rows * (w.k + kv_v) * (1 + vbytes)
+                    + sum(min(t, w.R) for t in T) * w.H_kv * 2 * 128 * 2)
+        launch = lambda: dec.prefill(lens, Tm, K, V)
+        back_to_back(launch, 1)
+        pf_ms = back_to_back(launch, args.prefill_reps)
+        mf_waves, mf_iters = 16384, 1024
+        sink = torch.empty(mf_waves * 64, dtype=torch.float64, device="cuda")
+        mf = lambda: S.swan_measure_mfma_f64(1.0, mf_waves, mf_iters, sink)
+        back_to_back(mf, 2)
+        mf_ms = back_to_back(mf, 5)
+        mf_tflops = mf_waves * mf_iters * 16384 / (mf_ms * 1e-3) / 1e12
+        del sink
+        pf_tflops = pf_flops / (pf_ms * 1e-3) / 1e12
+        prefill = {"kernel": "k_prefill", "ms": pf_ms, "reps": args.prefill_reps, "history_tokens": sum(T),
+                   "token_heads": th, "tokens_per_s": sum(T) / (pf_ms * 1e-3),
+                   "bytes_per_launch": pf_bytes, "GBps": pf_bytes / (pf_ms * 1e-3) / 1e9,
+                   "roofline": {"bound": "mfma", "achieved": pf_tflops, "peak": MFMA_F64_PEAK_TFLOPS,
+                                "unit": "TFLOP/s", "frac": pf_tflops / MFMA_F64_PEAK_TFLOPS,
+                                "algorithmic_flops_per_launch": pf_flops,
+                                "measured_ceiling_TFLOPs": mf_tflops,
+                                "frac_of_measured_ceiling": pf_tflops / mf_tflops}}
+        log(f"prefill conversion: {pf_ms:.3f} ms ({pf_tflops:.1f} TFLOP/s fp64 projection, "
+            f"{100 * pf_tflops / MFMA_F64_PEAK_TFLOPS:.1f}% of peak; fp64 matrix cores sustain {mf_tflops:.1f})")
+        del dec.history, K, V
+
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * 2 ** 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -423,6 +468,7 @@ def main():
         "stream_read": stream_read,
         "decode_gflops_per_step": float(np.mean(flops)) / 1e9,
         "roofline": roofline,
+        "prefill": prefill,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

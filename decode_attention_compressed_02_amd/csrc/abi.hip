@@ -235,6 +235,10 @@ swan_status scratch_for(hipStream_t stream, void **out)
 
 } // namespace
 
+namespace swan {
+hipError_t launch_mfma_f64(double x, int waves, int iters, double *sink, hipStream_t s); // measure.hip
+}
+
 extern "C" {
 
 const char *swan_status_str(swan_status s)
@@ -674,6 +678,16 @@ swan_status swan_measure_stream_read(const void *buf, size_t bytes, int32_t wave
         return fail(SWAN_ERR_INVALID_ARG, "waves = %d outside 1..%d", waves, swan::kMaxWaves);
     return hip_status(swan::launch_stream_read(buf, (int64_t)bytes, waves, sink, (hipStream_t)stream),
                       "swan_measure_stream_read launch");
+}
+
+swan_status swan_measure_mfma_f64(double x, int32_t waves, int32_t iters, double *sink, void *stream)
+{
+    if (!sink) return fail(SWAN_ERR_INVALID_ARG, "NULL sink");
+    if (waves < 1 || waves > swan::kMaxWaves)
+        return fail(SWAN_ERR_INVALID_ARG, "waves = %d outside 1..%d", waves, swan::kMaxWaves);
+    if (iters < 4 || iters > (1 << 20) || iters % 4)
+        return fail(SWAN_ERR_INVALID_ARG, "iters = %d: must be a multiple of 4 in 4..1048576", iters);
+    return hip_status(swan::launch_mfma_f64(x, waves, iters, sink, (hipStream_t)stream), "swan_measure_mfma_f64 launch");
 }
 
 } // extern "C"

@@ -1,6 +1,7 @@
-// measure.hip -- the streaming-read yardstick of swan_measure.h: how fast
-// this GPU reads a buffer once from HBM, the ceiling for a decode step that
-// must read its whole cache every step.
+// measure.hip -- the yardsticks of swan_measure.h: how fast this GPU reads a
+// buffer once from HBM (the ceiling for a decode step that must read its
+// whole cache every step), and how fast its matrix cores run fp64 products
+// (the ceiling for the prefill conversion's double-precision projection).
 //
 // One-wave workgroups each read one contiguous share of the buffer with
 // 16-byte non-temporal loads (lane l takes every 64th 16-byte unit from
@@ -37,6 +38,43 @@ __global__ __launch_bounds__(64) void k_stream_read(const msr_u32x4 *p, int64_t 
 hipError_t launch_stream_read(const void *buf, int64_t bytes, int waves, uint32_t *sink, hipStream_t s)
 {
     hipLaunchKernelGGL(k_stream_read, dim3(waves), dim3(kWave), 0, s, (const msr_u32x4 *)buf, bytes / 16, sink);
+    return hipGetLastError();
+}
+
+// fp64 matrix-core rate: every wave runs `iters` rounds of eight independent
+// 16x16x4 products (A and B all x), so each accumulator element gains 4 x^2
+// a round; the lane's four elements of all eight accumulators are summed
+// into sink[wave * 64 + lane] (128 x^2 iters when exact).  Workgroups of
+// four waves (one per SIMD of a CU); waves past `waves` exit at once.
+typedef double mf_f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kMfWaves = 4;
+
+__global__ __launch_bounds__(kMfWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void k_mfma_f64(double x, int waves, int iters, double *sink)
+{
+    const int64_t wave = (int64_t)blockIdx.x * kMfWaves + threadIdx.x / kWave;
+    if (wave >= waves) return;
+    mf_f64x4 acc[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[n] = (mf_f64x4){0.0, 0.0, 0.0, 0.0};
+    // rounds in groups of four (iters is a multiple of 4): a rolled loop of
+    // one round makes the compiler move the accumulators between register
+    // files every round
+    for (int i = 0; i < iters; i += 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int n = 0; n < 8; ++n) acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(x, x, acc[n], 0, 0, 0);
+    }
+    double s = 0.0;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) s += (acc[n][0] + acc[n][1]) + (acc[n][2] + acc[n][3]);
+    sink[wave * kWave + threadIdx.x % kWave] = s;
+}
+
+hipError_t launch_mfma_f64(double x, int waves, int iters, double *sink, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_mfma_f64, dim3((waves + kMfWaves - 1) / kMfWaves), dim3(kMfWaves * kWave), 0, s, x, waves,
+                       iters, sink);
     return hipGetLastError();
 }
 

@@ -23,11 +23,14 @@ def _log(*a):
     print("[state]", *a, file=sys.stderr, flush=True)
 
 
-def build_decoder(w: wl.Workload, split_tokens: int = 0, extra_steps: int = 0):
+def build_decoder(w: wl.Workload, split_tokens: int = 0, extra_steps: int = 0, keep_history: bool = False):
     """A SwanDecoder (PagedSwanDecoder for block_size > 0) holding workload
     w's history, with room for w.steps + extra_steps more tokens.  With
     w.layers = L > 1 the batch holds L x w.B sequences, layer l's at
-    l w.B .. (l + 1) w.B - 1 (workloads.layer(w, l) drew them)."""
+    l w.B .. (l + 1) w.B - 1 (workloads.layer(w, l) drew them).  With
+    keep_history (one layer only) the uploaded raw history stays on the GPU
+    as dec.history = (lengths, max length, raw keys, values), the arguments
+    of dec.prefill that built the cache."""
     L = max(1, w.layers)
     B, H, Bt = w.B, w.H_kv, w.B * max(1, w.layers)
     steps = w.steps + extra_steps
@@ -72,6 +75,8 @@ def build_decoder(w: wl.Workload, split_tokens: int = 0, extra_steps: int = 0):
         torch.cuda.synchronize()
     if L > 1:
         _log(f"generated, uploaded and converted {L} layers of {B}x{H}x{Tm}")
+    if keep_history and L == 1:
+        dec.history = (lens, Tm, K, V)
     del K, V
     torch.cuda.empty_cache()
     return dec

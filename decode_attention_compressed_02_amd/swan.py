@@ -20,7 +20,7 @@ EXPORTS = ("swan_status_str", "swan_last_error", "swan_row_stride", "swan_cache_
            "swan_append_evict", "swan_decode_workspace_bytes", "swan_decode_num_splits", "swan_decode_attn",
            "swan_decode_split", "swan_decode_reduce", "swan_prefill_convert", "swan_copy_blocks",
            "swan_project_append", "swan_paged_update", "swan_project_append_paged",
-           "swan_measure_stream_read", "swan_decode_attn_noalloc")
+           "swan_measure_stream_read", "swan_decode_attn_noalloc", "swan_measure_mfma_f64")
 
 
 class SwanError(RuntimeError):
@@ -73,6 +73,7 @@ def lib():
             "swan_project_append_paged": ([D, Cc, V, V, V, V, I32, V, F, V, V, V, V, I32, V, I32, V], C.c_int),
             "swan_measure_stream_read": ([V, SZ, I32, V, V], C.c_int),
             "swan_decode_attn_noalloc": ([D, Cc, V, I32, V, V, V], C.c_int),
+            "swan_measure_mfma_f64": ([C.c_double, I32, I32, V, V], C.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -254,3 +255,14 @@ def swan_measure_stream_read(buf, waves, sink, stream=None):
         raise ValueError("sink must hold waves * 64 uint32 words")
     _check(lib().swan_measure_stream_read(_ptr(buf, None, "buf"), nbytes, int(waves), _ptr(sink, None, "sink"),
                                           _stream(stream)))
+
+
+def swan_measure_mfma_f64(x, waves, iters, sink, stream=None):
+    """`waves` waves (workgroups of four) of `iters` rounds of eight fp64 16x16x4
+    matrix products each (16384 flops a wave a round); sink is a float64
+    device tensor of at least waves * 64 elements."""
+    import torch
+    if sink.numel() < waves * 64:
+        raise ValueError("sink must hold waves * 64 doubles")
+    _check(lib().swan_measure_mfma_f64(float(x), int(waves), int(iters), _ptr(sink, torch.float64, "sink"),
+                                       _stream(stream)))

@@ -8,6 +8,11 @@
  * is bound by memory bandwidth.  The ceiling a decode kernel can reach is
  * then what a plain streaming read of the same number of bytes achieves on
  * the same GPU, below the published peak.
+ *
+ * The prefill conversion projects every key of a history through P_QK in
+ * double precision, a dense contraction that runs on the fp64 matrix
+ * cores; its ceiling is the rate those cores sustain on independent
+ * products.
  */
 #ifndef SWAN_MEASURE_H
 #define SWAN_MEASURE_H
@@ -33,6 +38,19 @@ extern "C" {
  * 1..1048576 (nothing is launched); SWAN_ERR_HIP for a failed launch.
  */
 swan_status swan_measure_stream_read(const void *buf, size_t bytes, int32_t waves, uint32_t *sink, void *stream);
+
+/*
+ * fp64 matrix-core rate: `waves` waves (1..1048576, in workgroups of four)
+ * each run `iters` (a multiple of 4 in 4..1048576) rounds of eight
+ * independent v_mfma_f64_16x16x4f64 products (2 x 16 x 16 x 4 flops each,
+ * so 16384 flops a wave a round) with every A and B element equal to x, and
+ * write the sum of the lane's accumulator elements to sink[wave * 64 +
+ * lane] (device, waves * 64 doubles): 128 x^2 iters when no rounding occurs
+ * (x = 1).  Asynchronous on `stream`; the caller times it.  Errors:
+ * SWAN_ERR_INVALID_ARG for a NULL sink or waves / iters out of range
+ * (nothing is launched); SWAN_ERR_HIP for a failed launch.
+ */
+swan_status swan_measure_mfma_f64(double x, int32_t waves, int32_t iters, double *sink, void *stream);
 
 #ifdef __cplusplus
 }

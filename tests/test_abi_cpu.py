@@ -318,6 +318,16 @@ cases += [
     ("stream read 0 waves", sread(waves=0), E),
     ("stream read too many waves", sread(waves=(1 << 20) + 1), E),
 ]
+def mrate(waves=64, iters=16, sink=0x2000):
+    return L.swan_measure_mfma_f64(C.c_double(1.0), waves, iters, C.c_void_p(sink) if sink else None, st)
+cases += [
+    ("mfma rate null sink", mrate(sink=0), E),
+    ("mfma rate 0 waves", mrate(waves=0), E),
+    ("mfma rate too many waves", mrate(waves=(1 << 20) + 1), E),
+    ("mfma rate 0 iters", mrate(iters=0), E),
+    ("mfma rate iters not a multiple of 4", mrate(iters=6), E),
+    ("mfma rate too many iters", mrate(iters=(1 << 20) + 4), E),
+]
 def noalloc(d, c=cache, max_pos=50, **kw):
     a = dict(pos=F, qh=F, oh=F); a.update(kw)
     return L.swan_decode_attn_noalloc(C.byref(d), C.byref(c), a['pos'], max_pos, a['qh'], a['oh'], st)
