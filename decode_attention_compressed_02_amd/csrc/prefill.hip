@@ -1,12 +1,12 @@
 // prefill.hip -- convert a prefilled history into the hybrid cache (the step
-// before decoding starts: the SWAN page's hybrid cache keeps the newest R tokens dense
-// and every older one as its pruned sparse row).
+// before decoding starts: the SWAN page's hybrid cache keeps the newest R
+// tokens dense and every older one as its pruned sparse row).
 //
 // The key projection of a history is a dense contraction (tokens x 128
 // rotated coordinates times the 128 x 128 P_QK of the head), carried out in
 // double to match the decode-step projection, so it runs on the fp64 matrix
-// cores (v_mfma_f64_16x16x4f64).  One workgroup of four waves per (chunk of
-// 256 tokens, kv head, sequence):
+// cores (v_mfma_f64_16x16x4f64).  One workgroup of eight waves per (chunk of
+// 128 to 512 tokens, kv head, sequence; shorter chunks for small batches):
 //   0. P_QK of the head is staged in LDS as fp32 (64 KB, read once per
 //      chunk) in a layout where a lane's eight 16-column blocks are
 //      contiguous, and the 64 RoPE frequencies are computed once;
@@ -14,12 +14,24 @@
 //      (c, c + 64) of token l % 16 for the 16 values of c that its MFMA k
 //      column l / 16 covers, so the A operand never leaves registers;
 //   2. 32 k steps x 8 column blocks of MFMA give the tile's 16 x 128
-//      projected keys in double, each rounded once to fp16;
-//   3. the wave places its tokens, eight at a time through a 2 KB LDS
-//      stage: tokens older than len - R are pruned into their sparse rows
-//      (the same wave-level top-k as the append kernel, the threshold
-//      searches of four tokens' eight rows interleaved), the newest R go to
-//      buffer slots t mod R.  Values are rounded from fp32 to fp16 directly.
+//      projected keys in double;
+//   3. eight tokens at a time, their keys (rounded once to fp16, branch-free:
+//      fp16_round.h) and values (fp32 -> fp16, loaded one pass ahead) are
+//      staged in LDS as 16 rows; tokens older than len - R are pruned into
+//      their sparse rows, the newest R go to buffer slots t mod R.
+//
+// Pruning (SWAN page, pruning paragraph: a vector keeps its k coordinates of
+// largest magnitude) takes four lanes a row, lane 4 r + q holding
+// coordinates 32 q .. 32 q + 31 of row r as packed fp16, all in VALU
+// arithmetic: the k-th largest magnitude T is found bit by bit (the largest T
+// with at least k magnitudes >= T; a packed 16-bit subtract's sign bits mark
+// the magnitudes below a candidate and v_sad_u16 adds them up), then every
+// coordinate above T is kept together with the first k - #(above T) equal to
+// T in index order, the ranking of the append kernel's wave_prune_row.  Each
+// lane writes its kept entries, in index order, to the row's place in an LDS
+// output stage (the others to a scratch byte, so no lane branches), and
+// whole rows go to their slots with 32-bit stores.
+//
 // The result is identical to appending the tokens one at a time.  Keys are
 // rotated and projected in double, as in the decode-step projection, so that
 // their fp16 rounding (and with it the pruning) does not depend on float
@@ -30,34 +42,51 @@
 // holds D[4 r + l / 16][l % 16].  The contraction index k of k step s maps
 // to coordinate c(s, k) = 16 k + s for s < 16 and 64 + 16 k + (s - 16)
 // otherwise, so both halves of a RoPE pair sit in the same lane.
-#include "topk_rows.h"
+#include "fp16_round.h"
+#include "swan_internal.h"
 
 namespace swan {
 
-constexpr int kPfWaves = 4;            // waves per workgroup
+constexpr int kPfWaves = 8;            // waves per workgroup
 constexpr int kPfTile = 16;            // tokens per MFMA tile (one wave)
-constexpr int kPfChunk = 256;          // tokens per workgroup
+constexpr int kPfChunkMax = 512;       // tokens per workgroup (fewer when the grid would be small)
+constexpr int kPfComputeUnits = 256;   // of an MI355X
 constexpr int kPfBlocks = kD / 16;     // 16-column blocks of the output
 constexpr int kPfHalf = kPfTile / 2;   // tokens per placement pass
-constexpr int kPfGroup = 4;            // tokens whose rows are pruned together
+constexpr int kPfRow = kD + 8;         // staged row stride in fp16 (272 bytes: the quarter reads meet no bank twice)
+constexpr int kPfOut = 3 * kD + 16;    // bytes of a pruned row in the output stage: indices, values, a scratch slot
+constexpr int kPfTrash = 3 * kD;       // the scratch slot: entries that are not kept are written there
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef float pf_f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t pf_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t pf_u16x2 __attribute__((ext_vector_type(2)));
+typedef float pf_f32x2 __attribute__((ext_vector_type(2)));
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t pf_dpp(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
 
 // coordinate of contraction index k (= lane / 16) in k step s
 __device__ __forceinline__ int pf_coord(int s, int k) { return s < 16 ? 16 * k + s : kD / 2 + 16 * k + (s - 16); }
 
-__global__ __launch_bounds__(kPfWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill(PrefillArgs a)
+__global__ __launch_bounds__(kPfWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill(PrefillArgs a,
+                                                                                                   int chunk_len)
 {
     const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int T = min(a.len[b], a.max_len);
-    const int c0 = chunk * kPfChunk;
+    const int c0 = chunk * chunk_len;
     if (c0 >= T) return; // workgroup-uniform
 
     // P_QK[c][j] at pl[(c * 16 + j % 16) * 8 + j / 16]
     __shared__ __attribute__((aligned(16))) float pl[kD * 16 * kPfBlocks];
     __shared__ double theta[kD / 2];
-    __shared__ uint16_t kst[kPfWaves][kPfHalf][kD];
+    __shared__ __attribute__((aligned(16))) uint16_t kst[kPfWaves][2 * kPfHalf][kPfRow];
+    // pruned rows as stored: indices at [0, 128), values (vbytes each) from 128
+    __shared__ __attribute__((aligned(16))) uint8_t pout[kPfWaves][2 * kPfHalf][kPfOut];
+    __shared__ int64_t pslot[kPfWaves][kPfHalf]; // row slot of each token of a pass (-1: not pruned)
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     {
@@ -77,9 +106,13 @@ __global__ __launch_bounds__(kPfWaves * kWave) __attribute__((amdgpu_waves_per_e
     const float *vr = a.v_hat + u * a.T_stride * kD;
     const int kq = lane / 16, il = lane % 16; // MFMA k column and row of this lane's A element
     const int row_cap = a.geom.bs > 0 ? a.geom.max_blocks * a.geom.bs : a.geom.n_cap;
-    const int c_end = min(T, c0 + kPfChunk);
+    const int c_end = min(T, c0 + chunk_len);
 
     for (int t0 = c0 + wave * kPfTile; t0 < c_end; t0 += kPfWaves * kPfTile) {
+        // values of the tile's first eight tokens (tokens past T are not placed)
+        pf_f32x2 vpre[kPfHalf];
+#pragma unroll
+        for (int s = 0; s < kPfHalf; ++s) vpre[s] = *(const pf_f32x2 *)(vr + (int64_t)min(t0 + s, T - 1) * kD + 2 * lane);
         // ---- 1. rotated coordinates of token t0 + il: A[s] = x_rot[c(s, kq)]
         double A[32];
         {
@@ -130,50 +163,153 @@ __global__ __launch_bounds__(kPfWaves * kWave) __attribute__((amdgpu_waves_per_e
 #pragma unroll
             for (int r2 = 0; r2 < 2; ++r2)
 #pragma unroll
-                for (int n = 0; n < kPfBlocks; ++n) kst[wave][4 * r2 + kq][16 * n + il] = d2h(acc[n][2 * hp + r2]);
+                for (int n = 0; n < kPfBlocks; ++n) kst[wave][4 * r2 + kq][16 * n + il] = d2h_odd(acc[n][2 * hp + r2]);
+            // values of the same eight tokens, rounded to fp16, in rows 8..15 (two
+            // coordinates a lane, one 32-bit LDS write); the next pass's values
+            // are loaded now, to arrive while this pass is pruned
+#pragma unroll
+            for (int s = 0; s < kPfHalf; ++s) {
+                const uint32_t lo16 = f2h(vpre[s].x), hi16 = f2h(vpre[s].y);
+                *(uint32_t *)&kst[wave][kPfHalf + s][2 * lane] = lo16 | (hi16 << 16);
+            }
+            if (hp == 0) {
+#pragma unroll
+                for (int s = 0; s < kPfHalf; ++s)
+                    vpre[s] = *(const pf_f32x2 *)(vr + (int64_t)min(t0 + kPfHalf + s, T - 1) * kD + 2 * lane);
+            }
             // the wave reads what its own lanes wrote (LDS runs a wave's accesses in order)
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // four tokens (eight rows: key and value of each) at a time, so that
-            // the eight top-k threshold searches interleave
-            for (int g4 = 0; g4 < kPfHalf; g4 += kPfGroup) {
-                const int tb = t0 + kPfHalf * hp + g4;
-                if (tb >= T) break; // wave-uniform
-                uint16_t lo[2 * kPfGroup], hi[2 * kPfGroup];
-                int kk[2 * kPfGroup];
+            const int tb = t0 + kPfHalf * hp;
+            if (tb >= T) continue; // wave-uniform
+            // ---- prune the 16 staged rows, four lanes a row: lane 4 r + q holds
+            // coordinates 32 q .. 32 q + 31 of row r (rows 0..7 the keys, 8..15 the
+            // values of tokens tb .. tb + 7) as packed fp16
+            if (tb < T - a.R) { // some token of the pass is pruned (wave-uniform)
+                const int r = lane >> 2, q = lane & 3;
+                const int kr = r < kPfHalf ? a.k : a.k_v, ksr = r < kPfHalf ? a.geom.ks : a.geom.ks_v;
+                uint32_t x[16], m[16];
 #pragma unroll
-                for (int s = 0; s < kPfGroup; ++s) {
-                    const int t = tb + s;
-                    lo[2 * s] = kst[wave][g4 + s][lane];
-                    hi[2 * s] = kst[wave][g4 + s][lane + 64];
-                    const float *vt = vr + (int64_t)min(t, T - 1) * kD; // tokens past T are not placed
-                    lo[2 * s + 1] = f2h(vt[lane]);
-                    hi[2 * s + 1] = f2h(vt[lane + 64]);
-                    kk[2 * s] = a.k;
-                    kk[2 * s + 1] = a.k_v;
+                for (int v = 0; v < 4; ++v) {
+                    const pf_u32x4 w4 = *(const pf_u32x4 *)&kst[wave][r][32 * q + 8 * v];
+                    x[4 * v] = w4.x;
+                    x[4 * v + 1] = w4.y;
+                    x[4 * v + 2] = w4.z;
+                    x[4 * v + 3] = w4.w;
                 }
-                uint32_t thr[2 * kPfGroup];
-                if (tb < T - a.R) wave_topk_threshold<2 * kPfGroup>(lo, hi, kk, thr); // some token is pruned
 #pragma unroll
-                for (int s = 0; s < kPfGroup; ++s) {
+                for (int j = 0; j < 16; ++j) m[j] = x[j] & 0x7fff7fffu;
+                // the k-th largest magnitude T: the largest T with at least k
+                // magnitudes >= T, bit by bit; a packed subtract's sign bits count
+                // the magnitudes below the candidate
+                uint32_t Tt = 0;
+#pragma unroll
+                for (int bit = 14; bit >= 0; --bit) {
+                    const uint32_t c = Tt | (1u << bit);
+                    const pf_u16x2 cp = {(uint16_t)c, (uint16_t)c};
+                    uint32_t acc4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const pf_u16x2 d = __builtin_bit_cast(pf_u16x2, m[j]) - cp; // sign bit: m < c
+                        acc4[j & 3] = __builtin_amdgcn_sad_u16(__builtin_bit_cast(uint32_t, d) & 0x80008000u, 0u,
+                                                                acc4[j & 3]);
+                    }
+                    uint32_t lt = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+                    lt += pf_dpp<0xB1>(lt);
+                    lt += pf_dpp<0x4E>(lt);
+                    if (kD - (int)(lt >> 15) >= kr) Tt = c;
+                }
+                // kept: every magnitude above T, then the first need = k - #(above T)
+                // equal to T in index order (lower quarters first)
+                const pf_u16x2 tp = {(uint16_t)Tt, (uint16_t)Tt};
+                uint32_t gacc = 0, eacc = 0;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const pf_u16x2 mj = __builtin_bit_cast(pf_u16x2, m[j]);
+                    gacc = __builtin_amdgcn_sad_u16(__builtin_bit_cast(uint32_t, tp - mj) & 0x80008000u, 0u, gacc);
+                    eacc = __builtin_amdgcn_sad_u16(__builtin_bit_cast(uint32_t, mj - tp) & 0x80008000u, 0u, eacc);
+                }
+                const int n_gt = (int)(gacc >> 15), n_lt = (int)(eacc >> 15), n_eq = 32 - n_gt - n_lt;
+                // quad sums and exclusive prefixes (lane q of the row's quad)
+                const int g1 = (int)pf_dpp<0x00>(n_gt), g2 = (int)pf_dpp<0x55>(n_gt), g3 = (int)pf_dpp<0xAA>(n_gt),
+                          g4 = (int)pf_dpp<0xFF>(n_gt);
+                const int e1 = (int)pf_dpp<0x00>(n_eq), e2 = (int)pf_dpp<0x55>(n_eq), e3 = (int)pf_dpp<0xAA>(n_eq);
+                const int need = kr - (g1 + g2 + g3 + g4);
+                const int eq_before = (q > 0 ? e1 : 0) + (q > 1 ? e2 : 0) + (q > 2 ? e3 : 0);
+                const int allow = min(max(need - eq_before, 0), n_eq);
+                const int mine = n_gt + allow;
+                const int k1 = (int)pf_dpp<0x00>(mine), k2 = (int)pf_dpp<0x55>(mine), k3 = (int)pf_dpp<0xAA>(mine);
+                int pos = (q > 0 ? k1 : 0) + (q > 1 ? k2 : 0) + (q > 2 ? k3 : 0);
+                uint8_t *orow = pout[wave][r];
+                const int vb = a.geom.vbytes;
+                int eq_seen = 0;
+#pragma unroll
+                for (int i = 0; i < 32; ++i) {
+                    const uint32_t v = (i & 1) ? (x[i / 2] >> 16) : (x[i / 2] & 0xffffu);
+                    const uint32_t mag = v & 0x7fffu;
+                    const bool is_eq = mag == Tt;
+                    const bool keep = mag > Tt || (is_eq && eq_seen < allow);
+                    eq_seen += is_eq ? 1 : 0;
+                    // every lane writes: kept entries at their place, the rest to the scratch slot
+                    const int io = keep ? pos : kPfTrash, vo = keep ? kD + vb * pos : kPfTrash + 2;
+                    orow[io] = (uint8_t)(32 * q + i);
+                    if (vb == 1)
+                        orow[vo] = h2e4m3((uint16_t)v);
+                    else
+                        *(uint16_t *)(orow + vo) = (uint16_t)v;
+                    pos += keep ? 1 : 0;
+                }
+                // padding entries k .. ks - 1: index 0, value +0
+                for (int e = kr + q; e < ksr; e += 4) {
+                    orow[e] = 0;
+                    if (vb == 1)
+                        orow[kD + e] = 0;
+                    else
+                        *(uint16_t *)(orow + kD + 2 * e) = 0;
+                }
+                if (lane < kPfHalf) {
+                    const int t = tb + lane;
+                    pslot[wave][lane] = (t < T - a.R && t < row_cap) ? row_slot_rt(a.geom, b, h, t) : -1;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                // whole rows to their slots, one dword a lane (row widths are powers of two)
+#pragma unroll
+                for (int which = 0; which < 2; ++which) {
+                    const int ksw = which ? a.geom.ks_v : a.geom.ks;
+                    const int wsh = __builtin_ctz((unsigned)ksw) - 2;       // log2 of the index row's dwords
+                    const int vsh = wsh + (vb == 2 ? 1 : 0);                // log2 of the value row's dwords
+                    uint8_t *iplane = which ? a.vidx : a.kidx, *vplane = which ? a.vval : a.kval;
+                    for (int e = lane; e < (kPfHalf << wsh); e += kWave) {
+                        const int sidx = e >> wsh, w = e & ((1 << wsh) - 1);
+                        const int64_t slot = pslot[wave][sidx];
+                        if (slot >= 0)
+                            *(uint32_t *)(iplane + slot * ksw + 4 * w) =
+                                *(const uint32_t *)(pout[wave][which * kPfHalf + sidx] + 4 * w);
+                    }
+                    for (int e = lane; e < (kPfHalf << vsh); e += kWave) {
+                        const int sidx = e >> vsh, w = e & ((1 << vsh) - 1);
+                        const int64_t slot = pslot[wave][sidx];
+                        if (slot >= 0)
+                            *(uint32_t *)(vplane + slot * ksw * vb + 4 * w) =
+                                *(const uint32_t *)(pout[wave][which * kPfHalf + sidx] + kD + 4 * w);
+                    }
+                }
+            }
+            // ---- the newest R tokens go to the buffer
+            if (tb + kPfHalf > T - a.R) {
+                for (int s = 0; s < kPfHalf; ++s) {
                     const int t = tb + s;
                     if (t >= T) break; // wave-uniform
+                    if (t < T - a.R) continue;
 #pragma unroll
                     for (int which = 0; which < 2; ++which) {
-                        const int n = 2 * s + which;
-                        if (t < T - a.R) {
-                            const int64_t slot = t < row_cap ? row_slot_rt(a.geom, b, h, t) : -1;
-                            const int ks = which ? a.geom.ks_v : a.geom.ks;
-                            if (slot >= 0)
-                                wave_write_topk(lane, lo[n], hi[n], thr[n], kk[n], ks,
-                                                (which ? a.vidx : a.kidx) + slot * ks,
-                                                (which ? a.vval : a.kval) + slot * ks * a.geom.vbytes, a.geom.vbytes);
-                        } else {
-                            uint16_t *buf = (which ? a.vbuf : a.kbuf) + (u * a.R + t % a.R) * kD;
-                            buf[lane] = lo[n];
-                            buf[lane + 64] = hi[n];
-                        }
+                        const int row = which * kPfHalf + s;
+                        uint16_t *buf = (which ? a.vbuf : a.kbuf) + (u * a.R + t % a.R) * kD;
+                        buf[lane] = kst[wave][row][lane];
+                        buf[lane + 64] = kst[wave][row][lane + 64];
                     }
                 }
             }
@@ -187,8 +323,14 @@ __global__ __launch_bounds__(kPfWaves * kWave) __attribute__((amdgpu_waves_per_e
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s)
 {
-    const dim3 grid((a.max_len + kPfChunk - 1) / kPfChunk, a.H, a.B);
-    hipLaunchKernelGGL(k_prefill, grid, dim3(kPfWaves * kWave), 0, s, a);
+    // the longest chunk (P_QK staged once per chunk) that still gives about
+    // two workgroups per compute unit; one 16-token tile per wave at least
+    int chunk = kPfChunkMax;
+    while (chunk > kPfWaves * kPfTile &&
+           (int64_t)((a.max_len + chunk - 1) / chunk) * a.H * a.B < 2 * kPfComputeUnits)
+        chunk /= 2;
+    const dim3 grid((a.max_len + chunk - 1) / chunk, a.H, a.B);
+    hipLaunchKernelGGL(k_prefill, grid, dim3(kPfWaves * kWave), 0, s, a, chunk);
     return hipGetLastError();
 }
 
