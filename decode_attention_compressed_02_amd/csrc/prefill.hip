@@ -35,14 +35,18 @@
 // The result is identical to appending the tokens one at a time.  Keys are
 // rotated and projected in double, as in the decode-step projection, so that
 // their fp16 rounding (and with it the pruning) does not depend on float
-// rounding of intermediate products.
+// rounding of intermediate products; the rotation's sine and cosine come from
+// rope_trig.h (within ~1e-16 of the true values, as a library sincos).
 //
 // Operand layout of v_mfma_f64_16x16x4f64 (one wave): A[i][k] comes from lane
 // i + 16 k, B[k][j] from lane j + 16 k, and result register r of lane l
 // holds D[4 r + l / 16][l % 16].  The contraction index k of k step s maps
 // to coordinate c(s, k) = 16 k + s for s < 16 and 64 + 16 k + (s - 16)
 // otherwise, so both halves of a RoPE pair sit in the same lane.
+#include <type_traits>
+
 #include "fp16_round.h"
+#include "rope_trig.h"
 #include "swan_internal.h"
 
 namespace swan {
@@ -134,7 +138,7 @@ __global__ __launch_bounds__(kPfWaves * kWave) __attribute__((amdgpu_waves_per_e
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
                 double sn, cs;
-                sincos((double)t * theta[16 * kq + s], &sn, &cs);
+                rope_sincos((double)t * theta[16 * kq + s], sn, cs);
                 const double y0 = x0[s / 4][s % 4], y1 = x1[s / 4][s % 4];
                 A[s] = y0 * cs - y1 * sn;
                 A[16 + s] = y1 * cs + y0 * sn;
@@ -200,41 +204,42 @@ __global__ __launch_bounds__(kPfWaves * kWave) __attribute__((amdgpu_waves_per_e
                 }
 #pragma unroll
                 for (int j = 0; j < 16; ++j) m[j] = x[j] & 0x7fff7fffu;
+                // Counting by sums: for 15-bit magnitudes m and a candidate c, the packed
+                // 16-bit difference m - c wraps by 2^16 exactly when m < c, so the sum of
+                // the 32 differences (v_sad_u16 adds both halves, no wrap in 32 bits) is
+                // sum(m) - 32 c + 2^16 #(m < c): one subtract and one add a word.
+                uint32_t sm4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int j = 0; j < 16; ++j) sm4[j & 3] = __builtin_amdgcn_sad_u16(m[j], 0u, sm4[j & 3]);
+                const uint32_t sum_m = (sm4[0] + sm4[1]) + (sm4[2] + sm4[3]);
+                auto count_below = [&](uint32_t c) -> int { // #(m < c) over the lane's 32 coordinates
+                    const pf_u16x2 cp = {(uint16_t)c, (uint16_t)c};
+                    uint32_t acc4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        acc4[j & 3] = __builtin_amdgcn_sad_u16(
+                            __builtin_bit_cast(uint32_t, __builtin_bit_cast(pf_u16x2, m[j]) - cp), 0u, acc4[j & 3]);
+                    return (int)(((acc4[0] + acc4[1]) + (acc4[2] + acc4[3]) + 32u * c - sum_m) >> 16);
+                };
                 // the k-th largest magnitude T: the largest T with at least k
-                // magnitudes >= T, bit by bit; a packed subtract's sign bits count
-                // the magnitudes below the candidate
+                // magnitudes >= T, bit by bit
                 uint32_t Tt = 0;
 #pragma unroll
                 for (int bit = 14; bit >= 0; --bit) {
                     const uint32_t c = Tt | (1u << bit);
-                    const pf_u16x2 cp = {(uint16_t)c, (uint16_t)c};
-                    uint32_t acc4[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const pf_u16x2 d = __builtin_bit_cast(pf_u16x2, m[j]) - cp; // sign bit: m < c
-                        acc4[j & 3] = __builtin_amdgcn_sad_u16(__builtin_bit_cast(uint32_t, d) & 0x80008000u, 0u,
-                                                                acc4[j & 3]);
-                    }
-                    uint32_t lt = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+                    uint32_t lt = (uint32_t)count_below(c);
                     lt += pf_dpp<0xB1>(lt);
                     lt += pf_dpp<0x4E>(lt);
-                    if (kD - (int)(lt >> 15) >= kr) Tt = c;
+                    if (kD - (int)lt >= kr) Tt = c;
                 }
                 // kept: every magnitude above T, then the first need = k - #(above T)
                 // equal to T in index order (lower quarters first)
-                const pf_u16x2 tp = {(uint16_t)Tt, (uint16_t)Tt};
-                uint32_t gacc = 0, eacc = 0;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const pf_u16x2 mj = __builtin_bit_cast(pf_u16x2, m[j]);
-                    gacc = __builtin_amdgcn_sad_u16(__builtin_bit_cast(uint32_t, tp - mj) & 0x80008000u, 0u, gacc);
-                    eacc = __builtin_amdgcn_sad_u16(__builtin_bit_cast(uint32_t, mj - tp) & 0x80008000u, 0u, eacc);
-                }
-                const int n_gt = (int)(gacc >> 15), n_lt = (int)(eacc >> 15), n_eq = 32 - n_gt - n_lt;
+                const int n_lt = count_below(Tt), n_gt = 32 - count_below(Tt + 1), n_eq = 32 - n_gt - n_lt;
                 // quad sums and exclusive prefixes (lane q of the row's quad)
                 const int g1 = (int)pf_dpp<0x00>(n_gt), g2 = (int)pf_dpp<0x55>(n_gt), g3 = (int)pf_dpp<0xAA>(n_gt),
                           g4 = (int)pf_dpp<0xFF>(n_gt);
-                const int e1 = (int)pf_dpp<0x00>(n_eq), e2 = (int)pf_dpp<0x55>(n_eq), e3 = (int)pf_dpp<0xAA>(n_eq);
+                const int e1 = (int)pf_dpp<0x00>(n_eq), e2 = (int)pf_dpp<0x55>(n_eq), e3 = (int)pf_dpp<0xAA>(n_eq),
+                          e4 = (int)pf_dpp<0xFF>(n_eq);
                 const int need = kr - (g1 + g2 + g3 + g4);
                 const int eq_before = (q > 0 ? e1 : 0) + (q > 1 ? e2 : 0) + (q > 2 ? e3 : 0);
                 const int allow = min(max(need - eq_before, 0), n_eq);
@@ -243,23 +248,43 @@ __global__ __launch_bounds__(kPfWaves * kWave) __attribute__((amdgpu_waves_per_e
                 int pos = (q > 0 ? k1 : 0) + (q > 1 ? k2 : 0) + (q > 2 ? k3 : 0);
                 uint8_t *orow = pout[wave][r];
                 const int vb = a.geom.vbytes;
-                int eq_seen = 0;
-#pragma unroll
-                for (int i = 0; i < 32; ++i) {
-                    const uint32_t v = (i & 1) ? (x[i / 2] >> 16) : (x[i / 2] & 0xffffu);
-                    const uint32_t mag = v & 0x7fffu;
-                    const bool is_eq = mag == Tt;
-                    const bool keep = mag > Tt || (is_eq && eq_seen < allow);
-                    eq_seen += is_eq ? 1 : 0;
-                    // every lane writes: kept entries at their place, the rest to the scratch slot
-                    const int io = keep ? pos : kPfTrash, vo = keep ? kD + vb * pos : kPfTrash + 2;
+                // every lane writes: kept entries at their place, the rest to the scratch
+                // slot; VB (the value width) is a compile-time constant in each loop
+                auto put = [&](auto VB, int i, uint32_t v, bool keep) {
+                    constexpr int kVB = decltype(VB)::value;
+                    const int io = keep ? pos : kPfTrash, vo = keep ? kD + kVB * pos : kPfTrash + 2;
                     orow[io] = (uint8_t)(32 * q + i);
-                    if (vb == 1)
+                    if constexpr (kVB == 1)
                         orow[vo] = h2e4m3((uint16_t)v);
                     else
                         *(uint16_t *)(orow + vo) = (uint16_t)v;
                     pos += keep ? 1 : 0;
-                }
+                };
+                auto assemble = [&](auto VB) {
+                    if (__all(need == e1 + e2 + e3 + e4)) {
+                        // no row splits its coordinates equal to T (the usual case): each
+                        // keeps exactly the magnitudes >= T
+#pragma unroll
+                        for (int i = 0; i < 32; ++i) {
+                            const uint32_t v = (i & 1) ? (x[i / 2] >> 16) : (x[i / 2] & 0xffffu);
+                            put(VB, i, v, (v & 0x7fffu) >= Tt);
+                        }
+                    } else {
+                        int eq_seen = 0;
+#pragma unroll
+                        for (int i = 0; i < 32; ++i) {
+                            const uint32_t v = (i & 1) ? (x[i / 2] >> 16) : (x[i / 2] & 0xffffu);
+                            const uint32_t mag = v & 0x7fffu;
+                            const bool is_eq = mag == Tt;
+                            put(VB, i, v, mag > Tt || (is_eq && eq_seen < allow));
+                            eq_seen += is_eq ? 1 : 0;
+                        }
+                    }
+                };
+                if (vb == 1)
+                    assemble(std::integral_constant<int, 1>());
+                else
+                    assemble(std::integral_constant<int, 2>());
                 // padding entries k .. ks - 1: index 0, value +0
                 for (int e = kr + q; e < ksr; e += 4) {
                     orow[e] = 0;
