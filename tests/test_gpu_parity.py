@@ -530,6 +530,37 @@ def test_prefill_convert(R, k, vf, kv):
     assert rel_l2_max(out, want) < TOL
 
 
+@pytest.mark.parametrize("k,kv,vf", [(32, 0, 0), (64, 0, 1), (32, 51, 0)])
+def test_prefill_ties_at_the_threshold(k, kv, vf):
+    """Value rows drawn from five magnitudes (fp16-exact), so nearly every row
+    has more coordinates equal to its k-th largest magnitude than it keeps:
+    the kept ones must be the lowest indices among them (the oracle's
+    ranking), on the prefill's general tie path and in its row layout."""
+    w = wl.Workload("ties", 3, 8, 2, 64, k, (700, 333, 1030), seed=77, value_format=vf, k_v=kv)
+    K, V, Ts = hist_arrays(w)
+    r = rng(78)
+    V = (r.choice(np.array([0.25, 0.5, 1.0, 1.5, 2.0], np.float32), size=V.shape)
+         * r.choice(np.array([-1.0, 1.0], np.float32), size=V.shape)).astype(np.float32)
+    P = wl.projection_qk(w)
+    oc = oracle.OracleCache.for_workload(w)
+    oc.prefill(K, V, Ts, P.astype(np.float64), w.rope_base)
+    dec = make_decoder(oc, P)
+    dec.prefill(cuda(Ts.astype(np.int32)), int(Ts.max()), cuda(K), cuda(V))
+    torch.cuda.synchronize()
+    kv = kv or k
+    rows = download_rows(dec.cache, w.B, w.H_kv, oc.ncap)
+    for b in range(w.B):
+        n = max(0, int(Ts[b]) - w.R)
+        np.testing.assert_array_equal(rows[2][b, :, :n, :kv], oc.vidx[b, :, :n])
+        assert_values_bits(rows[3][b, :, :n, :kv], oc.vval[b, :, :n], vf)
+        np.testing.assert_array_equal(rows[0][b, :, :n, :k], oc.kidx[b, :, :n])
+        assert_values_bits(rows[1][b, :, :n, :k], oc.kval[b, :, :n], vf)
+    # the rows really split their ties: the k-th largest magnitude recurs past k
+    mags = np.abs(V[0, 0, :100])
+    kth = -np.sort(-mags, axis=1)[:, kv - 1]
+    assert ((mags >= kth[:, None]).sum(1) > kv).mean() > 0.5
+
+
 def test_fp8_values_decode_every_code():
     """One token, all 128 coordinates kept, no buffer: the output is the stored
     value vector itself (softmax over one token is exactly 1), so every finite
