@@ -17,6 +17,8 @@
 // in float could round one ulp away from the exact product and change which
 // coordinates survive pruning.  In double the result is the correctly
 // rounded fp16 of the exact value except within ~1e-16 of a midpoint.
+#include "fp16_round.h"
+#include "rope_trig.h"
 #include "swan_internal.h"
 
 namespace swan {
@@ -97,7 +99,7 @@ __device__ __forceinline__ void project_unit(const ProjectArgs &a, const AppendA
         const double theta = pow((double)a.base, -(double)tid / (double)(kD / 2));
         const int p = max(a.pos[b], 0);
         double sv, cv;
-        sincos((double)p * theta, &sv, &cv);
+        rope_sincos((double)p * theta, sv, cv);
         cs[tid] = cv;
         sn[tid] = sv;
     }
@@ -134,7 +136,7 @@ __device__ __forceinline__ void project_unit(const ProjectArgs &a, const AppendA
             for (int r = 0; r < kProjThreads / kD - 1; ++r) acc[v] += part[r][v][j];
 #pragma unroll
         for (int v = 0; v < G; ++v) a.q_hat[((int64_t)b * a.N_h + h * G + v) * kD + j] = (float)acc[v];
-        const uint16_t kh = d2h(acc[G]);
+        const uint16_t kh = d2h_odd(acc[G]);
         a.k_hat[((int64_t)b * a.H + h) * kD + j] = kh;
         if constexpr (APPEND) khs[j] = kh;
     }
