@@ -530,6 +530,60 @@ def test_prefill_convert(R, k, vf, kv):
     assert rel_l2_max(out, want) < TOL
 
 
+@pytest.mark.parametrize("k,kv,R,T,vf,bs", [
+    (1, 0, 0, (0, 1, 15, 17, 200), 0, 0),        # one kept coordinate, no buffer, empty and short sequences
+    (128, 0, 16, (17, 40, 129), 0, 0),           # every coordinate kept
+    (8, 16, 5, (3, 16, 333), 1, 0),              # narrow rows, values wider than keys, fp8
+    (32, 0, 8, (1, 30, 130), 0, 1),              # paged, one row a block (per-row block lookups)
+    (64, 0, 0, (16, 64, 1100), 1, 16),           # paged 16-row blocks, no buffer, fp8
+])
+def test_prefill_edge_shapes(k, kv, R, T, vf, bs):
+    """Prefill rows and buffer bit-exact against the oracle at the edges of
+    the conversion kernel: empty, one-token and tile-boundary sequences,
+    k = 1 and k = 128, a buffer longer than the history, rows narrower than
+    a lane quarter, and paged pools with 1- and 16-row blocks in a shuffled
+    order."""
+    w = wl.Workload("edge", len(T), 4, 2, R, k, (2000,) * len(T), seed=90 + k + bs, value_format=vf, k_v=kv)
+    Tm = max(max(T), 1)
+    K = np.zeros((w.B, w.H_kv, Tm, D), np.float32)
+    V = np.zeros_like(K)
+    for b in range(w.B):
+        if T[b]:
+            K[b, :, :T[b]], V[b, :, :T[b]] = wl.history(w, b, 0, T[b])
+    Ts = np.array(T, np.int64)
+    P = wl.projection_qk(w)
+    n_rows = max(1, max(T))
+    oc = oracle.OracleCache.for_workload(w, ncap=n_rows)
+    oc.prefill(K, V, Ts, P.astype(np.float64), w.rope_base)
+    kw = {}
+    bt = None
+    if bs:
+        max_blocks = (n_rows + bs - 1) // bs
+        nb = w.B * max_blocks + 3
+        bt = rng(5).permutation(nb)[:w.B * max_blocks].reshape(w.B, max_blocks)
+        kw = dict(block_size=bs, max_blocks=max_blocks, num_blocks=nb, block_table=bt)
+    dec = make_decoder(oc, P, **kw)
+    dec.prefill(cuda(Ts.astype(np.int32)), Tm, cuda(K), cuda(V))
+    torch.cuda.synchronize()
+    kv = kv or k
+    rows = download_rows(dec.cache, w.B, w.H_kv, n_rows, bt)
+    for b in range(w.B):
+        n = max(0, T[b] - R)
+        np.testing.assert_array_equal(rows[0][b, :, :n, :k], oc.kidx[b, :, :n])
+        assert_values_bits(rows[1][b, :, :n, :k], oc.kval[b, :, :n], vf)
+        np.testing.assert_array_equal(rows[2][b, :, :n, :kv], oc.vidx[b, :, :n])
+        assert_values_bits(rows[3][b, :, :n, :kv], oc.vval[b, :, :n], vf)
+        # padding entries: index 0, value +0
+        assert not rows[0][b, :, :n, k:].any() and not rows[1][b, :, :n, k:].any()
+        assert not rows[2][b, :, :n, kv:].any() and not rows[3][b, :, :n, kv:].any()
+    if R > 0:
+        kb, vb = (x.cpu().numpy().astype(np.float64) for x in dec.cache.buffer_views())
+        for b in range(w.B):
+            fill = min(T[b], R)
+            np.testing.assert_array_equal(kb[b, :, :fill], oc.ringk[b, :, :fill])
+            np.testing.assert_array_equal(vb[b, :, :fill], oc.ringv[b, :, :fill])
+
+
 @pytest.mark.parametrize("k,kv,vf", [(32, 0, 0), (64, 0, 1), (32, 51, 0)])
 def test_prefill_ties_at_the_threshold(k, kv, vf):
     """Value rows drawn from five magnitudes (fp16-exact), so nearly every row
