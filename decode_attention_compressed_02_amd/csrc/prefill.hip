@@ -5,8 +5,10 @@
 // The key projection of a history is a dense contraction (tokens x 128
 // rotated coordinates times the 128 x 128 P_QK of the head), carried out in
 // double to match the decode-step projection, so it runs on the fp64 matrix
-// cores (v_mfma_f64_16x16x4f64).  One workgroup of eight waves per (chunk of
-// 128 to 512 tokens, kv head, sequence; shorter chunks for small batches):
+// cores (v_mfma_f64_16x16x4f64).  One workgroup of eight waves per chunk of
+// 128 to 512 tokens of one (kv head, sequence) (shorter chunks for small
+// batches; only chunks that hold tokens are numbered, so ragged batches leave
+// no idle workgroups among the busy ones):
 //   0. P_QK of the head is staged in LDS as fp32 (64 KB, read once per
 //      chunk) in a layout where a lane's eight 16-column blocks are
 //      contiguous, and the 64 RoPE frequencies are computed once;
@@ -79,10 +81,55 @@ __device__ __forceinline__ int pf_coord(int s, int k) { return s < 16 ? 16 * k +
 __global__ __launch_bounds__(kPfWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill(PrefillArgs a,
                                                                                                    int chunk_len)
 {
-    const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // Work item = one chunk of one (sequence, kv head) that holds tokens,
+    // numbered sequence by sequence, head by head, chunk by chunk: the chunks
+    // of ragged sequences stay contiguous in the grid (so consecutive
+    // workgroups, spread over the XCDs in turn, all have work) and the grid's
+    // surplus workgroups, all at its end, exit at once.  Wave 0 finds the
+    // item's sequence from a prefix sum of the sequences' chunk counts.
+    __shared__ int64_t item_base;
+    __shared__ int item_b, item_chunks;
+    {
+        const int64_t item = blockIdx.x;
+        if (threadIdx.x < kWave) {
+            const int ln = threadIdx.x;
+            int64_t run = 0;
+            int found = -1, fn = 0;
+            int64_t fbase = 0;
+            for (int base = 0; base < a.B && found < 0; base += kWave) {
+                const int bb = base + ln;
+                const int n = bb < a.B ? (max(0, min(a.len[bb], a.max_len)) + chunk_len - 1) / chunk_len : 0;
+                const int64_t cnt = (int64_t)n * a.H;
+                int64_t incl = cnt; // inclusive prefix over the lanes
+#pragma unroll
+                for (int d = 1; d < kWave; d <<= 1) {
+                    const int64_t t = __shfl_up(incl, d);
+                    if (ln >= d) incl += t;
+                }
+                incl += run;
+                const uint64_t hit = __ballot(bb < a.B && incl > item);
+                if (hit) {
+                    const int l = __builtin_ctzll(hit);
+                    found = base + l;
+                    fbase = __shfl(incl - cnt, l);
+                    fn = __shfl(n, l);
+                }
+                run = __shfl(incl, kWave - 1);
+            }
+            if (ln == 0) {
+                item_b = found;
+                item_base = fbase;
+                item_chunks = fn;
+            }
+        }
+        __syncthreads();
+    }
+    if (item_b < 0) return; // workgroup-uniform: past the last item
+    const int b = item_b;
+    const int h = (int)(((int64_t)blockIdx.x - item_base) / item_chunks);
+    const int chunk = (int)(((int64_t)blockIdx.x - item_base) % item_chunks);
     const int T = min(a.len[b], a.max_len);
     const int c0 = chunk * chunk_len;
-    if (c0 >= T) return; // workgroup-uniform
 
     // P_QK[c][j] at pl[(c * 16 + j % 16) * 8 + j / 16]
     __shared__ __attribute__((aligned(16))) float pl[kD * 16 * kPfBlocks];
@@ -354,7 +401,11 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s)
     while (chunk > kPfWaves * kPfTile &&
            (int64_t)((a.max_len + chunk - 1) / chunk) * a.H * a.B < 2 * kPfComputeUnits)
         chunk /= 2;
-    const dim3 grid((a.max_len + chunk - 1) / chunk, a.H, a.B);
+    // one workgroup per chunk of the longest sequence for every (sequence,
+    // head): at least as many as there are work items
+    const int64_t items = (int64_t)((a.max_len + chunk - 1) / chunk) * a.H * a.B;
+    if (items > INT32_MAX) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)items);
     hipLaunchKernelGGL(k_prefill, grid, dim3(kPfWaves * kWave), 0, s, a, chunk);
     return hipGetLastError();
 }
