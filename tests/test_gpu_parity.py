@@ -82,6 +82,27 @@ def test_project_qk(N, H):
     np.testing.assert_array_equal(gk, oracle.round_f16(kh))
 
 
+def test_project_qk_large_positions():
+    """Positions around the RoPE sine/cosine routine's switch to the library
+    routine (angles of 2^20 pi/2 = 1 647 099.3 rad at the fastest frequency)
+    and far past it: q_hat within one float rounding of the oracle, k_hat
+    bit-exact."""
+    r = rng(4242)
+    B, N, H = 4, 8, 2
+    w = wl.Workload("proj", B, N, H, 16, 32, (1,) * B, seed=9)
+    P = wl.projection_qk(w)
+    q = r.standard_normal((B, N, D)).astype(np.float32) * 3
+    k = r.standard_normal((B, H, D)).astype(np.float32) * 3
+    pos = np.array([1_000_000, 1_647_000, 1_647_200, 2_000_000_000], np.int32)
+    dec = SwanDecoder(S.make_dims(B, N, H, 16, 32, n_cap=1), cuda(P))
+    dec.project(cuda(q), cuda(k), cuda(pos))
+    torch.cuda.synchronize()
+    oc = oracle.OracleCache(B, N, H, D, 16, 32, 1)
+    qh, kh = oc.project(q, k, pos.astype(np.int64), P.astype(np.float64))
+    assert rel_l2_max(dec.q_hat.cpu().numpy(), qh) < 1e-6
+    np.testing.assert_array_equal(dec.k_hat.cpu().numpy().astype(np.float64), oracle.round_f16(kh))
+
+
 def test_project_rounds_keys_once_to_fp16():
     """With P = I at position 0 the projection is the identity, so the stored
     key is the fp16 rounding of the raw float key: midpoints between fp16
